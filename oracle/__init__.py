@@ -1,0 +1,40 @@
+"""fp64 CPU oracle of the fused multi-head attention forward pass.
+
+TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import or run anything in this package.  It shares no code with the HIP path
+(no kernels, headers, helpers, tables or constants); both take their inputs
+from the separate ``workloads`` generator, which holds none of the attention
+arithmetic.
+
+Pins (tests/test_oracle.py, run with ``-m "not gpu"``):
+
+* format decoders: every code of bf16, fp16 and e4m3fn against torch/numpy casts,
+  plus values fixed by the format definitions;
+* brute force: pure-Python loops over tiny problems, written as the direct
+  softmax quotient without the max shift, every mask, GQA and packed batches;
+* library routine: torch's CPU ``scaled_dot_product_attention`` in fp64 for the
+  no-mask, top-left causal and explicit-mask cases;
+* closed forms: one key gives O = V[0]; constant V rows give that row; causal
+  row 0 gives V[0]; Q = 0 or Q = K = ones give uniform weights with known LSE;
+* invariants: rows of P sum to 1, sum_j exp(S_ij - LSE_i) = 1, K/V at masked
+  positions do not change O (bit-identical), key permutation invariance,
+  packed batch == per-sequence runs, GQA == MHA with repeated K/V heads,
+  causal-qend == causal-qbegin when Sq == Sk;
+* planted mistakes in a copy of the oracle (off-by-one diagonal, flipped qend
+  offset, wrong GQA head, missing scale, transposed operand) fail the pins;
+* the FLOP convention reproduces the TFLOP/s column printed by the sm120 article.
+
+No function is "parity unpinned" except the two choices the pages leave open:
+rows with no visible key (O = 0, LSE = -inf) and fp8 saturation at +-448, which
+are pinned only by those stated choices.
+"""
+from .attention import (  # noqa: F401
+    MASKS,
+    attention_dense,
+    attention_head,
+    attention_rows,
+    attention_varlen,
+    visible_keys,
+)
+from .formats import decode, decode_minifloat  # noqa: F401

@@ -1,0 +1,18 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module only draws and encodes inputs (random normals, lengths, fp8 per-tensor
+quantisation, padding and sentinels). It holds none of the attention arithmetic,
+so both the HIP path's tests and the CPU oracle can take their inputs from it.
+"""
+from .synth import (  # noqa: F401
+    CONFIGS,
+    DenseInputs,
+    VarlenInputs,
+    config_seed,
+    draw_normal,
+    make_dense,
+    make_varlen,
+    make_config,
+    quantize_e4m3,
+    to_bits,
+)

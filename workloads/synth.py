@@ -1,0 +1,288 @@
+"""Seeded synthetic Q/K/V for the attention forward pass (no attention arithmetic here).
+
+Recipe (the same for the HIP path's tests, the benchmark and the CPU oracle):
+
+* one ``numpy.random.default_rng(seed)`` (PCG64) stream per workload;
+* for packed variable-length batches the per-sequence lengths are drawn first,
+  then Q, then K, then V;
+* every tensor is a full ``standard_normal`` draw in float32, converted to the
+  storage type by torch's CPU round-to-nearest-even cast (fp16 / bf16);
+* fp8 tensors are quantised per tensor: ``s = amax|x| / 448`` and
+  ``x_q = e4m3fn(x / s)`` (torch's CPU cast, round to nearest even); the caller
+  folds the scales into the softmax scale and the output scale;
+* a packed batch has one leading padding sequence of valid but unused memory in
+  front of Q, K, V and O (``max_seqlen`` rows each); device pointers are passed
+  past it.  The O padding holds a sentinel bit pattern, the input padding holds
+  random values (or NaN when ``poison_pads`` is set).
+
+Tensors are returned on the CPU; callers move them to the device.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+TORCH_DTYPES = {
+    "f16": torch.float16,
+    "bf16": torch.bfloat16,
+    "f8e4m3": torch.float8_e4m3fn,
+}
+ELEM_BYTES = {"f16": 2, "bf16": 2, "f8e4m3": 1}
+E4M3_MAX = 448.0
+# Bit patterns written into the output padding; a kernel that writes outside its rows changes them.
+O_SENTINEL_BITS = {"f16": 0x7BAD, "bf16": 0x4B1D, "f8e4m3": 0x5A}
+
+
+def config_seed(config_id: int) -> int:
+    return 1000 + int(config_id)
+
+
+def draw_normal(rng: np.random.Generator, shape: Sequence[int]) -> np.ndarray:
+    """i.i.d. N(0, 1) in float32, drawn in C order."""
+    return rng.standard_normal(size=tuple(int(s) for s in shape), dtype=np.float32)
+
+
+def quantize_e4m3(x: torch.Tensor):
+    """Per-tensor e4m3fn quantisation: returns (codes as float8_e4m3fn, dequantisation scale)."""
+    amax = float(x.abs().max()) if x.numel() else 0.0
+    s = amax / E4M3_MAX if amax > 0.0 else 1.0
+    q = (x.to(torch.float32) / s).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    return q, s
+
+
+def _to_storage(x32: np.ndarray, dtype: str):
+    t = torch.from_numpy(x32)
+    if dtype == "f8e4m3":
+        return quantize_e4m3(t)
+    return t.to(TORCH_DTYPES[dtype]), 1.0
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw storage bits of a CPU tensor as an unsigned numpy array (uint8 or uint16)."""
+    t = t.detach().cpu().contiguous()
+    if t.element_size() == 1:
+        return t.view(torch.uint8).numpy()
+    if t.element_size() == 2:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.element_size() == 4:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    raise TypeError(f"unsupported element size {t.element_size()}")
+
+
+@dataclasses.dataclass
+class DenseInputs:
+    q: torch.Tensor  # [B, Sq, H, D]
+    k: torch.Tensor  # [B, Sk, H_kv, D]
+    v: torch.Tensor  # [B, Sk, H_kv, D]
+    B: int
+    Sq: int
+    Sk: int
+    H: int
+    H_kv: int
+    D: int
+    dtype: str
+    mask: str
+    scale: float  # softmax scale in terms of the real (dequantised) values
+    o_scale: float  # multiplier applied to O before the output conversion
+    seed: int
+    q_scale: float = 1.0  # fp8 dequantisation scales (1.0 otherwise)
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def kernel_scale(self) -> float:
+        """Softmax scale handed to the kernel, with the fp8 input scales folded in."""
+        return self.scale * self.q_scale * self.k_scale
+
+    @property
+    def kernel_o_scale(self) -> float:
+        return self.o_scale * self.v_scale
+
+    def flops(self) -> float:
+        """4*B*H*Sq*Sk*D, halved for the causal masks (the convention of the pages' benchmark)."""
+        f = 4.0 * self.B * self.H * self.Sq * self.Sk * self.D
+        return f / 2 if self.mask.startswith("causal") else f
+
+
+@dataclasses.dataclass
+class VarlenInputs:
+    q_buf: torch.Tensor  # [pad_q + total_q, H, D]; rows [pad_q, ...) are the packed sequences
+    k_buf: torch.Tensor  # [pad_k + total_k, H_kv, D]
+    v_buf: torch.Tensor
+    seqlens_q: np.ndarray  # int64 [B]
+    seqlens_k: np.ndarray
+    cu_q: np.ndarray  # int32 [B + 1], cu[0] = 0
+    cu_k: np.ndarray
+    pad_q: int
+    pad_k: int
+    H: int
+    H_kv: int
+    D: int
+    dtype: str
+    mask: str
+    scale: float
+    o_scale: float
+    seed: int
+    q_scale: float = 1.0
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def B(self) -> int:
+        return len(self.seqlens_q)
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_q[-1])
+
+    @property
+    def total_k(self) -> int:
+        return int(self.cu_k[-1])
+
+    @property
+    def max_q(self) -> int:
+        return int(self.seqlens_q.max()) if self.B else 0
+
+    @property
+    def max_k(self) -> int:
+        return int(self.seqlens_k.max()) if self.B else 0
+
+    @property
+    def q(self) -> torch.Tensor:
+        return self.q_buf[self.pad_q:]
+
+    @property
+    def k(self) -> torch.Tensor:
+        return self.k_buf[self.pad_k:]
+
+    @property
+    def v(self) -> torch.Tensor:
+        return self.v_buf[self.pad_k:]
+
+    @property
+    def kernel_scale(self) -> float:
+        return self.scale * self.q_scale * self.k_scale
+
+    @property
+    def kernel_o_scale(self) -> float:
+        return self.o_scale * self.v_scale
+
+    def new_output_buffer(self) -> torch.Tensor:
+        """O buffer with its own leading padding, every element set to the sentinel bits."""
+        rows = self.pad_q + self.total_q
+        bits = O_SENTINEL_BITS[self.dtype]
+        if ELEM_BYTES[self.dtype] == 1:
+            raw = torch.full((rows, self.H, self.D), bits, dtype=torch.uint8)
+        else:
+            raw = torch.full((rows, self.H, self.D), bits, dtype=torch.int16)
+        return raw.view(TORCH_DTYPES[self.dtype])
+
+    def flops_convention(self) -> float:
+        f = 4.0 * self.H * self.D * float(np.sum(self.seqlens_q.astype(np.float64) * self.seqlens_k))
+        return f / 2 if self.mask.startswith("causal") else f
+
+    def flops_exact(self) -> float:
+        """4*H*D times the number of (query, key) pairs the mask keeps."""
+        pairs = 0
+        for sq, sk in zip(self.seqlens_q.tolist(), self.seqlens_k.tolist()):
+            if self.mask == "causal_qbegin":
+                pairs += sum(min(sk, i + 1) for i in range(sq))
+            elif self.mask == "causal_qend":
+                off = sk - sq
+                pairs += sum(max(0, min(sk, i + off + 1)) for i in range(sq))
+            else:
+                pairs += sq * sk
+        return 4.0 * self.H * self.D * pairs
+
+
+def _dense_from_rng(rng, B, Sq, Sk, H, H_kv, D, dtype):
+    q, sq = _to_storage(draw_normal(rng, (B, Sq, H, D)), dtype)
+    k, sk = _to_storage(draw_normal(rng, (B, Sk, H_kv, D)), dtype)
+    v, sv = _to_storage(draw_normal(rng, (B, Sk, H_kv, D)), dtype)
+    return q, k, v, sq, sk, sv
+
+
+def make_dense(seed: int, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int, dtype: str,
+               mask: str = "none", scale: Optional[float] = None, o_scale: float = 1.0) -> DenseInputs:
+    rng = np.random.default_rng(seed)
+    q, k, v, sq, sk, sv = _dense_from_rng(rng, B, Sq, Sk, H, H_kv, D, dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return DenseInputs(q=q, k=k, v=v, B=B, Sq=Sq, Sk=Sk, H=H, H_kv=H_kv, D=D, dtype=dtype, mask=mask,
+                       scale=float(scale), o_scale=float(o_scale), seed=seed, q_scale=sq, k_scale=sk, v_scale=sv)
+
+
+def make_varlen(seed: int, seqlens_q: Sequence[int], seqlens_k: Sequence[int], H: int, H_kv: int, D: int,
+                dtype: str, mask: str = "none", scale: Optional[float] = None, o_scale: float = 1.0,
+                poison_pads: bool = False, rng: Optional[np.random.Generator] = None) -> VarlenInputs:
+    """Packed batch with explicit lengths.  ``rng`` continues a stream that already drew the lengths."""
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    lq = np.asarray(seqlens_q, dtype=np.int64)
+    lk = np.asarray(seqlens_k, dtype=np.int64)
+    assert lq.shape == lk.shape and lq.ndim == 1
+    cu_q = np.zeros(len(lq) + 1, dtype=np.int32)
+    cu_k = np.zeros(len(lk) + 1, dtype=np.int32)
+    cu_q[1:] = np.cumsum(lq)
+    cu_k[1:] = np.cumsum(lk)
+    pad_q = int(lq.max()) if len(lq) else 0
+    pad_k = int(lk.max()) if len(lk) else 0
+    q32 = draw_normal(rng, (pad_q + int(cu_q[-1]), H, D))
+    k32 = draw_normal(rng, (pad_k + int(cu_k[-1]), H_kv, D))
+    v32 = draw_normal(rng, (pad_k + int(cu_k[-1]), H_kv, D))
+    if dtype == "f8e4m3":
+        # quantise with the scale of the packed rows only, so the padding never changes the scales
+        q, sq = quantize_e4m3(torch.from_numpy(q32[pad_q:]))
+        k, sk = quantize_e4m3(torch.from_numpy(k32[pad_k:]))
+        v, sv = quantize_e4m3(torch.from_numpy(v32[pad_k:]))
+        qp = (torch.from_numpy(q32[:pad_q]) / sq).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+        kp = (torch.from_numpy(k32[:pad_k]) / sk).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+        vp = (torch.from_numpy(v32[:pad_k]) / sv).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+        q_buf, k_buf, v_buf = torch.cat([qp, q]), torch.cat([kp, k]), torch.cat([vp, v])
+    else:
+        q_buf = torch.from_numpy(q32).to(TORCH_DTYPES[dtype])
+        k_buf = torch.from_numpy(k32).to(TORCH_DTYPES[dtype])
+        v_buf = torch.from_numpy(v32).to(TORCH_DTYPES[dtype])
+        sq = sk = sv = 1.0
+    if poison_pads:
+        q_buf[:pad_q] = float("nan")
+        k_buf[:pad_k] = float("nan")
+        v_buf[:pad_k] = float("nan")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return VarlenInputs(q_buf=q_buf, k_buf=k_buf, v_buf=v_buf, seqlens_q=lq, seqlens_k=lk, cu_q=cu_q, cu_k=cu_k,
+                        pad_q=pad_q, pad_k=pad_k, H=H, H_kv=H_kv, D=D, dtype=dtype, mask=mask,
+                        scale=float(scale), o_scale=float(o_scale), seed=seed, q_scale=sq, k_scale=sk, v_scale=sv)
+
+
+# The five measured workloads.  Config 4 is run twice on the same inputs (residual, then causal-qend).
+CONFIGS = {
+    1: dict(name="tiny dense fp16 D64 no mask", kind="dense", B=1, H=2, H_kv=2, Sq=128, Sk=128, D=64,
+            dtype="f16", mask="none", lse=False, o_scale=1.0),
+    2: dict(name="prefill causal-qbegin bf16 D128 + LSE", kind="dense", B=4, H=16, H_kv=16, Sq=2048, Sk=2048,
+            D=128, dtype="bf16", mask="causal_qbegin", lse=True, o_scale=1.0),
+    3: dict(name="GQA causal long context bf16 D128", kind="dense", B=2, H=32, H_kv=8, Sq=8192, Sk=8192, D=128,
+            dtype="bf16", mask="causal_qbegin", lse=False, o_scale=1.0),
+    4: dict(name="packed varlen fp16 D64 residual / causal-qend", kind="varlen", nseq=8, sq_lo=64, sq_hi=1024,
+            sk_extra_hi=2048, H=16, H_kv=16, D=64, dtype="f16", masks=("residual", "causal_qend"), lse=False,
+            o_scale=1.0),
+    5: dict(name="fp8 e4m3 D128 no mask, output scale 0.5", kind="dense", B=8, H=16, H_kv=16, Sq=4096, Sk=4096,
+            D=128, dtype="f8e4m3", mask="none", lse=False, o_scale=0.5),
+}
+
+
+def make_config(config_id: int, seed: Optional[int] = None, mask: Optional[str] = None, poison_pads: bool = False):
+    c = CONFIGS[config_id]
+    seed = config_seed(config_id) if seed is None else seed
+    if c["kind"] == "dense":
+        return make_dense(seed, c["B"], c["Sq"], c["Sk"], c["H"], c["H_kv"], c["D"], c["dtype"],
+                          mask=mask or c["mask"], o_scale=c["o_scale"])
+    rng = np.random.default_rng(seed)
+    lq = rng.integers(c["sq_lo"], c["sq_hi"], size=c["nseq"], endpoint=True)
+    lk = lq + rng.integers(0, c["sk_extra_hi"], size=c["nseq"], endpoint=True)
+    return make_varlen(seed, lq, lk, c["H"], c["H_kv"], c["D"], c["dtype"], mask=mask or c["masks"][0],
+                       o_scale=c["o_scale"], poison_pads=poison_pads, rng=rng)
