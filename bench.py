@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+
+A step is one fmha_fwd call (the whole hot path) over one batch of seeded synthetic
+input already resident in device memory.  The default workload is the prefill
+causal-qbegin bf16 D=128 problem (B=4, H=16, S=2048, LSE written).  Rank 0 prints one
+JSON line with the throughput in TFLOP/s (4*B*H*Sq*Sk*D, halved for causal masks), the
+roofline of the kernel (FLOPs per launch over the average launch duration measured with
+HIP events on the launch stream, against MI355X's dense MFMA peak for the dtype), and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import head_attention_03_amd as fmha  # noqa: E402
+from workloads import CONFIGS, make_config, to_bits  # noqa: E402
+
+# MI355X published dense peaks (TFLOP/s): 256 CUs x 2.4 GHz x {4096 fp16/bf16, 8192 fp8} FLOP/clk/CU
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f8e4m3": 5033.2}
+KERNEL_SOURCE = os.path.join(ROOT, "head_attention_03_amd", "csrc", "fmha_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fmha_fwd_hbm_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(config_id: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on this kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("configs", {}).get(str(config_id))
+    if not entry or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(config_id: int, budget_s: float):
+    """The fp64 oracle as it stands, on whole (sequence, head) units of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    inp = make_config(config_id)
+    q = oracle.decode(to_bits(inp.q), inp.dtype) * inp.q_scale
+    k = oracle.decode(to_bits(inp.k), inp.dtype) * inp.k_scale
+    v = oracle.decode(to_bits(inp.v), inp.dtype) * inp.v_scale
+    group = inp.H // inp.H_kv
+    units = [(b, h) for b in range(inp.B) for h in range(inp.H)]
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    for b, h in units:
+        oracle.attention_head(q[b, :, h], k[b, :, h // group], v[b, :, h // group], inp.scale, inp.mask)
+        done += 1
+        flops += inp.flops() / len(units)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(units)} (sequence, head) units of the same workload, fp64 numpy, "
+                      f"{dt:.1f} s on {platform.processor() or platform.machine()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=sorted(CONFIGS))
+    ap.add_argument("--rotate", type=int, default=2, help="input buffer sets cycled through (defeats cache reuse)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU mode",
+              file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only; launch it without torch.distributed", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "needs a ROCm GPU"
+    fmha.load()
+
+    cid = args.config
+    c = CONFIGS[cid]
+    dev = torch.device("cuda:0")
+    inp = make_config(cid)
+    masks = [inp.mask] if c["kind"] == "dense" else list(c["masks"])
+    want_lse = bool(c["lse"])
+
+    # device buffers: `rotate` copies of the inputs, one output (and LSE) per copy
+    sets = []
+    for r in range(max(1, args.rotate)):
+        if c["kind"] == "dense":
+            q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+            o = torch.empty_like(q)
+            lse = torch.empty((inp.B, inp.H, inp.Sq), dtype=torch.float32, device=dev) if want_lse else None
+            sets.append(dict(q=q, k=k, v=v, o=o, lse=lse, varlen=None))
+        else:
+            q = inp.q_buf.to(dev)[inp.pad_q:]
+            k, v = inp.k_buf.to(dev)[inp.pad_k:], inp.v_buf.to(dev)[inp.pad_k:]
+            o = inp.new_output_buffer().to(dev)[inp.pad_q:]
+            cu_q, cu_k = torch.from_numpy(inp.cu_q).to(dev), torch.from_numpy(inp.cu_k).to(dev)
+            lse = torch.empty((inp.H, inp.total_q), dtype=torch.float32, device=dev) if want_lse else None
+            sets.append(dict(q=q, k=k, v=v, o=o, lse=lse, cu=(cu_q, cu_k),
+                             varlen=fmha.make_varlen(cu_q, cu_k, inp.total_q, inp.total_k)))
+    if c["kind"] == "dense":
+        B, Sq, Sk = inp.B, inp.Sq, inp.Sk
+        flops_step = inp.flops()
+    else:
+        B, Sq, Sk = inp.B, inp.max_q, inp.max_k
+        flops_step = 0.0
+        for m in masks:
+            inp.mask = m
+            flops_step += inp.flops_convention()
+
+    stream = torch.cuda.Stream(device=dev)  # default priority
+
+    def launch(i):
+        s = sets[i % len(sets)]
+        for m in masks:
+            st = fmha.fmha_fwd(s["q"], s["k"], s["v"], s["o"], s["lse"], B, Sq, Sk, inp.H, inp.H_kv, inp.D,
+                               inp.kernel_scale, m, inp.dtype, inp.kernel_o_scale, s["varlen"], stream)
+            if st != 0:
+                raise fmha.FmhaError(st)
+
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, each bracketed by HIP events recorded on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_launch_s = float(np.mean(launch_ms)) / 1e3 / len(masks)
+
+    value = flops_step * args.steps / elapsed / 1e12
+    achieved = flops_step / len(masks) / avg_launch_s / 1e12
+    peak = PEAK_TFLOPS[inp.dtype]
+    traffic = measured_traffic(cid)
+    cfg = {"workload": c["name"], "config_id": cid, "B": B, "Sq": Sq, "Sk": Sk, "H": inp.H, "H_kv": inp.H_kv,
+           "D": inp.D, "dtype": inp.dtype, "mask": "+".join(masks), "lse": want_lse, "seed": inp.seed,
+           "rotate_buffers": len(sets), "flop_per_step": flops_step}
+    out = {
+        "metric": "FMHA fwd TFLOP/s and % of MI355X dense MFMA peak (bf16, D=128, causal)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f16": "f16", "bf16": "bf16", "f8e4m3": "fp8_e4m3"}[inp.dtype],
+        "data": "synthetic (seeded N(0,1))",
+        "config": cfg,
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel_avg_us": round(avg_launch_s * 1e6, 3),
+                     "kernel_min_us": round(min(launch_ms) / len(masks) * 1e3, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cid, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,19 @@
+"""MI355X (gfx950) fused multi-head attention forward pass.
+
+The computation lives in libfmha.so (hand-written HIP, C ABI in include/fmha.h); this
+package only loads it and marshals arguments.
+"""
+from ._lib import (  # noqa: F401
+    DTYPES,
+    EXPORTS,
+    LIB_PATH,
+    MASKS,
+    FmhaError,
+    check,
+    fmha_fwd,
+    fmha_status_string,
+    fmha_varlen,
+    fmha_version,
+    load,
+    make_varlen,
+)

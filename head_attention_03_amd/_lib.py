@@ -1,0 +1,99 @@
+"""ctypes binding of libfmha.so: the C ABI of include/fmha.h, argument marshalling only.
+
+The functions keep the C names.  Pointers may be passed as integers or as any object
+with ``data_ptr()`` (a torch tensor); nothing here computes any part of the attention.
+Loading fails with an exception when the HIP library has not been built: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfmha.so")
+
+DTYPES = {"f16": 0, "bf16": 1, "f8e4m3": 2}
+MASKS = {"none": 0, "residual": 1, "causal_qbegin": 2, "causal_qend": 3}
+STATUS = {0: "FMHA_OK", 1: "FMHA_ERR_NULL_POINTER", 2: "FMHA_ERR_INVALID_SHAPE", 3: "FMHA_ERR_UNSUPPORTED",
+          4: "FMHA_ERR_MISALIGNED", 5: "FMHA_ERR_INVALID_ARGUMENT", 6: "FMHA_ERR_HIP"}
+# every symbol include/fmha.h declares
+EXPORTS = ("fmha_fwd", "fmha_status_string", "fmha_version")
+
+
+class FmhaError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"{STATUS.get(status, status)}: {fmha_status_string(status)}")
+        self.status = status
+
+
+class fmha_varlen(ctypes.Structure):
+    _fields_ = [("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+                ("total_length_q", ctypes.c_int32), ("total_length_k", ctypes.c_int32)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m head_attention_03_amd.build` "
+                          "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.fmha_fwd.restype = ctypes.c_int
+    lib.fmha_fwd.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int32] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.POINTER(fmha_varlen), ctypes.c_void_p]
+    lib.fmha_status_string.restype = ctypes.c_char_p
+    lib.fmha_status_string.argtypes = [ctypes.c_int]
+    lib.fmha_version.restype = ctypes.c_int32
+    lib.fmha_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    return int(x)
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        return None
+    if hasattr(s, "cuda_stream"):
+        return int(s.cuda_stream)
+    return int(s)
+
+
+def make_varlen(cu_seqlens_q, cu_seqlens_k, total_length_q: int, total_length_k: int) -> fmha_varlen:
+    return fmha_varlen(_ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(total_length_q), int(total_length_k))
+
+
+def fmha_fwd(q, k, v, o, lse, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int, scale: float, mask, dtype,
+             o_scale: float = 1.0, varlen: Optional[fmha_varlen] = None, stream=None) -> int:
+    """Call the C entry point; returns the fmha_status code.  ``mask``/``dtype`` take enum values or names."""
+    lib = load()
+    mask = MASKS[mask] if isinstance(mask, str) else int(mask)
+    dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    vl = ctypes.byref(varlen) if varlen is not None else None
+    return int(lib.fmha_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Sq), int(Sk), int(H),
+                            int(H_kv), int(D), float(scale), mask, dtype, float(o_scale), vl, _stream(stream)))
+
+
+def fmha_status_string(status: int) -> str:
+    return load().fmha_status_string(int(status)).decode()
+
+
+def fmha_version() -> int:
+    return int(load().fmha_version())
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise FmhaError(status)

@@ -1,0 +1,467 @@
+// Fused multi-head attention forward pass for gfx950 (AMD Instinct MI355X, CDNA4).
+//
+// O = softmax(scale * Q K^T + mask) V, computed one K/V tile at a time with an online
+// softmax, so S and P live only in registers (the method of the wingedge777 article
+// "[CUDA 优化实战] fmha sm120: 超越 torch.sdpa(flash-attention-2)", sections
+// "1. flash attention" and "2. fmha 实现").  Masks, packed variable-length batches, GQA
+// and the LSE output follow the CUTLASS Blackwell FMHA example as the trdm.cn
+// walk-through "CUTLASS Blackwell FMHA 示例完全解析" describes it (sections on the fusion
+// point fmha_fusion.hpp, variable sequence length, verification, GQA/MQA strides).
+//
+// CDNA4 design (the pages' TMA / ldmatrix / mma.sync machinery has no counterpart here):
+//
+// * One workgroup = 4 waves of 64 lanes = 128 query rows (32 per wave) of one
+//   (sequence, head).  K/V tiles of 64 keys stream through LDS, double buffered, filled
+//   by buffer loads that write LDS directly (no VGPR staging).  The buffer descriptor
+//   bounds every load to the rows of the current sequence: rows past the end read as 0,
+//   which is how ragged tails and packed sequences are handled without touching
+//   neighbouring memory.
+// * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_{bf16,f16}:
+//   A = 32 keys x 16 dims read from LDS, B = 16 dims x 32 queries held in VGPRs for the
+//   whole loop.  In the accumulator layout lane l then owns query l%32, and lanes l and
+//   l^32 together own all 32 keys of the block, so a row max or sum is an in-lane reduction
+//   plus one v_permlane32_swap.
+// * The same accumulator layout is, key for key, the B operand layout of the second
+//   product O^T += V^T P^T: the probabilities are converted in registers (v_cvt_pk_*)
+//   and fed straight back to the matrix cores (the counterpart of the article's section
+//   "Ps 寄存器重排").  The V^T operand comes from the row-major V tile through
+//   ds_read_b64_tr_b16 transpose reads.
+// * exp2 with scale*log2(e) folded into one FMA per score.  The running maximum is only
+//   raised when a tile's maximum exceeds it by more than 2^8 (a lazy rescale in the spirit
+//   of the article's section "lazy rescale": probabilities stay <= 256, far inside the
+//   range of the 16-bit and fp8 operand types, and the O rescale is skipped for most tiles).
+// * The row sum l accumulates the *rounded* probabilities that feed the matrix cores
+//   (v_dot2_f32_{bf16,f16} against 1.0), so the normalisation matches the numerator.
+// * Tiles are split into fully visible ones, which run no mask code, and boundary tiles
+//   (causal diagonal, ragged tail), the trip-count split of the CUTLASS fusion point.
+// * Work order: heaviest q-tiles first (causal), and workgroups of one (sequence, head
+//   group) land on the same XCD so they share K/V in that XCD's L2.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include <type_traits>
+
+#include "fmha.h"
+
+namespace fmha {
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+constexpr int kBN = 64;           // keys per K/V tile
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: raise the running max only past 2^8
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 buffer descriptor: raw 32-bit dwords
+
+enum : int { kF16 = 0, kBF16 = 1 };
+
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* cu_q;  // null for dense batches
+  const int32_t* cu_k;
+  int32_t B, Sq, Sk, H, H_kv, group;  // Sq / Sk: lengths (packed: maxima)
+  int32_t total_q;                    // packed: rows of q (LSE row length)
+  int32_t n_qtiles;
+  int32_t causal;   // 1 for both causal masks
+  int32_t qend;     // causal aligned to the last key
+  int32_t xcd_per;  // (sequence, head) pairs per XCD when B*H % 8 == 0, else 0
+  float scale_log2; // scale * log2(e)
+  float o_scale;
+};
+
+// ------------------------------------------------------------------------------------
+// device primitives
+// ------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+__device__ inline float wave_row_max(float x) {  // max of lanes l and l^32
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                            false, false);
+  return __builtin_fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ inline float wave_row_sum(float x) {  // sum of lanes l and l^32
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                            false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// 16-byte chunk swizzle of a K/V tile row j in LDS (CPR chunks per row).  Rows 0..15 map
+// to distinct chunks, so the 32-row b128 reads of K spread over all banks; four
+// consecutive rows move whole chunk pairs, so the 4-row transpose reads of V do too.
+template <int CPR>
+__device__ inline int swz(int j) {
+  return (2 * (j & 3) + ((j >> 2) & 1) + 8 * ((j >> 3) & 1)) & (CPR - 1);
+}
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<kBF16> {
+  typedef bf16x8 frag;
+  __device__ static inline uint32_t pack(float a, float b) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32, round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static inline float dot_one(uint32_t pk, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
+  }
+  __device__ static inline f32x16 mma(i32x4 a, i32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                  0, 0, 0);
+  }
+};
+template <>
+struct Elem<kF16> {
+  typedef f16x8 frag;
+  __device__ static inline uint32_t pack(float a, float b) {
+    f16x2 v = {(_Float16)a, (_Float16)b};  // v_cvt_pk_f16_f32, round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static inline float dot_one(uint32_t pk, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), one, acc, false);
+  }
+  __device__ static inline f32x16 mma(i32x4 a, i32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                 0, 0);
+  }
+};
+
+// ------------------------------------------------------------------------------------
+// the kernel (fp16 / bf16)
+// ------------------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads, 2) void fmha_fwd_kernel(const Params p) {
+  constexpr int E = 2;             // bytes per element
+  constexpr int RB = D * E;        // bytes per K/V row
+  constexpr int CPR = RB / 16;     // 16-byte chunks per row
+  constexpr int TILE = kBN * RB;   // bytes per K or V tile
+  constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
+  constexpr int NDB = D / 32;      // 32-wide blocks of the head dimension in O
+  constexpr int LOADS = TILE / (kThreads * 16);  // 16-byte LDS-direct loads per thread per tile
+  static_assert(LOADS >= 1 && TILE % (kThreads * 16) == 0, "tile must split into 16-byte loads");
+  typedef Elem<DT> T;
+
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [stage][K, V]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l32 = lane & 31;
+  const int h32 = lane >> 5;
+
+  // ---- which (sequence, head, q-tile) this workgroup owns ---------------------------
+  const int BH = p.B * p.H;
+  const int x = blockIdx.x;
+  int bh, qt_rev;
+  if (p.xcd_per) {  // round-robin dispatch puts workgroup x on XCD x % 8
+    const int slot = x >> 3;
+    qt_rev = slot / p.xcd_per;
+    bh = (x & 7) * p.xcd_per + slot % p.xcd_per;
+  } else {
+    qt_rev = x / BH;
+    bh = x % BH;
+  }
+  const int qt = p.n_qtiles - 1 - qt_rev;  // heaviest causal tiles first
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int kvh = h / p.group;
+
+  int q_row0, Sq_b, k_row0, Sk_b;
+  if (p.cu_q) {
+    q_row0 = p.cu_q[b];
+    Sq_b = p.cu_q[b + 1] - q_row0;
+    k_row0 = p.cu_k[b];
+    Sk_b = p.cu_k[b + 1] - k_row0;
+  } else {
+    q_row0 = b * p.Sq;
+    Sq_b = p.Sq;
+    k_row0 = b * p.Sk;
+    Sk_b = p.Sk;
+  }
+  const int q0 = qt * kBM;
+  if (q0 >= Sq_b) return;
+  const int off = p.qend ? Sk_b - Sq_b : 0;
+  int k_end = Sk_b;
+  if (p.causal) k_end = min(Sk_b, q0 + kBM + off);
+  const int n_tiles = k_end > 0 ? (k_end + kBN - 1) / kBN : 0;
+  int n_full = Sk_b / kBN;  // tiles every row of this workgroup sees completely
+  if (p.causal) n_full = min(n_full, q0 + off + 1 > 0 ? (q0 + off + 1) / kBN : 0);
+  n_full = min(n_full, n_tiles);
+
+  const uint32_t qstride = (uint32_t)p.H * D * E;     // bytes between rows of one head
+  const uint32_t kstride = (uint32_t)p.H_kv * D * E;
+  const size_t q_base = ((size_t)q_row0 * p.H + h) * D * E;
+  const size_t k_base = ((size_t)k_row0 * p.H_kv + kvh) * D * E;
+  const uint32_t q_bytes = Sq_b > 0 ? (uint32_t)(Sq_b - 1) * qstride + RB : 0;
+  const uint32_t k_bytes = Sk_b > 0 ? (uint32_t)(Sk_b - 1) * kstride + RB : 0;
+  const auto rq = make_rsrc((const char*)p.q + q_base, q_bytes);
+  const auto rk = make_rsrc((const char*)p.k + k_base, k_bytes);
+  const auto rv = make_rsrc((const char*)p.v + k_base, k_bytes);
+  const auto ro = make_rsrc((const char*)p.o + q_base, q_bytes);
+
+  // ---- Q fragment: B operand of S^T = K Q^T, lane owns query l32, dims 8*h32.. of each k-step
+  const int qi = q0 + wave * 32 + l32;  // query row inside the sequence
+  i32x4 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)qi * qstride + (16 * ks + 8 * h32) * E, 0, 0);
+
+  // ---- K/V tile loads straight into LDS -----------------------------------------------
+  auto issue_tile = [&](int t, int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int blk = i * kWaves + wave;  // which 1 KiB block of the tile this wave fills
+      const int pos = blk * 64 + lane;    // 16-byte chunk position in LDS
+      const int j = pos / CPR;
+      const int c = (pos % CPR) ^ swz<CPR>(j);
+      const uint32_t voff = (uint32_t)(t * kBN + j) * kstride + c * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)&smem[stage][0][blk * 1024], 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&smem[stage][1][blk * 1024], 16, voff, 0, 0, 0);
+    }
+  };
+
+  f32x16 acc_o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
+  float m_run = -__builtin_inff();  // running max of scale*log2(e)*s for query l32
+  float l_run = 0.0f;               // this lane's part of the row sum
+
+  const float sl2 = p.scale_log2;
+  const int qrow_vis = qi + off;  // last visible key of this query under a causal mask
+
+  // Per-lane LDS byte offsets.  The swizzle only touches chunk bits that the k-step (K) or
+  // the d-block (V) index leaves clear, so every read address is one of these bases XOR a
+  // compile-time constant, plus an immediate row offset.
+  const int k_lane = l32 * RB + ((h32 ^ swz<CPR>(l32)) * 16);
+  const int g16 = (lane >> 4) & 1;
+  const int s16 = lane & 15;
+  const int v_row0 = 4 * h32 + (s16 >> 2);  // row inside a 16-row group, first transpose read
+  const int v_part = 2 * g16 + ((s16 & 3) >> 1);
+  const int v_lane0 = v_row0 * RB + ((v_part ^ swz<CPR>(v_row0)) * 16) + 8 * (s16 & 1);
+  const int v_lane1 = (v_row0 + 8) * RB + ((v_part ^ swz<CPR>(v_row0 + 8)) * 16) + 8 * (s16 & 1);
+
+  auto step = [&](int t, const char* Ks, const char* Vs, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    int ka = k_lane, va0 = v_lane0, va1 = v_lane1;
+    asm volatile("" : "+v"(ka), "+v"(va0), "+v"(va1));  // keep derived addresses out of loop-invariant code
+    // S^T for two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      s[jb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const i32x4 a = *(const i32x4*)(Ks + 32 * jb * RB + (ka ^ (32 * ks)));
+        s[jb] = T::mma(a, qf[ks], s[jb]);
+      }
+    }
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = t * kBN + 32 * jb + (r >> 2) * 8 + 4 * h32 + (r & 3);
+          const bool vis = key < Sk_b && (!p.causal || key <= qrow_vis);
+          s[jb][r] = vis ? s[jb][r] : -__builtin_inff();
+        }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[jb][r]);
+    mx = wave_row_max(mx);
+    const float m_cand = mx * sl2;
+    if (__any(m_cand > m_run + kRescaleThreshold)) {
+      const float m_new = __builtin_fmaxf(m_run, m_cand);
+      const float alpha = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
+    // probabilities, packed in the B-operand order of the PV product
+    uint32_t pk[2][8];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][2 * q], sl2, -m_use));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][2 * q + 1], sl2, -m_use));
+        pk[jb][q] = T::pack(e0, e1);
+        l_run = T::dot_one(pk[jb][q], l_run);
+      }
+    // O^T += V^T P^T, 16 keys per MFMA
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const i32x4 bp = {(int)pk[jb][4 * c], (int)pk[jb][4 * c + 1], (int)pk[jb][4 * c + 2], (int)pk[jb][4 * c + 3]};
+        const int rows = (32 * jb + 16 * c) * RB;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + rows + (va0 ^ (64 * db))));
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + rows + (va1 ^ (64 * db))));
+          const i32x4 a = {__builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 0, 1)),
+                           __builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 2, 3)),
+                           __builtin_bit_cast(int, __builtin_shufflevector(v1, v1, 0, 1)),
+                           __builtin_bit_cast(int, __builtin_shufflevector(v1, v1, 2, 3))};
+          acc_o[db] = T::mma(a, bp, acc_o[db]);
+        }
+      }
+  };
+
+  // One barrier per tile: it publishes tile t (every wave waited for its own loads) and
+  // retires all reads of the other stage, which the loads of tile t + 1 then overwrite.
+  auto tile = [&](int t, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int STAGE = decltype(stage_tag)::value;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < n_tiles) issue_tile(t + 1, STAGE ^ 1);
+    if (t < n_full)
+      step(t, smem[STAGE][0], smem[STAGE][1], std::false_type{});
+    else
+      step(t, smem[STAGE][0], smem[STAGE][1], std::true_type{});
+  };
+  if (n_tiles > 0) issue_tile(0, 0);
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) tile(t + 1, std::integral_constant<int, 1>{});
+  }
+
+  // ---- epilogue: normalise, scale, convert, store rows inside the sequence -------------
+  const float l_tot = wave_row_sum(l_run);
+  const float inv = l_tot > 0.0f ? p.o_scale / l_tot : 0.0f;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * db + 8 * g + 4 * h32;
+      const i32x2 w = {(int)T::pack(acc_o[db][4 * g] * inv, acc_o[db][4 * g + 1] * inv),
+                       (int)T::pack(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv)};
+      __builtin_amdgcn_raw_buffer_store_b64(w, ro, (uint32_t)qi * qstride + d * E, 0, 0);
+    }
+  if (p.lse && h32 == 0 && qi < Sq_b) {
+    const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f
+                                   : -__builtin_inff();
+    const size_t idx = p.cu_q ? (size_t)h * p.total_q + q_row0 + qi : ((size_t)b * p.H + h) * p.Sq + qi;
+    p.lse[idx] = lse;
+  }
+}
+
+template <int DT, int D>
+hipError_t launch(const Params& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((fmha_fwd_kernel<DT, D>), dim3(grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace fmha
+
+// --------------------------------------------------------------------------------------
+// C ABI
+// --------------------------------------------------------------------------------------
+extern "C" {
+
+const char* fmha_status_string(fmha_status s) {
+  switch (s) {
+    case FMHA_OK: return "ok";
+    case FMHA_ERR_NULL_POINTER: return "null pointer (q, k, v, o, or only one of the cu_seqlens pointers)";
+    case FMHA_ERR_INVALID_SHAPE: return "invalid shape (negative size, H % H_kv != 0, D not in {32, 64, 128})";
+    case FMHA_ERR_UNSUPPORTED: return "unsupported (dtype or mask out of range, or tensor too large for 32-bit offsets)";
+    case FMHA_ERR_MISALIGNED: return "misaligned pointer (q, k, v, o need 16 bytes, lse needs 4)";
+    case FMHA_ERR_INVALID_ARGUMENT: return "invalid argument (scale must be finite and > 0, o_scale finite)";
+    case FMHA_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t fmha_version(void) { return 100; }
+
+fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Sq,
+                     int32_t Sk, int32_t H, int32_t H_kv, int32_t D, float scale, fmha_mask mask, fmha_dtype dtype,
+                     float o_scale, const fmha_varlen* varlen, hipStream_t stream) {
+  using namespace fmha;
+  const bool packed = varlen != nullptr;
+  const bool no_keys = packed ? varlen->total_length_k == 0 : Sk == 0;  // k and v may then be NULL
+  if (!q || !o || (!no_keys && (!k || !v))) return FMHA_ERR_NULL_POINTER;
+  if (packed && (!varlen->cu_seqlens_q != !varlen->cu_seqlens_k)) return FMHA_ERR_NULL_POINTER;
+  if (packed && !varlen->cu_seqlens_q) return FMHA_ERR_NULL_POINTER;
+  if (B < 0 || Sq < 0 || Sk < 0 || H < 0 || H_kv < 0) return FMHA_ERR_INVALID_SHAPE;
+  if (H > 0 && (H_kv < 1 || H % H_kv != 0)) return FMHA_ERR_INVALID_SHAPE;
+  if (D != 32 && D != 64 && D != 128) return FMHA_ERR_INVALID_SHAPE;
+  if (packed && (varlen->total_length_q < 0 || varlen->total_length_k < 0)) return FMHA_ERR_INVALID_SHAPE;
+  if ((int)dtype < 0 || (int)dtype > 2) return FMHA_ERR_UNSUPPORTED;
+  if ((int)mask < 0 || (int)mask > 3) return FMHA_ERR_UNSUPPORTED;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FMHA_ERR_MISALIGNED;
+  if ((uintptr_t)lse & 3) return FMHA_ERR_MISALIGNED;
+  if (!(scale > 0.0f) || !isfinite(scale) || !isfinite(o_scale)) return FMHA_ERR_INVALID_ARGUMENT;
+  if (dtype == FMHA_DTYPE_F8E4M3) return FMHA_ERR_UNSUPPORTED;
+
+  const int64_t esz = dtype == FMHA_DTYPE_F8E4M3 ? 1 : 2;
+  // every per-sequence byte offset must fit the 31-bit range of a buffer descriptor
+  const int64_t rows_q = packed ? varlen->total_length_q : Sq;
+  const int64_t rows_k = packed ? varlen->total_length_k : Sk;
+  const int64_t lim = (int64_t)1 << 31;
+  if (rows_q * H * D * esz >= lim || rows_k * H_kv * D * esz >= lim) return FMHA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || Sq == 0 || (packed && varlen->total_length_q == 0)) return FMHA_OK;
+
+  Params p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.cu_q = packed ? varlen->cu_seqlens_q : nullptr;
+  p.cu_k = packed ? varlen->cu_seqlens_k : nullptr;
+  p.B = B;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.H = H;
+  p.H_kv = H_kv;
+  p.group = H / H_kv;
+  p.total_q = packed ? varlen->total_length_q : 0;
+  p.n_qtiles = (Sq + kBM - 1) / kBM;
+  p.causal = mask == FMHA_MASK_CAUSAL_QBEGIN || mask == FMHA_MASK_CAUSAL_QEND;
+  p.qend = mask == FMHA_MASK_CAUSAL_QEND;
+  const int64_t BH = (int64_t)B * H;
+  const int64_t grid = BH * p.n_qtiles;
+  if (grid >= lim) return FMHA_ERR_UNSUPPORTED;
+  p.xcd_per = (BH % 8 == 0) ? (int32_t)(BH / 8) : 0;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.o_scale = o_scale;
+
+  hipError_t err = hipSuccess;
+  if (dtype == FMHA_DTYPE_BF16) {
+    if (D == 32) err = launch<kBF16, 32>(p, (int)grid, stream);
+    if (D == 64) err = launch<kBF16, 64>(p, (int)grid, stream);
+    if (D == 128) err = launch<kBF16, 128>(p, (int)grid, stream);
+  } else {
+    if (D == 32) err = launch<kF16, 32>(p, (int)grid, stream);
+    if (D == 64) err = launch<kF16, 64>(p, (int)grid, stream);
+    if (D == 128) err = launch<kF16, 128>(p, (int)grid, stream);
+  }
+  return err == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
+}
+
+}  // extern "C"

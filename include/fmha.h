@@ -1,0 +1,127 @@
+/*
+ * fmha.h -- fused multi-head attention forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libfmha.so.  One call computes, for every sequence b, query head h and
+ * query row i,
+ *
+ *     O[b, i, h, :] = o_scale * sum_j softmax_j(scale * Q[b, i, h, :] . K[b, j, h_kv, :] + mask) * V[b, j, h_kv, :]
+ *
+ * with h_kv = h / (H / H_kv), tile by tile with an online softmax, so the score and
+ * probability matrices never reach device memory.  This is the method of the
+ * wingedge777 article "[CUDA 优化实战] fmha sm120: 超越 torch.sdpa(flash-attention-2)"
+ * (sections "1. flash attention" and "2. fmha 实现"), with the masks, packed
+ * variable-length batches, GQA/MQA head sharing, LSE output and fp8 output scale of
+ * the CUTLASS Blackwell FMHA example (trdm.cn walk-through "CUTLASS Blackwell FMHA
+ * 示例完全解析", sections on the fusion point fmha_fusion.hpp, variable sequence
+ * length, verification and GQA/MQA strides; CUTLASS examples/77_blackwell_fmha
+ * README, "FMHA for Blackwell: Forward").
+ *
+ * Ownership: every pointer is device memory owned by the caller.  The library
+ * allocates nothing, keeps no pointer after a call returns and holds no mutable
+ * global state, so calls from several host threads are safe.  Work is enqueued on
+ * `stream` and runs asynchronously; errors inside the kernel surface at the
+ * caller's next synchronisation.
+ */
+#ifndef FMHA_H_
+#define FMHA_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V and O (all four share it). */
+typedef enum {
+  FMHA_DTYPE_F16 = 0,    /* IEEE binary16 */
+  FMHA_DTYPE_BF16 = 1,   /* bfloat16 */
+  FMHA_DTYPE_F8E4M3 = 2  /* OCP fp8 E4M3FN (largest finite 448, no infinities) */
+} fmha_dtype;
+
+/* Masks of the CUTLASS fusion point (trdm.cn walk-through, section on fmha_fusion.hpp).
+ * Every mask also hides the keys j >= Sk_b of the sequence.
+ *   NONE, RESIDUAL     query i sees every key j < Sk_b (identical results; RESIDUAL is
+ *                      kept for interface parity: partial last tiles are always masked)
+ *   CAUSAL_QBEGIN      query i sees key j iff j <= i                (top-left aligned)
+ *   CAUSAL_QEND        query i sees key j iff j <= i + (Sk_b - Sq_b) (bottom-right aligned)
+ * A query row that sees no key gets O = 0 and LSE = -inf. */
+typedef enum {
+  FMHA_MASK_NONE = 0,
+  FMHA_MASK_RESIDUAL = 1,
+  FMHA_MASK_CAUSAL_QBEGIN = 2,
+  FMHA_MASK_CAUSAL_QEND = 3
+} fmha_mask;
+
+typedef enum {
+  FMHA_OK = 0,
+  FMHA_ERR_NULL_POINTER = 1,     /* q, o, or (when there are keys) k or v is NULL, or only one
+                                    cu_seqlens pointer is set */
+  FMHA_ERR_INVALID_SHAPE = 2,    /* negative sizes, H % H_kv != 0, D not in {32, 64, 128}, totals < 0 */
+  FMHA_ERR_UNSUPPORTED = 3,      /* dtype/mask enum out of range, or a tensor too large for 32-bit offsets */
+  FMHA_ERR_MISALIGNED = 4,       /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
+  FMHA_ERR_INVALID_ARGUMENT = 5, /* scale not finite and > 0, or o_scale not finite */
+  FMHA_ERR_HIP = 6               /* the kernel launch failed (hipGetLastError) */
+} fmha_status;
+
+/* Packed variable-length batch, after CUTLASS's VariableLength {max_length,
+ * cumulative_length, total_length} (trdm.cn walk-through, section on variable
+ * sequence length).  Sequence b owns rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) of q
+ * and o and rows [cu_seqlens_k[b], cu_seqlens_k[b+1]) of k and v.
+ *   cu_seqlens_q, cu_seqlens_k  device int32 arrays of B + 1 entries, non-decreasing,
+ *                               entry 0 is 0 and entry B is the total; each length must
+ *                               not exceed the Sq / Sk passed to fmha_fwd (the maxima).
+ *                               They are read on the device only and cannot be checked.
+ *   total_length_q/k            number of packed rows (= cu_seqlens[B]); sizes of the LSE
+ *                               rows and the bound used for 32-bit offsets.
+ * The library reads and writes only rows inside [cu[b], cu[b+1]); padding the caller
+ * keeps around the packed rows is never touched. */
+typedef struct {
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int32_t total_length_q;
+  int32_t total_length_k;
+} fmha_varlen;
+
+/*
+ * fmha_fwd -- enqueue one attention forward pass.
+ *
+ *   q      [B, Sq, H, D]     dense, contiguous   |  [total_length_q, H, D]     packed
+ *   k, v   [B, Sk, H_kv, D]  dense, contiguous   |  [total_length_k, H_kv, D]  packed
+ *          (may be NULL when there are no keys: Sk == 0, or total_length_k == 0)
+ *   o      same shape as q, written (rows outside the sequences are left untouched)
+ *   lse    NULL, or fp32 [B, H, Sq] (dense) / [H, total_length_q] (packed):
+ *          natural-log log-sum-exp of scale * q.k over the visible keys (-inf if none)
+ *   B      number of sequences (>= 0);  Sq, Sk: lengths (packed: the maximum lengths)
+ *   H, H_kv  query heads and key/value heads, H % H_kv == 0 (H_kv == 1 is MQA)
+ *   D      head dimension: 32, 64 or 128
+ *   scale  softmax scale (finite, > 0), applied to q.k in fp32.  For fp8 inputs the
+ *          caller folds the per-tensor dequantisation scales of q and k into it.
+ *   mask   see fmha_mask
+ *   dtype  element type of q, k, v and o
+ *   o_scale  fp32 multiplier applied to the normalised output before the conversion to
+ *          dtype (fp8 output scale; for fp8 inputs the caller folds v's scale in).
+ *          fp8 outputs saturate to +-448; fp16/bf16 outputs round to nearest even.
+ *   varlen NULL for dense batches, else the packed description above
+ *   stream HIP stream the kernel is enqueued on (0 = the null stream)
+ *
+ * Validation happens on the host before anything is enqueued; on error nothing is
+ * launched and no memory is touched.  Sizes that give no work (B, H, Sq or a total
+ * of 0) return FMHA_OK without a launch.
+ */
+fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
+                     float scale, fmha_mask mask, fmha_dtype dtype, float o_scale,
+                     const fmha_varlen* varlen, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fmha_status_string(fmha_status status);
+
+/* Library version as 10000 * major + 100 * minor + patch. */
+int32_t fmha_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FMHA_H_ */

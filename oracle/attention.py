@@ -42,14 +42,15 @@ import numpy as np
 MASKS = ("none", "residual", "causal_qbegin", "causal_qend")
 
 
-def visible_keys(sq: int, sk: int, mask: str) -> np.ndarray:
-    """Boolean [sq, sk]: True where query i may attend to key j."""
+def visible_keys(sq: int, sk: int, mask: str, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Boolean [sq, sk] (or [len(rows), sk]): True where query i may attend to key j."""
     if mask not in MASKS:
         raise ValueError(f"unknown mask {mask!r}")
-    i = np.arange(sq)[:, None]
+    i = (np.arange(sq) if rows is None else np.asarray(rows))[:, None]
+    sq_rows = i.shape[0]
     j = np.arange(sk)[None, :]
     if mask in ("none", "residual"):
-        return np.ones((sq, sk), dtype=bool)
+        return np.ones((sq_rows, sk), dtype=bool)
     if mask == "causal_qbegin":
         return j <= i
     return j <= i + (sk - sq)
@@ -141,7 +142,7 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, ma
             qi = q[q0 + i:q0 + i + 1, h]
             kk, vv = k[k0:k1, kvh], v[k0:k1, kvh]
         # the row of the mask that belongs to query i of a [sq, sk] problem
-        vis = visible_keys(sq, sk, mask)[i]
+        vis = visible_keys(sq, sk, mask, rows=[i])[0]
         o_row, lse_row = attention_head(qi, kk[vis], vv[vis], scale, "none")
         o[n] = o_row[0]
         lse[n] = lse_row[0]

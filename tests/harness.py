@@ -1,0 +1,116 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI, run the oracle.
+
+The HIP side only ever sees device buffers and the C entry point; the oracle side only
+ever sees the generator's CPU tensors decoded to fp64.  The two meet in ``compare``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import sys
+from typing import Optional
+
+import numpy as np
+import torch
+
+import head_attention_03_amd as fmha
+import oracle
+from workloads import DenseInputs, VarlenInputs, to_bits
+from workloads.synth import ELEM_BYTES, TORCH_DTYPES
+
+# Tolerances stated for the method: max-abs error on O (and LSE) for 16-bit types, and on
+# the dequantised fp8 output for fp8 (CUTLASS's verification uses 1e-2 / 1e-1).
+TOL = {"f16": 1e-2, "bf16": 1e-2, "f8e4m3": 6e-2}
+LSE_TOL = 1e-2
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@dataclasses.dataclass
+class GpuResult:
+    o_bits: np.ndarray  # raw output bits (packed: the whole buffer including the padding)
+    lse: Optional[np.ndarray]
+    status: int
+
+
+def run_dense(inp: DenseInputs, want_lse: bool = False, stream=None, o_init_bits: Optional[int] = None) -> GpuResult:
+    dev = torch.device("cuda:0")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    if o_init_bits is None:
+        o = torch.empty_like(q)
+    else:
+        raw = torch.full(q.shape, o_init_bits, dtype=torch.uint8 if ELEM_BYTES[inp.dtype] == 1 else torch.int16)
+        o = raw.view(TORCH_DTYPES[inp.dtype]).to(dev)
+    lse = torch.empty((inp.B, inp.H, inp.Sq), dtype=torch.float32, device=dev) if want_lse else None
+    st = fmha.fmha_fwd(q, k, v, o, lse, inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D, inp.kernel_scale, inp.mask,
+                       inp.dtype, inp.kernel_o_scale, None,
+                       stream if stream is not None else torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return GpuResult(o_bits=to_bits(o.cpu()), lse=lse.cpu().numpy() if want_lse else None, status=st)
+
+
+def run_varlen(inp: VarlenInputs, want_lse: bool = False, stream=None) -> GpuResult:
+    dev = torch.device("cuda:0")
+    q_buf, k_buf, v_buf = inp.q_buf.to(dev), inp.k_buf.to(dev), inp.v_buf.to(dev)
+    o_buf = inp.new_output_buffer().to(dev)
+    cu_q = torch.from_numpy(inp.cu_q).to(dev)
+    cu_k = torch.from_numpy(inp.cu_k).to(dev)
+    lse = torch.empty((inp.H, max(inp.total_q, 1)), dtype=torch.float32, device=dev) if want_lse else None
+    vl = fmha.make_varlen(cu_q, cu_k, inp.total_q, inp.total_k)
+    st = fmha.fmha_fwd(q_buf[inp.pad_q:], k_buf[inp.pad_k:], v_buf[inp.pad_k:], o_buf[inp.pad_q:], lse, inp.B,
+                       inp.max_q, inp.max_k, inp.H, inp.H_kv, inp.D, inp.kernel_scale, inp.mask, inp.dtype,
+                       inp.kernel_o_scale, vl, stream if stream is not None else torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return GpuResult(o_bits=to_bits(o_buf.cpu()), lse=lse.cpu().numpy()[:, :inp.total_q] if want_lse else None,
+                     status=st)
+
+
+def decoded(inp, which: str) -> np.ndarray:
+    """fp64 values of an input tensor, dequantised for fp8."""
+    t = getattr(inp, which)
+    s = {"q": inp.q_scale, "k": inp.k_scale, "v": inp.v_scale}[which]
+    return oracle.decode(to_bits(t), inp.dtype) * s
+
+
+def oracle_dense(inp: DenseInputs):
+    return oracle.attention_dense(decoded(inp, "q"), decoded(inp, "k"), decoded(inp, "v"), inp.scale, inp.mask,
+                                  o_scale=inp.o_scale)
+
+
+def oracle_varlen(inp: VarlenInputs):
+    return oracle.attention_varlen(decoded(inp, "q"), decoded(inp, "k"), decoded(inp, "v"), inp.cu_q, inp.cu_k,
+                                   inp.scale, inp.mask, o_scale=inp.o_scale)
+
+
+def output_floor(expected: np.ndarray, dtype: str) -> float:
+    """max |round(O) - O|: the error of the best possible output in this format."""
+    if dtype == "f8e4m3":
+        t = torch.from_numpy(expected.astype(np.float32)).clamp(-448, 448).to(torch.float8_e4m3fn)
+    else:
+        t = torch.from_numpy(expected.astype(np.float32)).to(TORCH_DTYPES[dtype])
+    return float(np.abs(oracle.decode(to_bits(t), dtype) - expected).max()) if expected.size else 0.0
+
+
+def compare(name: str, got_bits: np.ndarray, dtype: str, expected: np.ndarray, got_lse=None, expected_lse=None,
+            tol: Optional[float] = None):
+    """Element-by-element check of the decoded GPU output against the oracle; returns the max error."""
+    tol = TOL[dtype] if tol is None else tol
+    got = oracle.decode(got_bits, dtype)
+    assert got.shape == expected.shape, (got.shape, expected.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite outputs"
+    err = float(np.abs(got - expected).max()) if got.size else 0.0
+    fl = output_floor(expected, dtype)
+    rel = float(np.linalg.norm(got - expected) / max(np.linalg.norm(expected), 1e-30)) if got.size else 0.0
+    msg = f"{name}: max|err| {err:.3e} (format floor {fl:.3e}, tol {tol:g}), rel fro {rel:.3e}"
+    if got_lse is not None:
+        fin = np.isfinite(expected_lse)
+        assert np.array_equal(fin, np.isfinite(got_lse)), f"{name}: LSE finiteness differs"
+        assert np.all(np.isneginf(got_lse[~fin])), f"{name}: rows without keys must have LSE = -inf"
+        lerr = float(np.abs(got_lse[fin] - expected_lse[fin]).max()) if fin.any() else 0.0
+        msg += f", lse max|err| {lerr:.3e}"
+        assert lerr <= LSE_TOL, msg
+    log(msg)
+    assert err <= tol, msg
+    return err

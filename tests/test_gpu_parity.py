@@ -1,0 +1,209 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on an MI355X.
+
+Small cases are compared element by element; the full-size configurations on sampled
+rows that the oracle computes one at a time.  Shapes span several q- and k-tiles with
+ragged tails; the packed-batch shapes follow the CUTLASS example's test list (zero-length
+sequences, tiny and non-divisible lengths, both causal alignments).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from harness import (TOL, compare, decoded, log, oracle_dense, oracle_varlen, run_dense, run_varlen)
+from workloads import make_config, make_dense, make_varlen, to_bits
+from workloads.synth import O_SENTINEL_BITS
+
+pytestmark = pytest.mark.gpu
+
+MASKS = ("none", "residual", "causal_qbegin", "causal_qend")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import head_attention_03_amd as fmha
+    fmha.load()  # fails loudly when libfmha.so is missing
+
+
+def _dense_case(name, inp, want_lse=True):
+    log(f"[case] {name} dtype={inp.dtype} B={inp.B} Sq={inp.Sq} Sk={inp.Sk} H={inp.H} H_kv={inp.H_kv} D={inp.D} "
+        f"mask={inp.mask} seed={inp.seed}")
+    res = run_dense(inp, want_lse=want_lse)
+    assert res.status == 0
+    o, lse = oracle_dense(inp)
+    compare(name, res.o_bits, inp.dtype, o, res.lse, lse if want_lse else None)
+    return res
+
+
+def test_config1_tiny():
+    _dense_case("config 1", make_config(1))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("mask", MASKS)
+def test_dense_masks_dims(dtype, D, mask):
+    inp = make_dense(2000 + D, 2, 200, 333, 4, 2, D, dtype, mask=mask)
+    _dense_case(f"dense {dtype} D{D} {mask}", inp)
+
+
+@pytest.mark.parametrize("mask", ["causal_qbegin", "causal_qend", "none"])
+def test_more_queries_than_keys(mask):
+    # under causal-qend the first Sq - Sk rows see no key: O = 0, LSE = -inf
+    inp = make_dense(2101, 1, 333, 200, 2, 2, 64, "bf16", mask=mask)
+    _dense_case(f"Sq>Sk {mask}", inp)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=1, H=1, H_kv=1, Sq=1013, Sk=1024, D=128, mask="causal_qend", dtype="f16"),
+    dict(B=2, H=4, H_kv=4, Sq=512, Sk=512, D=64, mask="none", dtype="f16"),
+    dict(B=2, H=4, H_kv=2, Sq=512, Sk=512, D=64, mask="causal_qbegin", dtype="bf16"),
+    dict(B=1, H=4, H_kv=4, Sq=512, Sk=512, D=128, mask="residual", dtype="bf16"),
+    dict(B=1, H=3, H_kv=1, Sq=77, Sk=1, D=64, mask="none", dtype="bf16"),
+    dict(B=3, H=2, H_kv=2, Sq=1, Sk=129, D=128, mask="causal_qend", dtype="f16"),
+    dict(B=1, H=2, H_kv=2, Sq=64, Sk=64, D=32, mask="causal_qbegin", dtype="f16"),
+])
+def test_edge_shapes(shape):
+    s = dict(shape)
+    inp = make_dense(2200, s.pop("B"), s.pop("Sq"), s.pop("Sk"), s.pop("H"), s.pop("H_kv"), s.pop("D"),
+                     s.pop("dtype"), mask=s.pop("mask"))
+    _dense_case(f"edge {shape}", inp)
+
+
+def test_no_keys_gives_zero_and_neg_inf():
+    inp = make_dense(2300, 1, 70, 0, 2, 2, 64, "f16", mask="none")
+    res = run_dense(inp, want_lse=True)
+    assert res.status == 0
+    assert not oracle.decode(res.o_bits, "f16").any()
+    assert np.all(np.isneginf(res.lse))
+
+
+def test_gqa_equals_mha_with_repeated_heads():
+    inp = make_dense(2400, 2, 300, 300, 8, 2, 128, "bf16", mask="causal_qbegin")
+    rep = make_dense(2400, 2, 300, 300, 8, 2, 128, "bf16", mask="causal_qbegin")
+    rep.k = inp.k.repeat_interleave(4, dim=2).contiguous()
+    rep.v = inp.v.repeat_interleave(4, dim=2).contiguous()
+    rep.H_kv = 8
+    a, b = run_dense(inp, want_lse=True), run_dense(rep, want_lse=True)
+    assert np.array_equal(a.o_bits, b.o_bits) and np.array_equal(a.lse, b.lse)
+
+
+def test_mqa():
+    _dense_case("mqa", make_dense(2450, 1, 257, 190, 6, 1, 64, "f16", mask="causal_qend"))
+
+
+def test_bitwise_repeatable():
+    inp = make_dense(2500, 2, 700, 900, 4, 4, 128, "bf16", mask="causal_qend")
+    runs = [run_dense(inp, want_lse=True) for _ in range(3)]
+    for r in runs[1:]:
+        assert np.array_equal(r.o_bits, runs[0].o_bits) and np.array_equal(r.lse, runs[0].lse)
+
+
+# ----------------------------------------------------------------------------------------------
+# packed variable-length batches
+# ----------------------------------------------------------------------------------------------
+def _varlen_case(name, inp, want_lse=True):
+    log(f"[case] {name} dtype={inp.dtype} seqlens_q={inp.seqlens_q.tolist()} seqlens_k={inp.seqlens_k.tolist()} "
+        f"H={inp.H} H_kv={inp.H_kv} D={inp.D} mask={inp.mask} seed={inp.seed}")
+    res = run_varlen(inp, want_lse=want_lse)
+    assert res.status == 0
+    o, lse = oracle_varlen(inp)
+    compare(name, res.o_bits[inp.pad_q:], inp.dtype, o, res.lse, lse if want_lse else None)
+    # the leading padding of O is never written
+    assert np.all(res.o_bits[:inp.pad_q] == O_SENTINEL_BITS[inp.dtype]), f"{name}: O padding was written"
+    return res
+
+
+@pytest.mark.parametrize("mask", ["residual", "causal_qend"])
+def test_config4_varlen(mask):
+    _varlen_case(f"config 4 {mask}", make_config(4, mask=mask))
+
+
+CMAKE_VARLEN = [
+    ([128], [128], 8, 4, 128, "none"),
+    ([256, 256, 256, 256], [256, 768, 512, 512], 4, 4, 128, "none"),
+    ([256, 256, 256, 256], [256, 0, 1280, 512], 4, 2, 64, "residual"),
+    ([256, 0, 512, 256], [256, 256, 512, 256], 4, 2, 64, "none"),
+    ([3, 2], [2, 5], 2, 2, 64, "none"),
+    ([17, 10], [13, 10], 2, 1, 128, "causal_qend"),
+    ([1], [1], 1, 1, 64, "causal_qbegin"),
+    ([177, 845], [257, 766], 4, 4, 128, "none"),
+    ([17], [257], 2, 2, 128, "causal_qbegin"),
+    ([17], [257], 2, 2, 128, "causal_qend"),
+    ([1013], [1024], 2, 2, 64, "causal_qend"),
+    ([1024], [1035], 2, 2, 32, "causal_qend"),
+]
+
+
+@pytest.mark.parametrize("case", CMAKE_VARLEN, ids=lambda c: f"q{c[0]}-k{c[1]}-{c[5]}-D{c[4]}")
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_varlen_shapes(case, dtype):
+    lq, lk, H, H_kv, D, mask = case
+    _varlen_case(f"varlen {lq}/{lk}", make_varlen(2600, lq, lk, H, H_kv, D, dtype, mask=mask))
+
+
+def test_varlen_poisoned_padding_never_read():
+    inp = make_varlen(2700, [100, 37, 250], [90, 300, 5], 4, 2, 64, "bf16", mask="causal_qend", poison_pads=True)
+    _varlen_case("varlen NaN pads", inp)
+
+
+def test_varlen_equals_dense_runs():
+    lq, lk = [130, 64, 7], [200, 64, 300]
+    inp = make_varlen(2800, lq, lk, 4, 2, 128, "bf16", mask="causal_qend")
+    packed = run_varlen(inp, want_lse=False)
+    for b in range(3):
+        qs = slice(int(inp.cu_q[b]), int(inp.cu_q[b + 1]))
+        ks = slice(int(inp.cu_k[b]), int(inp.cu_k[b + 1]))
+        dense = make_dense(0, 1, lq[b], lk[b], 4, 2, 128, "bf16", mask="causal_qend")
+        dense.q = inp.q[qs].unsqueeze(0).contiguous()
+        dense.k = inp.k[ks].unsqueeze(0).contiguous()
+        dense.v = inp.v[ks].unsqueeze(0).contiguous()
+        one = run_dense(dense)
+        assert np.array_equal(packed.o_bits[inp.pad_q + qs.start:inp.pad_q + qs.stop], one.o_bits[0])
+
+
+# ----------------------------------------------------------------------------------------------
+# full-size configurations, in the launch configuration the benchmark times, on sampled rows
+# ----------------------------------------------------------------------------------------------
+def _sample_rows(rng, B, H, Sq, n_random=192):
+    rows = {0, 1, 2, 31, 32, 63, 64, 127, 128, 129, Sq // 2, Sq - 129, Sq - 128, Sq - 2, Sq - 1}
+    picks = [(b, h, i) for b in range(B) for h in (0, H - 1) for i in sorted(rows) if 0 <= i < Sq]
+    picks += [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(Sq))) for _ in range(n_random)]
+    return picks
+
+
+@pytest.mark.parametrize("config_id", [2, 3])
+def test_full_size_config_sampled(config_id):
+    inp = make_config(config_id)
+    want_lse = config_id == 2
+    log(f"[case] full config {config_id}: {inp.dtype} B={inp.B} S={inp.Sq} H={inp.H}/{inp.H_kv} D={inp.D} "
+        f"{inp.mask} seed={inp.seed}")
+    res = run_dense(inp, want_lse=want_lse)
+    assert res.status == 0
+    picks = _sample_rows(np.random.default_rng(inp.seed), inp.B, inp.H, inp.Sq)
+    o_exp, lse_exp = oracle.attention_rows(decoded(inp, "q"), decoded(inp, "k"), decoded(inp, "v"), inp.scale,
+                                           inp.mask, picks, o_scale=inp.o_scale)
+    got = np.stack([res.o_bits[b, i, h] for b, h, i in picks])
+    got_lse = np.array([res.lse[b, h, i] for b, h, i in picks]) if want_lse else None
+    compare(f"config {config_id} sampled {len(picks)} rows", got, inp.dtype, o_exp, got_lse,
+            lse_exp if want_lse else None)
+
+
+# ----------------------------------------------------------------------------------------------
+# negative control: an oracle with a planted mistake must disagree with the HIP path
+# ----------------------------------------------------------------------------------------------
+def test_planted_oracle_mistake_is_detected():
+    inp = make_dense(2900, 1, 256, 256, 2, 2, 64, "f16", mask="causal_qbegin")
+    res = run_dense(inp)
+    q, k, v = decoded(inp, "q"), decoded(inp, "k"), decoded(inp, "v")
+    # diagonal dropped: query i sees only keys j < i
+    wrong = np.zeros_like(q)
+    for h in range(2):
+        s = inp.scale * q[0, :, h] @ k[0, :, h].T
+        vis = np.tril(np.ones((256, 256), bool), -1)
+        vis[0, 0] = True
+        e = np.where(vis, np.exp(s - np.where(vis, s, -np.inf).max(1, keepdims=True)), 0)
+        wrong[0, :, h] = (e / e.sum(1, keepdims=True)) @ v[0, :, h]
+    err = np.abs(oracle.decode(res.o_bits, "f16") - wrong).max()
+    assert err > 10 * TOL["f16"], err
