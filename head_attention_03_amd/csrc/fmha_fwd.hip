@@ -56,12 +56,16 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per K/V tile
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: raise the running max only past 2^8
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 buffer descriptor: raw 32-bit dwords
+constexpr int kSchedMfma = 0x008;    // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedDsRead = 0x100;
+constexpr int kPrefetch = 6;         // LDS reads kept in flight ahead of the MFMAs
+constexpr int kWaitVmcnt0 = 0x0F70;           // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima
 
 enum : int { kF16 = 0, kBF16 = 1 };
 
@@ -93,6 +97,30 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
 }
 
+// Same descriptor as raw SGPR words, for the inline-asm LDS-direct load below.
+__device__ inline i32x4 make_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const i32x4 r = {__builtin_amdgcn_readfirstlane((int)(uint32_t)a), __builtin_amdgcn_readfirstlane((int)(a >> 32)),
+                   __builtin_amdgcn_readfirstlane((int)bytes), (int)kRsrcWord3};
+  return r;
+}
+
+// 16 bytes per lane from a buffer straight into LDS at lds_addr + 16 * lane (lds_addr is
+// wave-uniform).  Written as inline asm so the compiler does not track it: it would
+// otherwise wait for these loads before LDS reads it cannot prove disjoint, which undoes the
+// prefetch; the phase schedule waits for them explicitly.  M0 is saved and restored.
+__device__ inline void lds_load16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(lds_addr)
+      : "memory");
+}
+
 __device__ inline float wave_row_max(float x) {  // max of lanes l and l^32
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
                                             false, false);
@@ -102,6 +130,16 @@ __device__ inline float wave_row_sum(float x) {  // sum of lanes l and l^32
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
                                             false, false);
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Workgroup barrier for the phase schedule.  Unlike __syncthreads() it carries no release
+// fence, which would also wait for the K/V loads still in flight for a later phase; the only
+// ordering needed is that this wave's LDS reads have returned (lgkmcnt(0)) before another
+// wave may overwrite the buffer, and the loads are waited for explicitly (vmcnt) where due.
+__device__ inline void phase_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // 16-byte chunk swizzle of a K/V tile row j in LDS (CPR chunks per row).  Rows 0..15 map
@@ -150,24 +188,39 @@ struct Elem<kF16> {
 // ------------------------------------------------------------------------------------
 // the kernel (fp16 / bf16)
 // ------------------------------------------------------------------------------------
+// Phase schedule.  The 8 waves form two groups, A = waves 0-3 and B = waves 4-7, so every
+// SIMD holds one wave of each.  Time is cut into phases separated by workgroup barriers.
+// In phase 2t group A runs the matrix work of tile t (S(t) = K(t) Q^T and O += V(t-1) P(t-1))
+// while group B runs the softmax of tile t-1; in phase 2t+1 the roles swap.  Each SIMD thus
+// always has one wave feeding its matrix core and one wave on the vector ALU (the two-tile
+// ping-pong of the CUTLASS design, built here from the single workgroup barrier).
+// K(t+1) and V(t) are requested at the start of phase 2t and waited for at the end of phase
+// 2t+1, two phases ahead of their first use.
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads, 2) void fmha_fwd_kernel(const Params p) {
+__global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   constexpr int E = 2;             // bytes per element
   constexpr int RB = D * E;        // bytes per K/V row
   constexpr int CPR = RB / 16;     // 16-byte chunks per row
   constexpr int TILE = kBN * RB;   // bytes per K or V tile
   constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
   constexpr int NDB = D / 32;      // 32-wide blocks of the head dimension in O
-  constexpr int LOADS = TILE / (kThreads * 16);  // 16-byte LDS-direct loads per thread per tile
-  static_assert(LOADS >= 1 && TILE % (kThreads * 16) == 0, "tile must split into 16-byte loads");
+  constexpr int BLOCKS = TILE / 1024;  // 1 KiB blocks per tile: one LDS-direct load of one wave each
+  static_assert(TILE % 1024 == 0, "tile must split into 1 KiB blocks");
   typedef Elem<DT> T;
 
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [stage][K, V]
+  // Four separate LDS objects (K and V, two stages): the compiler can then tell that the
+  // loads filling one stage never alias the reads of the other, and inserts no wait for them.
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int l32 = lane & 31;
   const int h32 = lane >> 5;
+  const int group = wave >> 2;             // 0 = A, 1 = B
+  const int rblk = 2 * (wave & 3) + group; // 32-row block of the workgroup tile owned by this wave
 
   // ---- which (sequence, head, q-tile) this workgroup owns ---------------------------
   const int BH = p.B * p.H;
@@ -201,12 +254,20 @@ __global__ __launch_bounds__(kThreads, 2) void fmha_fwd_kernel(const Params p) {
   const int q0 = qt * kBM;
   if (q0 >= Sq_b) return;
   const int off = p.qend ? Sk_b - Sq_b : 0;
-  int k_end = Sk_b;
-  if (p.causal) k_end = min(Sk_b, q0 + kBM + off);
-  const int n_tiles = k_end > 0 ? (k_end + kBN - 1) / kBN : 0;
-  int n_full = Sk_b / kBN;  // tiles every row of this workgroup sees completely
-  if (p.causal) n_full = min(n_full, q0 + off + 1 > 0 ? (q0 + off + 1) / kBN : 0);
-  n_full = min(n_full, n_tiles);
+  // keys visible to the last valid row of a row range, as an exclusive end
+  auto key_end = [&](int last_row) { return p.causal ? min(Sk_b, last_row + off + 1) : Sk_b; };
+  const int wg_end = key_end(min(Sq_b, q0 + kBM) - 1);
+  const int n_tiles = wg_end > 0 ? (wg_end + kBN - 1) / kBN : 0;
+  // per wave: the last tile holding a key any of its valid rows sees, and the first tile
+  // that some row of the wave does not see completely (mask needed from there on)
+  const int qw0 = q0 + 32 * rblk;
+  int w_last = -1, w_full = 0;
+  if (qw0 < Sq_b) {
+    const int e = key_end(min(Sq_b, qw0 + 32) - 1);
+    w_last = e > 0 ? (e - 1) / kBN : -1;
+    const int first_sees = p.causal ? min(Sk_b, qw0 + off + 1) : Sk_b;
+    w_full = first_sees > 0 ? first_sees / kBN : 0;
+  }
 
   const uint32_t qstride = (uint32_t)p.H * D * E;     // bytes between rows of one head
   const uint32_t kstride = (uint32_t)p.H_kv * D * E;
@@ -215,39 +276,45 @@ __global__ __launch_bounds__(kThreads, 2) void fmha_fwd_kernel(const Params p) {
   const uint32_t q_bytes = Sq_b > 0 ? (uint32_t)(Sq_b - 1) * qstride + RB : 0;
   const uint32_t k_bytes = Sk_b > 0 ? (uint32_t)(Sk_b - 1) * kstride + RB : 0;
   const auto rq = make_rsrc((const char*)p.q + q_base, q_bytes);
-  const auto rk = make_rsrc((const char*)p.k + k_base, k_bytes);
-  const auto rv = make_rsrc((const char*)p.v + k_base, k_bytes);
+  const i32x4 rk = make_rsrc_words((const char*)p.k + k_base, k_bytes);
+  const i32x4 rv = make_rsrc_words((const char*)p.v + k_base, k_bytes);
   const auto ro = make_rsrc((const char*)p.o + q_base, q_bytes);
 
   // ---- Q fragment: B operand of S^T = K Q^T, lane owns query l32, dims 8*h32.. of each k-step
-  const int qi = q0 + wave * 32 + l32;  // query row inside the sequence
+  const int qi = qw0 + l32;  // query row inside the sequence
   i32x4 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     qf[ks] = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)qi * qstride + (16 * ks + 8 * h32) * E, 0, 0);
+  // Wait for Q here with the builtin (whose effect the compiler tracks): otherwise it keeps
+  // partial vmcnt waits for Q inside the loop, and those would also stall on the K/V loads.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  // ---- K/V tile loads straight into LDS -----------------------------------------------
-  auto issue_tile = [&](int t, int stage) __attribute__((always_inline)) {
+  // ---- K/V tile loads straight into LDS: wave w fills 1 KiB blocks w, w + 8, ... --------
+  auto issue = [&](i32x4 rsrc, int t, char* dst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int blk = i * kWaves + wave;  // which 1 KiB block of the tile this wave fills
-      const int pos = blk * 64 + lane;    // 16-byte chunk position in LDS
-      const int j = pos / CPR;
-      const int c = (pos % CPR) ^ swz<CPR>(j);
-      const uint32_t voff = (uint32_t)(t * kBN + j) * kstride + c * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)&smem[stage][0][blk * 1024], 16, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&smem[stage][1][blk * 1024], 16, voff, 0, 0, 0);
+    for (int blk0 = 0; blk0 < BLOCKS; blk0 += kWaves) {
+      const int blk = blk0 + wave;
+      if (BLOCKS % kWaves == 0 || blk < BLOCKS) {
+        const int pos = blk * 64 + lane;  // 16-byte chunk position in LDS
+        const int j = pos / CPR;
+        const int c = (pos % CPR) ^ swz<CPR>(j);
+        const uint32_t voff = (uint32_t)(t * kBN + j) * kstride + c * 16;
+        const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void*)(dst + blk * 1024);
+        lds_load16(rsrc, voff, __builtin_amdgcn_readfirstlane(lds_addr));
+      }
     }
   };
 
   f32x16 acc_o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
+  f32x16 s[2];                      // scores of the tile between its matrix and softmax phases
+  uint32_t pk[2][8];                // probabilities of the tile between its softmax and PV phases
   float m_run = -__builtin_inff();  // running max of scale*log2(e)*s for query l32
   float l_run = 0.0f;               // this lane's part of the row sum
-
   const float sl2 = p.scale_log2;
-  const int qrow_vis = qi + off;  // last visible key of this query under a causal mask
+  const int qrow_vis = qi + off;    // last visible key of this query under a causal mask
 
   // Per-lane LDS byte offsets.  The swizzle only touches chunk bits that the k-step (K) or
   // the d-block (V) index leaves clear, so every read address is one of these bases XOR a
@@ -260,22 +327,84 @@ __global__ __launch_bounds__(kThreads, 2) void fmha_fwd_kernel(const Params p) {
   const int v_lane0 = v_row0 * RB + ((v_part ^ swz<CPR>(v_row0)) * 16) + 8 * (s16 & 1);
   const int v_lane1 = (v_row0 + 8) * RB + ((v_part ^ swz<CPR>(v_row0 + 8)) * 16) + 8 * (s16 & 1);
 
-  auto step = [&](int t, const char* Ks, const char* Vs, auto masked_tag) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // one QK^T MFMA of the tile: k-step ks of key block jb
+  auto qk_mma = [&](const char* Ks, int ka, int i) __attribute__((always_inline)) {
+    const int jb = i & 1, ks = i >> 1;
+    const i32x4 a = *(const i32x4*)(Ks + 32 * jb * RB + (ka ^ (32 * ks)));
+    s[jb] = T::mma(a, qf[ks], s[jb]);
+  };
+  // one PV MFMA: d-block db, 16-key chunk (jb, c)
+  auto pv_mma = [&](const char* Vs, int va0, int va1, int i) __attribute__((always_inline)) {
+    const int db = i % NDB, jc = i / NDB, jb = jc >> 1, c = jc & 1;
+    const int rows = (32 * jb + 16 * c) * RB;
+    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + rows + (va0 ^ (64 * db))));
+    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + rows + (va1 ^ (64 * db))));
+    const i32x4 a = {__builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 0, 1)),
+                     __builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 2, 3)),
+                     __builtin_bit_cast(int, __builtin_shufflevector(v1, v1, 0, 1)),
+                     __builtin_bit_cast(int, __builtin_shufflevector(v1, v1, 2, 3))};
+    const i32x4 bp = {(int)pk[jb][4 * c], (int)pk[jb][4 * c + 1], (int)pk[jb][4 * c + 2], (int)pk[jb][4 * c + 3]};
+    acc_o[db] = T::mma(a, bp, acc_o[db]);
+  };
+  constexpr int NQK = 2 * KS;   // MFMAs of S^T for one tile
+  constexpr int NPV = 4 * NDB;  // MFMAs of O^T += V^T P^T for one tile
+
+  // matrix phase of tile t: S(t) (if t is a tile of this wave) and O += V(t-1) P(t-1)
+  auto matrix_phase = [&](int t, const char* Ks, const char* Vs) __attribute__((always_inline)) {
+    const bool do_qk = t < n_tiles && t <= w_last;
+    const bool do_pv = t >= 1 && t - 1 <= w_last;
     int ka = k_lane, va0 = v_lane0, va1 = v_lane1;
     asm volatile("" : "+v"(ka), "+v"(va0), "+v"(va1));  // keep derived addresses out of loop-invariant code
-    // S^T for two 32-key blocks
-    f32x16 s[2];
+    if (do_qk) {
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+    }
+    // The LDS reads run kPrefetch reads ahead of the MFMAs that consume them (pinned with
+    // scheduling groups: the compiler alone keeps only one or two in flight, which leaves
+    // the matrix core waiting on LDS latency).
+    if (do_qk && do_pv) {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      s[jb] = f32x16{};
+      for (int i = 0; i < (NQK > NPV ? NQK : NPV); ++i) {
+        if (i < NQK) qk_mma(Ks, ka, i);
+        if (i < NPV) pv_mma(Vs, va0, va1, i);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const i32x4 a = *(const i32x4*)(Ks + 32 * jb * RB + (ka ^ (32 * ks)));
-        s[jb] = T::mma(a, qf[ks], s[jb]);
+      for (int i = 0; i < (NQK > NPV ? NQK : NPV); ++i) {
+        if (i < NQK) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        if (i < NPV) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+      }
+    } else if (do_qk) {
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) qk_mma(Ks, ka, i);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+    } else if (do_pv) {
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) pv_mma(Vs, va0, va1, i);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
     }
-    if constexpr (MASKED) {
+  };
+
+  // softmax phase of tile t: mask, running max, lazy rescale, probabilities
+  auto softmax_phase = [&](int t) __attribute__((always_inline)) {
+    if (t >= n_tiles || t > w_last) return;
+    if (t >= w_full) {
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
@@ -301,8 +430,6 @@ __global__ __launch_bounds__(kThreads, 2) void fmha_fwd_kernel(const Params p) {
       m_run = m_new;
     }
     const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
-    // probabilities, packed in the B-operand order of the PV product
-    uint32_t pk[2][8];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
@@ -312,42 +439,53 @@ __global__ __launch_bounds__(kThreads, 2) void fmha_fwd_kernel(const Params p) {
         pk[jb][q] = T::pack(e0, e1);
         l_run = T::dot_one(pk[jb][q], l_run);
       }
-    // O^T += V^T P^T, 16 keys per MFMA
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const i32x4 bp = {(int)pk[jb][4 * c], (int)pk[jb][4 * c + 1], (int)pk[jb][4 * c + 2], (int)pk[jb][4 * c + 3]};
-        const int rows = (32 * jb + 16 * c) * RB;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + rows + (va0 ^ (64 * db))));
-          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + rows + (va1 ^ (64 * db))));
-          const i32x4 a = {__builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 0, 1)),
-                           __builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 2, 3)),
-                           __builtin_bit_cast(int, __builtin_shufflevector(v1, v1, 0, 1)),
-                           __builtin_bit_cast(int, __builtin_shufflevector(v1, v1, 2, 3))};
-          acc_o[db] = T::mma(a, bp, acc_o[db]);
-        }
-      }
   };
 
-  // One barrier per tile: it publishes tile t (every wave waited for its own loads) and
-  // retires all reads of the other stage, which the loads of tile t + 1 then overwrite.
-  auto tile = [&](int t, auto stage_tag) __attribute__((always_inline)) {
-    constexpr int STAGE = decltype(stage_tag)::value;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(t + 1, STAGE ^ 1);
-    if (t < n_full)
-      step(t, smem[STAGE][0], smem[STAGE][1], std::false_type{});
-    else
-      step(t, smem[STAGE][0], smem[STAGE][1], std::true_type{});
+  // this wave's work in a phase whose index (within its own schedule) is my = 4u + M
+  auto act = [&](int my, auto m_tag) __attribute__((always_inline)) {
+    constexpr int M = decltype(m_tag)::value;
+    const int t = my >> 1;
+    if constexpr (M % 2 == 0) {
+      // K(t) sits in stage t % 2 = M / 2, V(t - 1) in the other stage.  The matrix work runs
+      // at raised wave priority so the SIMD issues its MFMAs ahead of the softmax VALU work
+      // of the other group's wave.
+      __builtin_amdgcn_s_setprio(1);
+      if constexpr (M / 2 == 0)
+        matrix_phase(t, k_lds0, v_lds1);
+      else
+        matrix_phase(t, k_lds1, v_lds0);
+      __builtin_amdgcn_s_setprio(0);
+    } else {
+      softmax_phase(t);
+    }
   };
-  if (n_tiles > 0) issue_tile(0, 0);
-  for (int t = 0; t < n_tiles; t += 2) {
-    tile(t, std::integral_constant<int, 0>{});
-    if (t + 1 < n_tiles) tile(t + 1, std::integral_constant<int, 1>{});
+
+  const int n_phases = 2 * n_tiles + 2;
+  auto phase = [&](int ph, auto k_tag) __attribute__((always_inline)) {
+    constexpr int K = decltype(k_tag)::value;  // ph % 4
+    if constexpr (K % 2 == 0) {
+      const int t = ph >> 1;  // t % 2 == K / 2
+      if (t + 1 < n_tiles) issue(rk, t + 1, K / 2 == 0 ? k_lds1 : k_lds0);
+      if (t < n_tiles) issue(rv, t, K / 2 == 0 ? v_lds0 : v_lds1);
+    }
+    if (group == 0)
+      act(ph, std::integral_constant<int, K>{});
+    else if (ph >= 1)
+      act(ph - 1, std::integral_constant<int, (K + 3) % 4>{});
+    if constexpr (K % 2 == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    phase_barrier();
+  };
+
+  if (n_tiles > 0) issue(rk, 0, k_lds0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  phase_barrier();
+  for (int ph = 0; ph < n_phases; ph += 4) {
+    phase(ph, std::integral_constant<int, 0>{});
+    phase(ph + 1, std::integral_constant<int, 1>{});
+    if (ph + 2 < n_phases) {
+      phase(ph + 2, std::integral_constant<int, 2>{});
+      phase(ph + 3, std::integral_constant<int, 3>{});
+    }
   }
 
   // ---- epilogue: normalise, scale, convert, store rows inside the sequence -------------
@@ -369,7 +507,6 @@ __global__ __launch_bounds__(kThreads, 2) void fmha_fwd_kernel(const Params p) {
     p.lse[idx] = lse;
   }
 }
-
 template <int DT, int D>
 hipError_t launch(const Params& p, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((fmha_fwd_kernel<DT, D>), dim3(grid), dim3(kThreads), 0, stream, p);
