@@ -92,6 +92,7 @@ struct Params {
 // ------------------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
@@ -108,7 +109,9 @@ __device__ inline i32x4 make_rsrc_words(const void* base, uint32_t bytes) {
 // 16 bytes per lane from a buffer straight into LDS at lds_addr + 16 * lane (lds_addr is
 // wave-uniform).  Written as inline asm so the compiler does not track it: it would
 // otherwise wait for these loads before LDS reads it cannot prove disjoint, which undoes the
-// prefetch; the phase schedule waits for them explicitly.  M0 is saved and restored.
+// prefetch; the phase schedule waits for them explicitly.  No memory clobber: the LDS reads
+// of the current stage may move across it (it only ever writes the other stage), while the
+// volatile asm statements (loads, waits, barriers) keep their order.  M0 is saved and restored.
 __device__ inline void lds_load16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
   int saved;
   asm volatile(
@@ -117,8 +120,7 @@ __device__ inline void lds_load16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr) 
       "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(voff), "s"(rsrc), "s"(lds_addr)
-      : "memory");
+      : "v"(voff), "s"(rsrc), "s"(lds_addr));
 }
 
 __device__ inline float wave_row_max(float x) {  // max of lanes l and l^32
@@ -140,6 +142,13 @@ __device__ inline void phase_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N)
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // 16-byte chunk swizzle of a K/V tile row j in LDS (CPR chunks per row).  Rows 0..15 map
@@ -199,24 +208,30 @@ struct Elem<kF16> {
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   constexpr int E = 2;             // bytes per element
-  constexpr int RB = D * E;        // bytes per K/V row
+  constexpr int RB = D * E;        // bytes per K/V row, in memory and in LDS (swizzled)
   constexpr int CPR = RB / 16;     // 16-byte chunks per row
-  constexpr int TILE = kBN * RB;   // bytes per K or V tile
+  constexpr int TILE = kBN * RB;   // LDS bytes per K or V tile
+  constexpr int KBLK = TILE / 1024;  // 1 KiB LDS-direct loads (64 lanes x 16 B) per K or V tile
+  constexpr int NBLK = 2 * KBLK;
+  constexpr int NSTAGE = 3;          // K/V tile pairs resident in LDS: in use, landed, landing
+  constexpr int STAGE = 2 * TILE;    // LDS bytes per stage: K tile, then V tile
+  constexpr int LPP = (NBLK + 15) / 16;  // loads one wave issues per phase
+  static_assert(NBLK % 8 == 0, "every wave issues the same number of tile loads");
   constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
   constexpr int NDB = D / 32;      // 32-wide blocks of the head dimension in O
-  constexpr int BLOCKS = TILE / 1024;  // 1 KiB blocks per tile: one LDS-direct load of one wave each
-  static_assert(TILE % 1024 == 0, "tile must split into 1 KiB blocks");
   typedef Elem<DT> T;
 
-  // Four separate LDS objects (K and V, two stages): the compiler can then tell that the
-  // loads filling one stage never alias the reads of the other, and inserts no wait for them.
-  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE];
-  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE];
+  // The tile loads are inline assembly the compiler cannot see, so it inserts no waits for
+  // them: every wait on them below is explicit.
+  __shared__ __attribute__((aligned(1024))) char kv_lds[NSTAGE * STAGE];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)kv_lds;  // LDS address of stage 0
 
   const int lane = threadIdx.x & 63;
+  // (Left as a per-lane value on purpose: branches on the wave group then compile to exec
+  // masks over one register assignment; as scalar branches, they make the register
+  // allocator copy the accumulators at every join.)
   const int wave = threadIdx.x >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // the same, in a scalar register
   const int l32 = lane & 31;
   const int h32 = lane >> 5;
   const int group = wave >> 2;             // 0 = A, 1 = B
@@ -258,13 +273,11 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   auto key_end = [&](int last_row) { return p.causal ? min(Sk_b, last_row + off + 1) : Sk_b; };
   const int wg_end = key_end(min(Sq_b, q0 + kBM) - 1);
   const int n_tiles = wg_end > 0 ? (wg_end + kBN - 1) / kBN : 0;
-  // per wave: the last tile holding a key any of its valid rows sees, and the first tile
-  // that some row of the wave does not see completely (mask needed from there on)
+  // per wave: the first tile that some row of the wave does not see completely (the mask
+  // is applied from there on)
   const int qw0 = q0 + 32 * rblk;
-  int w_last = -1, w_full = 0;
+  int w_full = 0;
   if (qw0 < Sq_b) {
-    const int e = key_end(min(Sq_b, qw0 + 32) - 1);
-    w_last = e > 0 ? (e - 1) / kBN : -1;
     const int first_sees = p.causal ? min(Sk_b, qw0 + off + 1) : Sk_b;
     w_full = first_sees > 0 ? first_sees / kBN : 0;
   }
@@ -290,27 +303,43 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // partial vmcnt waits for Q inside the loop, and those would also stall on the K/V loads.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  // ---- K/V tile loads straight into LDS: wave w fills 1 KiB blocks w, w + 8, ... --------
-  auto issue = [&](i32x4 rsrc, int t, char* dst) __attribute__((always_inline)) {
+  // ---- K/V tile loads straight into LDS, one 1 KiB block (64 lanes x 16 B) per instruction.
+  // Block b of a tile covers rows 64b/CPR.. of it; lane l fills LDS chunk (64b + l) % CPR of
+  // its row j with memory chunk ((64b + l) % CPR) ^ swz(j).
+  //
+  // Step t consumes L(t) = {K(t), V(t-1)} from LDS stage t % 3.  L(t+2) is requested during
+  // phases 2t and 2t+1 by all 8 waves: block b of its NBLK blocks (K first, then V) by wave
+  // b % 8 in the phase of parity (b / 8) % 2, spread over that wave's MFMA or softmax work.
+  // (Issued in bursts, or by fewer waves, the loads queue at the CU's vector-memory path and
+  // stall the issuing waves for hundreds of cycles.)  A load of a tile past either end of
+  // the sequence reads zeros, so each wave issues the same NBLK / 8 loads every step, and
+  // the number it has in flight at a step's end is that constant.
+  auto tile_off = [&](int t) __attribute__((always_inline)) -> uint32_t { return (uint32_t)(t * kBN) * kstride; };
+  uint32_t ld_off[2][LPP];  // per-lane byte offsets inside a tile of this wave's blocks
 #pragma unroll
-    for (int blk0 = 0; blk0 < BLOCKS; blk0 += kWaves) {
-      const int blk = blk0 + wave;
-      if (BLOCKS % kWaves == 0 || blk < BLOCKS) {
-        const int pos = blk * 64 + lane;  // 16-byte chunk position in LDS
-        const int j = pos / CPR;
-        const int c = (pos % CPR) ^ swz<CPR>(j);
-        const uint32_t voff = (uint32_t)(t * kBN + j) * kstride + c * 16;
-        const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void*)(dst + blk * 1024);
-        lds_load16(rsrc, voff, __builtin_amdgcn_readfirstlane(lds_addr));
-      }
+  for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+    for (int i = 0; i < LPP; ++i) {
+      const int b = 16 * i + 8 * pp + wave_u;
+      const int pos = (b % KBLK) * 64 + lane;  // 16-byte chunk position inside the tile
+      const int j = pos / CPR;
+      ld_off[pp][i] = (uint32_t)j * kstride + (((pos % CPR) ^ swz<CPR>(j)) * 16);
     }
+  // load i of phase parity pp for L(tl), tl >= 0, into stage tl % 3
+  auto load_unit = [&](int tl, int pp, int i) __attribute__((always_inline)) {
+    const int b0 = 16 * i + 8 * pp;  // first block of this (pp, i) over the 8 waves
+    if (b0 >= NBLK) return;          // compile-time after unrolling
+    const bool is_k = b0 + 8 <= KBLK ? true : b0 >= KBLK ? false : b0 + wave_u < KBLK;
+    const uint32_t goff = (is_k ? tile_off(tl) : tile_off(tl - 1)) + ld_off[pp][i];
+    const uint32_t lds_addr = lds0 + (uint32_t)((tl % NSTAGE) * STAGE + (b0 + wave_u) * 1024);
+    lds_load16(is_k ? rk : rv, goff, __builtin_amdgcn_readfirstlane(lds_addr));
   };
 
   f32x16 acc_o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
   f32x16 s[2];                      // scores of the tile between its matrix and softmax phases
-  uint32_t pk[2][8];                // probabilities of the tile between its softmax and PV phases
+  uint32_t pk[2][8] = {};           // probabilities of the tile between its softmax and PV phases
   float m_run = -__builtin_inff();  // running max of scale*log2(e)*s for query l32
   float l_run = 0.0f;               // this lane's part of the row sum
   const float sl2 = p.scale_log2;
@@ -319,26 +348,28 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // Per-lane LDS byte offsets.  The swizzle only touches chunk bits that the k-step (K) or
   // the d-block (V) index leaves clear, so every read address is one of these bases XOR a
   // compile-time constant, plus an immediate row offset.
-  const int k_lane = l32 * RB + ((h32 ^ swz<CPR>(l32)) * 16);
+  const int k_lane = l32 * RB + ((h32 ^ swz<CPR>(l32)) * 16);  // K row l32, chunk 2 ks + h32
   const int g16 = (lane >> 4) & 1;
   const int s16 = lane & 15;
-  const int v_row0 = 4 * h32 + (s16 >> 2);  // row inside a 16-row group, first transpose read
+  // V transpose read: row 4 h32 + s16 / 4 of a 16-row group (and that row + 8), 8 bytes at
+  // column 16 g16 + 4 (s16 % 4)
+  const int v_row0 = 4 * h32 + (s16 >> 2);
   const int v_part = 2 * g16 + ((s16 & 3) >> 1);
-  const int v_lane0 = v_row0 * RB + ((v_part ^ swz<CPR>(v_row0)) * 16) + 8 * (s16 & 1);
-  const int v_lane1 = (v_row0 + 8) * RB + ((v_part ^ swz<CPR>(v_row0 + 8)) * 16) + 8 * (s16 & 1);
+  const int v_lane0 = TILE + v_row0 * RB + ((v_part ^ swz<CPR>(v_row0)) * 16) + 8 * (s16 & 1);
+  const int v_lane1 = TILE + (v_row0 + 8) * RB + ((v_part ^ swz<CPR>(v_row0 + 8)) * 16) + 8 * (s16 & 1);
 
-  // one QK^T MFMA of the tile: k-step ks of key block jb
-  auto qk_mma = [&](const char* Ks, int ka, int i) __attribute__((always_inline)) {
+  // one QK^T MFMA of the tile: k-step ks of key block jb (ka: k_lane + the stage's address)
+  auto qk_mma = [&](uint32_t ka, int i) __attribute__((always_inline)) {
     const int jb = i & 1, ks = i >> 1;
-    const i32x4 a = *(const i32x4*)(Ks + 32 * jb * RB + (ka ^ (32 * ks)));
+    const i32x4 a = *(const lds_i32x4*)(uintptr_t)((ka ^ (32 * ks)) + 32 * jb * RB);
     s[jb] = T::mma(a, qf[ks], s[jb]);
   };
   // one PV MFMA: d-block db, 16-key chunk (jb, c)
-  auto pv_mma = [&](const char* Vs, int va0, int va1, int i) __attribute__((always_inline)) {
+  auto pv_mma = [&](uint32_t va0, uint32_t va1, int i) __attribute__((always_inline)) {
     const int db = i % NDB, jc = i / NDB, jb = jc >> 1, c = jc & 1;
-    const int rows = (32 * jb + 16 * c) * RB;
-    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + rows + (va0 ^ (64 * db))));
-    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + rows + (va1 ^ (64 * db))));
+    const uint32_t rows = (32 * jb + 16 * c) * RB;
+    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)((va0 ^ (64 * db)) + rows));
+    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)((va1 ^ (64 * db)) + rows));
     const i32x4 a = {__builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 0, 1)),
                      __builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 2, 3)),
                      __builtin_bit_cast(int, __builtin_shufflevector(v1, v1, 0, 1)),
@@ -349,62 +380,46 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   constexpr int NQK = 2 * KS;   // MFMAs of S^T for one tile
   constexpr int NPV = 4 * NDB;  // MFMAs of O^T += V^T P^T for one tile
 
-  // matrix phase of tile t: S(t) (if t is a tile of this wave) and O += V(t-1) P(t-1)
-  auto matrix_phase = [&](int t, const char* Ks, const char* Vs) __attribute__((always_inline)) {
-    const bool do_qk = t < n_tiles && t <= w_last;
-    const bool do_pv = t >= 1 && t - 1 <= w_last;
-    int ka = k_lane, va0 = v_lane0, va1 = v_lane1;
+  // matrix phase of tile t: S(t) = K(t) Q^T and O += V(t-1) P(t-1), from LDS stage t % 3;
+  // hook(j), j < LPP, issues this wave's loads of the phase.  Every wave runs every tile of
+  // the workgroup: past a wave's last visible tile its probabilities are zero, and the
+  // phase takes as long as the busiest wave of the group anyway.
+  auto matrix_phase = [&](int t, auto& hook) __attribute__((always_inline)) {
+    constexpr int N = NQK > NPV ? NQK : NPV;
+    const uint32_t st = lds0 + (uint32_t)((t % NSTAGE) * STAGE);
+    uint32_t ka = k_lane + st, va0 = v_lane0 + st, va1 = v_lane1 + st;
     asm volatile("" : "+v"(ka), "+v"(va0), "+v"(va1));  // keep derived addresses out of loop-invariant code
-    if (do_qk) {
-      s[0] = f32x16{};
-      s[1] = f32x16{};
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i < NQK) qk_mma(ka, i);
+      if (i < NPV) pv_mma(va0, va1, i);
+#pragma unroll
+      for (int j = 0; j < LPP; ++j)  // load j goes after step j * N / LPP
+        if ((j * N) / LPP == i) hook(j);
     }
     // The LDS reads run kPrefetch reads ahead of the MFMAs that consume them (pinned with
     // scheduling groups: the compiler alone keeps only one or two in flight, which leaves
     // the matrix core waiting on LDS latency).
-    if (do_qk && do_pv) {
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
 #pragma unroll
-      for (int i = 0; i < (NQK > NPV ? NQK : NPV); ++i) {
-        if (i < NQK) qk_mma(Ks, ka, i);
-        if (i < NPV) pv_mma(Vs, va0, va1, i);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
-#pragma unroll
-      for (int i = 0; i < (NQK > NPV ? NQK : NPV); ++i) {
-        if (i < NQK) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        }
-        if (i < NPV) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        }
-      }
-    } else if (do_qk) {
-#pragma unroll
-      for (int i = 0; i < NQK; ++i) qk_mma(Ks, ka, i);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
-#pragma unroll
-      for (int i = 0; i < NQK; ++i) {
+    for (int i = 0; i < N; ++i) {
+      if (i < NQK) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
-    } else if (do_pv) {
-#pragma unroll
-      for (int i = 0; i < NPV; ++i) pv_mma(Vs, va0, va1, i);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
-#pragma unroll
-      for (int i = 0; i < NPV; ++i) {
+      if (i < NPV) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
     }
   };
 
-  // softmax phase of tile t: mask, running max, lazy rescale, probabilities
-  auto softmax_phase = [&](int t) __attribute__((always_inline)) {
-    if (t >= n_tiles || t > w_last) return;
-    if (t >= w_full) {
+  // softmax phase of tile t: mask, running max, lazy rescale, probabilities; hook(j), j <
+  // LPP, issues this wave's loads of the phase, spread over the exponentials
+  auto softmax_phase = [&](int t, auto& hook) __attribute__((always_inline)) {
+    if (t >= w_full) {  // some key of the tile is hidden from some row of the wave
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
@@ -438,55 +453,78 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
         const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][2 * q + 1], sl2, -m_use));
         pk[jb][q] = T::pack(e0, e1);
         l_run = T::dot_one(pk[jb][q], l_run);
+#pragma unroll
+        for (int j = 0; j < LPP; ++j)  // load j goes after exponential pair j * 16 / LPP
+          if ((j * 16) / LPP == 8 * jb + q) hook(j);
       }
   };
 
-  // this wave's work in a phase whose index (within its own schedule) is my = 4u + M
-  auto act = [&](int my, auto m_tag) __attribute__((always_inline)) {
-    constexpr int M = decltype(m_tag)::value;
-    const int t = my >> 1;
-    if constexpr (M % 2 == 0) {
-      // K(t) sits in stage t % 2 = M / 2, V(t - 1) in the other stage.  The matrix work runs
-      // at raised wave priority so the SIMD issues its MFMAs ahead of the softmax VALU work
-      // of the other group's wave.
-      __builtin_amdgcn_s_setprio(1);
-      if constexpr (M / 2 == 0)
-        matrix_phase(t, k_lds0, v_lds1);
-      else
-        matrix_phase(t, k_lds1, v_lds0);
-      __builtin_amdgcn_s_setprio(0);
-    } else {
-      softmax_phase(t);
-    }
+  // The matrix work runs at raised wave priority so the SIMD issues its MFMAs ahead of the
+  // softmax VALU work of the other group's wave.
+  auto matrix_prio = [&](int t, auto& hook) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    matrix_phase(t, hook);
+    __builtin_amdgcn_s_setprio(0);
   };
-
-  const int n_phases = 2 * n_tiles + 2;
-  auto phase = [&](int ph, auto k_tag) __attribute__((always_inline)) {
-    constexpr int K = decltype(k_tag)::value;  // ph % 4
-    if constexpr (K % 2 == 0) {
-      const int t = ph >> 1;  // t % 2 == K / 2
-      if (t + 1 < n_tiles) issue(rk, t + 1, K / 2 == 0 ? k_lds1 : k_lds0);
-      if (t < n_tiles) issue(rv, t, K / 2 == 0 ? v_lds0 : v_lds1);
-    }
-    if (group == 0)
-      act(ph, std::integral_constant<int, K>{});
-    else if (ph >= 1)
-      act(ph - 1, std::integral_constant<int, (K + 3) % 4>{});
-    if constexpr (K % 2 == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // The loads of phase ph request part ph % 2 of L(ph / 2 + 2).  At the end of an odd phase
+  // 2t+1, L(t+1) must have landed for step t+1; only this wave's requests for L(t+2) may
+  // still be in flight.
+  auto even_end = [&]() __attribute__((always_inline)) { phase_barrier(); };
+  auto odd_end = [&]() __attribute__((always_inline)) {
+    wait_vmcnt<NBLK / 8>();
     phase_barrier();
   };
+  auto no_work = [&](int tl, auto pp_tag) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LPP; ++i) load_unit(tl, decltype(pp_tag)::value, i);
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
 
-  if (n_tiles > 0) issue(rk, 0, k_lds0);
+  // prologue: L(0) (K(0) and the zero V(-1)) and L(1) into stages 0 and 1
+  no_work(0, P0{});
+  no_work(0, P1{});
+  no_work(1, P0{});
+  no_work(1, P1{});
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   phase_barrier();
-  for (int ph = 0; ph < n_phases; ph += 4) {
-    phase(ph, std::integral_constant<int, 0>{});
-    phase(ph + 1, std::integral_constant<int, 1>{});
-    if (ph + 2 < n_phases) {
-      phase(ph + 2, std::integral_constant<int, 2>{});
-      phase(ph + 3, std::integral_constant<int, 3>{});
+  // Phases 0 .. 2 n_tiles + 1.  Group A: matrix(t) in phase 2t, softmax(t) in 2t+1.  Group B:
+  // softmax(t-1) in phase 2t, matrix(t) in 2t+1.  Each group runs its own straight loop
+  // (the two meet at the same barriers), so no phase body branches on the group.
+  if (group == 0) {
+    for (int t = 0; t < n_tiles; ++t) {
+      auto h0 = [&](int i) __attribute__((always_inline)) { load_unit(t + 2, 0, i); };
+      auto h1 = [&](int i) __attribute__((always_inline)) { load_unit(t + 2, 1, i); };
+      matrix_prio(t, h0);
+      even_end();
+      softmax_phase(t, h1);
+      odd_end();
+    }
+    {
+      auto h0 = [&](int i) __attribute__((always_inline)) { load_unit(n_tiles + 2, 0, i); };
+      matrix_prio(n_tiles, h0);  // O += V(n-1) P(n-1)
+      even_end();
+      no_work(n_tiles + 2, P1{});
+      odd_end();
+    }
+  } else {
+    no_work(2, P0{});
+    even_end();
+    for (int t = 0; t < n_tiles; ++t) {
+      auto h1 = [&](int i) __attribute__((always_inline)) { load_unit(t + 2, 1, i); };
+      auto h0 = [&](int i) __attribute__((always_inline)) { load_unit(t + 3, 0, i); };
+      matrix_prio(t, h1);
+      odd_end();
+      softmax_phase(t, h0);
+      even_end();
+    }
+    {
+      auto h1 = [&](int i) __attribute__((always_inline)) { load_unit(n_tiles + 2, 1, i); };
+      matrix_prio(n_tiles, h1);
+      odd_end();
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the requests past the end
 
   // ---- epilogue: normalise, scale, convert, store rows inside the sequence -------------
   const float l_tot = wave_row_sum(l_run);
