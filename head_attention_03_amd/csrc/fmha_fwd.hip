@@ -30,8 +30,14 @@
 //   raised when a tile's maximum exceeds it by more than 2^8 (a lazy rescale in the spirit
 //   of the article's section "lazy rescale": probabilities stay <= 256, far inside the
 //   range of the 16-bit and fp8 operand types, and the O rescale is skipped for most tiles).
-// * The row sum l accumulates the *rounded* probabilities that feed the matrix cores
-//   (v_dot2_f32_{bf16,f16} against 1.0), so the normalisation matches the numerator.
+// * The row sum l: on tiles that need the mask (the causal diagonal, the ragged tail) it
+//   adds the rounded 16-bit probabilities the matrix cores see, so a row with few visible
+//   keys is normalised by exactly the weights of its numerator; on fully visible tiles it
+//   adds the fp32 probabilities (as the FlashAttention papers do), two VALU operations
+//   cheaper per pair.  Both use two independent partial sums per lane.  (v_dot2 against
+//   1.0 would sum the rounded values in one operation, but on gfx950 the dot instructions
+//   wait behind the MFMAs of the wave that shares the SIMD: the softmax phase took 15%
+//   longer with them.)
 // * Tiles are split into fully visible ones, which run no mask code, and boundary tiles
 //   (causal diagonal, ragged tail), the trip-count split of the CUTLASS fusion point.
 // * Work order: heaviest q-tiles first (causal), and workgroups of one (sequence, head
@@ -168,10 +174,9 @@ struct Elem<kBF16> {
     bf16x2 v = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32, round to nearest even
     return __builtin_bit_cast(uint32_t, v);
   }
-  __device__ static inline float dot_one(uint32_t pk, float acc) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
-  }
+  // the two packed values as fp32 (exact)
+  __device__ static inline float lo(uint32_t pk) { return __builtin_bit_cast(float, pk << 16); }
+  __device__ static inline float hi(uint32_t pk) { return __builtin_bit_cast(float, pk & 0xFFFF0000u); }
   __device__ static inline f32x16 mma(i32x4 a, i32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                   0, 0, 0);
@@ -184,10 +189,9 @@ struct Elem<kF16> {
     f16x2 v = {(_Float16)a, (_Float16)b};  // v_cvt_pk_f16_f32, round to nearest even
     return __builtin_bit_cast(uint32_t, v);
   }
-  __device__ static inline float dot_one(uint32_t pk, float acc) {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), one, acc, false);
-  }
+  // the two packed values as fp32 (exact)
+  __device__ static inline float lo(uint32_t pk) { return (float)__builtin_bit_cast(f16x2, pk)[0]; }
+  __device__ static inline float hi(uint32_t pk) { return (float)__builtin_bit_cast(f16x2, pk)[1]; }
   __device__ static inline f32x16 mma(i32x4 a, i32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                  0, 0);
@@ -341,9 +345,11 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   f32x16 s[2];                      // scores of the tile between its matrix and softmax phases
   uint32_t pk[2][8] = {};           // probabilities of the tile between its softmax and PV phases
   float m_run = -__builtin_inff();  // running max of scale*log2(e)*s for query l32
-  float l_run = 0.0f;               // this lane's part of the row sum
+  float l_run = 0.0f;               // this lane's part of the row sum (l_run + l_run2)
+  float l_run2 = 0.0f;
   const float sl2 = p.scale_log2;
-  const int qrow_vis = qi + off;    // last visible key of this query under a causal mask
+  // last key visible to this lane's query, less the lane's key offset 4 h32 inside a tile
+  const int vis_last = (p.causal ? min(Sk_b - 1, qi + off) : Sk_b - 1) - 4 * h32;
 
   // Per-lane LDS byte offsets.  The swizzle only touches chunk bits that the k-step (K) or
   // the d-block (V) index leaves clear, so every read address is one of these bases XOR a
@@ -420,14 +426,13 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // LPP, issues this wave's loads of the phase, spread over the exponentials
   auto softmax_phase = [&](int t, auto& hook) __attribute__((always_inline)) {
     if (t >= w_full) {  // some key of the tile is hidden from some row of the wave
+      // score (jb, r) belongs to key t kBN + 4 h32 + 32 jb + 8 (r / 4) + r % 4
+      const int lim = vis_last - t * kBN;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t * kBN + 32 * jb + (r >> 2) * 8 + 4 * h32 + (r & 3);
-          const bool vis = key < Sk_b && (!p.causal || key <= qrow_vis);
-          s[jb][r] = vis ? s[jb][r] : -__builtin_inff();
-        }
+        for (int r = 0; r < 16; ++r)
+          s[jb][r] = 32 * jb + 8 * (r >> 2) + (r & 3) <= lim ? s[jb][r] : -__builtin_inff();
     }
     float mx = s[0][0];
 #pragma unroll
@@ -440,23 +445,45 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       const float m_new = __builtin_fmaxf(m_run, m_cand);
       const float alpha = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
+      l_run2 *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
       m_run = m_new;
     }
     const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
+    // exponentials, packing and row sums; ROUNDED: sum the 16-bit values the matrix cores
+    // see, else the fp32 ones (see the row-sum note at the top of this file)
+    auto exps = [&](auto rounded_tag) __attribute__((always_inline)) {
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][2 * q], sl2, -m_use));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][2 * q + 1], sl2, -m_use));
+          pk[jb][q] = T::pack(e0, e1);
+          if constexpr (decltype(rounded_tag)::value) {
+            l_run += T::lo(pk[jb][q]);
+            l_run2 += T::hi(pk[jb][q]);
+          } else {
+            l_run += e0;
+            l_run2 += e1;
+          }
+#pragma unroll
+          for (int j = 0; j < LPP; ++j)  // load j goes after exponential pair j * 16 / LPP
+            if ((j * 16) / LPP == 8 * jb + q) hook(j);
+        }
+    };
+    if (t >= w_full)
+      exps(std::true_type{});
+    else
+      exps(std::false_type{});
+    // Pin the results here: the compiler may otherwise sink the tail of this arithmetic past
+    // the phase barrier, into the matrix phase that follows on this wave.
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][2 * q], sl2, -m_use));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][2 * q + 1], sl2, -m_use));
-        pk[jb][q] = T::pack(e0, e1);
-        l_run = T::dot_one(pk[jb][q], l_run);
-#pragma unroll
-        for (int j = 0; j < LPP; ++j)  // load j goes after exponential pair j * 16 / LPP
-          if ((j * 16) / LPP == 8 * jb + q) hook(j);
-      }
+      asm volatile("" : "+v"(pk[jb][0]), "+v"(pk[jb][1]), "+v"(pk[jb][2]), "+v"(pk[jb][3]), "+v"(pk[jb][4]),
+                   "+v"(pk[jb][5]), "+v"(pk[jb][6]), "+v"(pk[jb][7]));
+    asm volatile("" : "+v"(l_run), "+v"(l_run2), "+v"(m_run));
   };
 
   // The matrix work runs at raised wave priority so the SIMD issues its MFMAs ahead of the
@@ -527,7 +554,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the requests past the end
 
   // ---- epilogue: normalise, scale, convert, store rows inside the sequence -------------
-  const float l_tot = wave_row_sum(l_run);
+  const float l_tot = wave_row_sum(l_run + l_run2);
   const float inv = l_tot > 0.0f ? p.o_scale / l_tot : 0.0f;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
