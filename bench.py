@@ -33,23 +33,31 @@ from workloads import CONFIGS, make_config, to_bits  # noqa: E402
 # MI355X published dense peaks (TFLOP/s): 256 CUs x 2.4 GHz x {4096 fp16/bf16, 8192 fp8} FLOP/clk/CU
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f8e4m3": 5033.2}
 KERNEL_SOURCE = os.path.join(ROOT, "head_attention_03_amd", "csrc", "fmha_fwd.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fmha_fwd_hbm_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(config_id: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on this kernel source."""
+def workload_slug(c: dict) -> str:
+    """File-name tag of a workload: dtype, head dim, mask, sizes."""
+    if c["kind"] == "dense":
+        heads = f"h{c['H']}" if c["H"] == c["H_kv"] else f"h{c['H']}kv{c['H_kv']}"
+        return f"{c['dtype']}_d{c['D']}_{c['mask']}_b{c['B']}_{heads}_s{c['Sq']}"
+    return f"{c['dtype']}_d{c['D']}_varlen{c['nseq']}_h{c['H']}"
+
+
+def measured_traffic(c: dict):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload,
+    if it was taken on the current kernel source (else None)."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(os.path.join(PROFILES, f"fmha_fwd_{workload_slug(c)}_traffic.json")))
     except (OSError, ValueError):
         return None
-    entry = rec.get("configs", {}).get(str(config_id))
-    if not entry or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(config_id: int, budget_s: float):
@@ -147,22 +155,23 @@ def main():
         launch(i)
     torch.cuda.synchronize()
 
-    # timed region: K back-to-back steps between two HIP events recorded on the launch stream
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: K back-to-back steps; HIP events recorded on the launch stream around
+    # every step give the kernel's own duration (without the gaps between launches)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
     for i in range(args.steps):
+        evs[i][0].record(stream)
         launch(i)
-    ev1.record(stream)
+        evs[i][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    avg_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps / len(masks)
+    avg_launch_s = sum(a.elapsed_time(b) for a, b in evs) / 1e3 / args.steps / len(masks)
 
     value = flops_step * args.steps / elapsed / 1e12
     achieved = flops_step / len(masks) / avg_launch_s / 1e12
     peak = PEAK_TFLOPS[inp.dtype]
-    traffic = measured_traffic(cid)
+    traffic = measured_traffic(c)
     cfg = {"workload": c["name"], "config_id": cid, "B": B, "Sq": Sq, "Sk": Sk, "H": inp.H, "H_kv": inp.H_kv,
            "D": inp.D, "dtype": inp.dtype, "mask": "+".join(masks), "lse": want_lse, "seed": inp.seed,
            "rotate_buffers": len(sets), "flop_per_step": flops_step}
