@@ -303,9 +303,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     qf[ks] = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)qi * qstride + (16 * ks + 8 * h32) * E, 0, 0);
-  // Wait for Q here with the builtin (whose effect the compiler tracks): otherwise it keeps
-  // partial vmcnt waits for Q inside the loop, and those would also stall on the K/V loads.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // (Q is waited for in the prologue below, together with the first two K/V tiles.)
 
   // ---- K/V tile loads straight into LDS, one 1 KiB block (64 lanes x 16 B) per instruction.
   // Block b of a tile covers rows 64b/CPR.. of it; lane l fills LDS chunk (64b + l) % CPR of
@@ -513,7 +511,10 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   no_work(0, P1{});
   no_work(1, P0{});
   no_work(1, P1{});
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Wait for Q and the tiles with the builtin (whose effect the compiler tracks): otherwise
+  // it keeps partial vmcnt waits for Q inside the loop, and those would also stall on the
+  // K/V loads.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   phase_barrier();
   // Phases 0 .. 2 n_tiles + 1.  Group A: matrix(t) in phase 2t, softmax(t) in 2t+1.  Group B:
   // softmax(t-1) in phase 2t, matrix(t) in 2t+1.  Each group runs its own straight loop
@@ -551,11 +552,17 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       odd_end();
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the requests past the end
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the requests past the end (they write LDS)
 
-  // ---- epilogue: normalise, scale, convert, store rows inside the sequence -------------
+  // ---- epilogue: normalise, scale, convert; stage each wave's 32 x D tile of O through LDS
+  // (free now) so the stores write whole rows, 16 bytes per lane, instead of 16-byte pieces
+  // of 32 rows.  Rows past the sequence fall outside the O descriptor and are dropped.
+  phase_barrier();  // every wave's requests past the end have landed and its reads are done
   const float l_tot = wave_row_sum(l_run + l_run2);
   const float inv = l_tot > 0.0f ? p.o_scale / l_tot : 0.0f;
+  constexpr int OST = RB + 16;  // LDS bytes per staged O row (padded against bank conflicts)
+  static_assert(kWaves * 32 * OST <= NSTAGE * STAGE, "O staging fits in the K/V stages");
+  char* const ot = kv_lds + wave * 32 * OST;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -563,8 +570,15 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       const int d = 32 * db + 8 * g + 4 * h32;
       const i32x2 w = {(int)T::pack(acc_o[db][4 * g] * inv, acc_o[db][4 * g + 1] * inv),
                        (int)T::pack(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv)};
-      __builtin_amdgcn_raw_buffer_store_b64(w, ro, (uint32_t)qi * qstride + d * E, 0, 0);
+      *(i32x2*)(ot + l32 * OST + d * E) = w;
     }
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = i * RPI + lane / CPR, chunk = lane % CPR;
+    const i32x4 w = *(const i32x4*)(ot + row * OST + chunk * 16);
+    __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)(qw0 + row) * qstride + chunk * 16, 0, 0);
+  }
   if (p.lse && h32 == 0 && qi < Sq_b) {
     const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f
                                    : -__builtin_inff();
