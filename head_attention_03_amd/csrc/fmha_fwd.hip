@@ -56,6 +56,7 @@ namespace fmha {
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -67,13 +68,19 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per K/V tile
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: raise the running max only past 2^8
+// fp8 probabilities are shifted up by 2^kF8Shift before the e4m3 conversion (and the running
+// max is raised past 2^kF8Threshold), so they span [2^-9, 2^8] with e4m3 normals covering
+// down to 2^-6 below the running max of the row, instead of most of a long row's weights
+// landing among the subnormals.  The shift cancels in O = sum p v / sum p; the LSE removes it.
+constexpr float kF8Shift = 6.0f;
+constexpr float kF8Threshold = 2.0f;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 buffer descriptor: raw 32-bit dwords
 constexpr int kSchedMfma = 0x008;    // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedDsRead = 0x100;
 constexpr int kPrefetch = 6;         // LDS reads kept in flight ahead of the MFMAs
 constexpr int kWaitVmcnt0 = 0x0F70;           // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima
 
-enum : int { kF16 = 0, kBF16 = 1 };
+enum : int { kF16 = 0, kBF16 = 1, kF8 = 2 };
 
 struct Params {
   const void* q;
@@ -99,6 +106,7 @@ struct Params {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
@@ -198,8 +206,31 @@ struct Elem<kF16> {
   }
 };
 
+// fp8 e4m3 (OCP e4m3fn): S^T and O^T on the 32x32x64 f8f6f4 MFMA, unit block scales
+// (E8M0 127 = 2^0) since the per-tensor scales are folded into scale and o_scale.
+__device__ inline f32x16 mma_f8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+// four fp32 values -> four e4m3 bytes (round to nearest even; inputs within +-448)
+__device__ inline uint32_t pack_f8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+template <int I>
+__device__ inline float f8_byte(uint32_t w) { return __builtin_amdgcn_cvt_f32_fp8((int)w, I); }
+
+// 16-byte chunk swizzle of an 8-bit K/V tile row j in LDS (CPR chunks per row, P = 256 / row
+// bytes rows per 256-byte bank window).  The 16 rows of a b128 K read land in 16 distinct
+// chunk slots of the bank window, and so do the 8 rows x 2 chunks of a transposed 8-bit V read.
+template <int CPR>
+__device__ inline int swz8(int j) {
+  constexpr int P = 256 / (16 * CPR);
+  return 2 * ((j / P) % (CPR / 2)) + ((j >> 3) & 1);
+}
+
 // ------------------------------------------------------------------------------------
-// the kernel (fp16 / bf16)
+// the kernel (fp16 / bf16 / fp8 e4m3)
 // ------------------------------------------------------------------------------------
 // Phase schedule.  The 8 waves form two groups, A = waves 0-3 and B = waves 4-7, so every
 // SIMD holds one wave of each.  Time is cut into phases separated by workgroup barriers.
@@ -211,7 +242,8 @@ struct Elem<kF16> {
 // 2t+1, two phases ahead of their first use.
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
-  constexpr int E = 2;             // bytes per element
+  constexpr bool F8 = DT == kF8;
+  constexpr int E = F8 ? 1 : 2;    // bytes per element
   constexpr int RB = D * E;        // bytes per K/V row, in memory and in LDS (swizzled)
   constexpr int CPR = RB / 16;     // 16-byte chunks per row
   constexpr int TILE = kBN * RB;   // LDS bytes per K or V tile
@@ -221,9 +253,11 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   constexpr int STAGE = 2 * TILE;    // LDS bytes per stage: K tile, then V tile
   constexpr int LPP = (NBLK + 15) / 16;  // loads one wave issues per phase
   static_assert(NBLK % 8 == 0, "every wave issues the same number of tile loads");
-  constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
+  static_assert(!F8 || D >= 64, "fp8 needs D >= 64 (one 64-deep MFMA k-step)");
+  constexpr int KS = F8 ? D / 64 : D / 16;  // MFMA k-steps over the head dimension
   constexpr int NDB = D / 32;      // 32-wide blocks of the head dimension in O
-  typedef Elem<DT> T;
+  typedef Elem<DT == kF8 ? kBF16 : DT> T;  // (fp8 uses the helpers above instead)
+  auto sw = [](int j) __attribute__((always_inline)) { return F8 ? swz8<CPR>(j) : swz<CPR>(j); };
 
   // The tile loads are inline assembly the compiler cannot see, so it inserts no waits for
   // them: every wait on them below is explicit.
@@ -299,10 +333,13 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
 
   // ---- Q fragment: B operand of S^T = K Q^T, lane owns query l32, dims 8*h32.. of each k-step
   const int qi = qw0 + l32;  // query row inside the sequence
-  i32x4 qf[KS];
+  // (fp8: 32 bytes, dims 64 ks + 32 h32 .., per 64-deep k-step, in qf[2 ks], qf[2 ks + 1])
+  constexpr int NQF = F8 ? 2 * KS : KS;
+  i32x4 qf[NQF];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qf[ks] = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)qi * qstride + (16 * ks + 8 * h32) * E, 0, 0);
+  for (int i = 0; i < NQF; ++i)
+    qf[i] = __builtin_amdgcn_raw_buffer_load_b128(
+        rq, (uint32_t)qi * qstride + (F8 ? 64 * (i >> 1) + 32 * h32 + 16 * (i & 1) : (16 * i + 8 * h32) * E), 0, 0);
   // (Q is waited for in the prologue below, together with the first two K/V tiles.)
 
   // ---- K/V tile loads straight into LDS, one 1 KiB block (64 lanes x 16 B) per instruction.
@@ -325,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       const int b = 16 * i + 8 * pp + wave_u;
       const int pos = (b % KBLK) * 64 + lane;  // 16-byte chunk position inside the tile
       const int j = pos / CPR;
-      ld_off[pp][i] = (uint32_t)j * kstride + (((pos % CPR) ^ swz<CPR>(j)) * 16);
+      ld_off[pp][i] = (uint32_t)j * kstride + (((pos % CPR) ^ sw(j)) * 16);
     }
   // load i of phase parity pp for L(tl), tl >= 0, into stage tl % 3
   auto load_unit = [&](int tl, int pp, int i) __attribute__((always_inline)) {
@@ -341,10 +378,14 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
   f32x16 s[2];                      // scores of the tile between its matrix and softmax phases
-  uint32_t pk[2][8] = {};           // probabilities of the tile between its softmax and PV phases
+  constexpr int NPK = F8 ? 4 : 8;   // packed probability registers per 32-key block
+  uint32_t pk[2][NPK] = {};         // probabilities of the tile between its softmax and PV phases
   float m_run = -__builtin_inff();  // running max of scale*log2(e)*s for query l32
   float l_run = 0.0f;               // this lane's part of the row sum (l_run + l_run2)
   float l_run2 = 0.0f;
+  // fp8: what the rounded sums of masked tiles leave out of the exact row sum (the LSE uses
+  // the exact sum; a 3-bit-mantissa rounding would otherwise move it by up to ~0.03)
+  float l_fix = 0.0f;
   const float sl2 = p.scale_log2;
   // last key visible to this lane's query, less the lane's key offset 4 h32 inside a tile
   const int vis_last = (p.causal ? min(Sk_b - 1, qi + off) : Sk_b - 1) - 4 * h32;
@@ -352,24 +393,51 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // Per-lane LDS byte offsets.  The swizzle only touches chunk bits that the k-step (K) or
   // the d-block (V) index leaves clear, so every read address is one of these bases XOR a
   // compile-time constant, plus an immediate row offset.
-  const int k_lane = l32 * RB + ((h32 ^ swz<CPR>(l32)) * 16);  // K row l32, chunk 2 ks + h32
+  //   16-bit: K row l32, chunk 2 ks + h32; fp8: K row l32, chunks 4 ks + 2 h32 (+1).
+  const int k_lane = l32 * RB + (((F8 ? 2 * h32 : h32) ^ sw(l32)) * 16);
+  const int k_lane2 = l32 * RB + (((2 * h32 + 1) ^ sw(l32)) * 16);  // fp8 only
   const int g16 = (lane >> 4) & 1;
   const int s16 = lane & 15;
-  // V transpose read: row 4 h32 + s16 / 4 of a 16-row group (and that row + 8), 8 bytes at
-  // column 16 g16 + 4 (s16 % 4)
-  const int v_row0 = 4 * h32 + (s16 >> 2);
-  const int v_part = 2 * g16 + ((s16 & 3) >> 1);
-  const int v_lane0 = TILE + v_row0 * RB + ((v_part ^ swz<CPR>(v_row0)) * 16) + 8 * (s16 & 1);
-  const int v_lane1 = TILE + (v_row0 + 8) * RB + ((v_part ^ swz<CPR>(v_row0 + 8)) * 16) + 8 * (s16 & 1);
+  // 16-bit V transpose read (ds_read_b64_tr_b16): row 4 h32 + s16 / 4 of a 16-row group (and
+  // that row + 8), 8 bytes at column 16 g16 + 4 (s16 % 4).
+  // fp8 (ds_read_b64_tr_b8, which hands lane j of each 16-lane group byte j % 8 of the words
+  // of lanes j / 8, j / 8 + 2, ..): lane l supplies row 8 h32 + s16 / 2 of a 16-row chunk,
+  // 8 bytes at column 16 g16 + 8 (s16 % 2), and gets column l32 of rows 8 h32 + 0..7.
+  const int v_row0 = F8 ? 8 * h32 + (s16 >> 1) : 4 * h32 + (s16 >> 2);
+  const int v_part = F8 ? g16 : 2 * g16 + ((s16 & 3) >> 1);
+  const int v_lane0 = TILE + v_row0 * RB + ((v_part ^ sw(v_row0)) * 16) + 8 * (s16 & 1);
+  const int v_lane1 = TILE + (v_row0 + 8) * RB + ((v_part ^ sw(v_row0 + 8)) * 16) + 8 * (s16 & 1);
 
-  // one QK^T MFMA of the tile: k-step ks of key block jb (ka: k_lane + the stage's address)
-  auto qk_mma = [&](uint32_t ka, int i) __attribute__((always_inline)) {
+  // one QK^T MFMA of the tile: k-step ks of key block jb (ka, kb: k_lane, k_lane2 + the
+  // stage's address)
+  auto qk_mma = [&](uint32_t ka, uint32_t kb, int i) __attribute__((always_inline)) {
     const int jb = i & 1, ks = i >> 1;
-    const i32x4 a = *(const lds_i32x4*)(uintptr_t)((ka ^ (32 * ks)) + 32 * jb * RB);
-    s[jb] = T::mma(a, qf[ks], s[jb]);
+    if constexpr (F8) {
+      const i32x4 a0 = *(const lds_i32x4*)(uintptr_t)((ka ^ (64 * ks)) + 32 * jb * RB);
+      const i32x4 a1 = *(const lds_i32x4*)(uintptr_t)((kb ^ (64 * ks)) + 32 * jb * RB);
+      const i32x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const i32x8 b = __builtin_shufflevector(qf[2 * ks], qf[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      s[jb] = mma_f8(a, b, s[jb]);
+    } else {
+      const i32x4 a = *(const lds_i32x4*)(uintptr_t)((ka ^ (32 * ks)) + 32 * jb * RB);
+      s[jb] = T::mma(a, qf[ks], s[jb]);
+    }
   };
-  // one PV MFMA: d-block db, 16-key chunk (jb, c)
+  // one PV MFMA.  16-bit: d-block db, 16-key chunk (jb, c).  fp8: d-block i, all 64 keys; byte
+  // 8 c + r of either operand is key 16 c + 8 h32 + r (the probabilities are regrouped to
+  // this order at the end of the softmax, and the transposed V reads deliver it).
   auto pv_mma = [&](uint32_t va0, uint32_t va1, int i) __attribute__((always_inline)) {
+    if constexpr (F8) {
+      i32x2 t[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        t[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)((va0 ^ (32 * i)) + 16 * c * RB));
+      const i32x8 a = {t[0][0], t[0][1], t[1][0], t[1][1], t[2][0], t[2][1], t[3][0], t[3][1]};
+      const i32x8 b = {(int)pk[0][0], (int)pk[0][1], (int)pk[0][2], (int)pk[0][3],
+                       (int)pk[1][0], (int)pk[1][1], (int)pk[1][2], (int)pk[1][3]};
+      acc_o[i] = mma_f8(a, b, acc_o[i]);
+      return;
+    }
     const int db = i % NDB, jc = i / NDB, jb = jc >> 1, c = jc & 1;
     const uint32_t rows = (32 * jb + 16 * c) * RB;
     const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)((va0 ^ (64 * db)) + rows));
@@ -381,8 +449,10 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     const i32x4 bp = {(int)pk[jb][4 * c], (int)pk[jb][4 * c + 1], (int)pk[jb][4 * c + 2], (int)pk[jb][4 * c + 3]};
     acc_o[db] = T::mma(a, bp, acc_o[db]);
   };
-  constexpr int NQK = 2 * KS;   // MFMAs of S^T for one tile
-  constexpr int NPV = 4 * NDB;  // MFMAs of O^T += V^T P^T for one tile
+  constexpr int NQK = 2 * KS;                // MFMAs of S^T for one tile
+  constexpr int NPV = F8 ? NDB : 4 * NDB;    // MFMAs of O^T += V^T P^T for one tile
+  constexpr int RQK = F8 ? 2 : 1;            // LDS reads per S^T MFMA
+  constexpr int RPV = F8 ? 4 : 2;            // LDS reads per O^T MFMA
 
   // matrix phase of tile t: S(t) = K(t) Q^T and O += V(t-1) P(t-1), from LDS stage t % 3;
   // hook(j), j < LPP, issues this wave's loads of the phase.  Every wave runs every tile of
@@ -391,13 +461,17 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   auto matrix_phase = [&](int t, auto& hook) __attribute__((always_inline)) {
     constexpr int N = NQK > NPV ? NQK : NPV;
     const uint32_t st = lds0 + (uint32_t)((t % NSTAGE) * STAGE);
-    uint32_t ka = k_lane + st, va0 = v_lane0 + st, va1 = v_lane1 + st;
-    asm volatile("" : "+v"(ka), "+v"(va0), "+v"(va1));  // keep derived addresses out of loop-invariant code
+    uint32_t ka = k_lane + st, kb = k_lane2 + st, va0 = v_lane0 + st, va1 = v_lane1 + st;
+    // keep derived addresses out of loop-invariant code
+    if constexpr (F8)
+      asm volatile("" : "+v"(ka), "+v"(kb), "+v"(va0));
+    else
+      asm volatile("" : "+v"(ka), "+v"(va0), "+v"(va1));
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      if (i < NQK) qk_mma(ka, i);
+      if (i < NQK) qk_mma(ka, kb, i);
       if (i < NPV) pv_mma(va0, va1, i);
 #pragma unroll
       for (int j = 0; j < LPP; ++j)  // load j goes after step j * N / LPP
@@ -411,11 +485,11 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     for (int i = 0; i < N; ++i) {
       if (i < NQK) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RQK, 0);
       }
       if (i < NPV) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPV, 0);
       }
     }
   };
@@ -439,49 +513,77 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[jb][r]);
     mx = wave_row_max(mx);
     const float m_cand = mx * sl2;
-    if (__any(m_cand > m_run + kRescaleThreshold)) {
+    if (__any(m_cand > m_run + (F8 ? kF8Threshold : kRescaleThreshold))) {
       const float m_new = __builtin_fmaxf(m_run, m_cand);
       const float alpha = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
       l_run2 *= alpha;
+      if constexpr (F8) l_fix *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
       m_run = m_new;
     }
-    const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
+    const float m_use = (m_run == -__builtin_inff() ? 0.0f : m_run) - (F8 ? kF8Shift : 0.0f);
     // exponentials, packing and row sums; ROUNDED: sum the 16-bit values the matrix cores
     // see, else the fp32 ones (see the row-sum note at the top of this file)
     auto exps = [&](auto rounded_tag) __attribute__((always_inline)) {
+      constexpr bool ROUNDED = decltype(rounded_tag)::value;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][2 * q], sl2, -m_use));
-          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][2 * q + 1], sl2, -m_use));
-          pk[jb][q] = T::pack(e0, e1);
-          if constexpr (decltype(rounded_tag)::value) {
-            l_run += T::lo(pk[jb][q]);
-            l_run2 += T::hi(pk[jb][q]);
+        for (int qd = 0; qd < 4; ++qd) {  // scores 4 qd .. 4 qd + 3: keys 8 qd + 4 h32 + 0..3
+          float e[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][4 * qd + u], sl2, -m_use));
+          if constexpr (F8) {
+            const uint32_t w = pack_f8x4(e[0], e[1], e[2], e[3]);
+            pk[jb][qd] = w;
+            if constexpr (ROUNDED) {
+              const float r = (f8_byte<0>(w) + f8_byte<1>(w)) + (f8_byte<2>(w) + f8_byte<3>(w));
+              l_run += r;
+              l_fix += ((e[0] + e[1]) + (e[2] + e[3])) - r;
+            }
           } else {
-            l_run += e0;
-            l_run2 += e1;
+            pk[jb][2 * qd] = T::pack(e[0], e[1]);
+            pk[jb][2 * qd + 1] = T::pack(e[2], e[3]);
+            if constexpr (ROUNDED) {
+              l_run += T::lo(pk[jb][2 * qd]) + T::lo(pk[jb][2 * qd + 1]);
+              l_run2 += T::hi(pk[jb][2 * qd]) + T::hi(pk[jb][2 * qd + 1]);
+            }
+          }
+          if constexpr (!ROUNDED) {
+            l_run += e[0] + e[2];
+            l_run2 += e[1] + e[3];
           }
 #pragma unroll
-          for (int j = 0; j < LPP; ++j)  // load j goes after exponential pair j * 16 / LPP
-            if ((j * 16) / LPP == 8 * jb + q) hook(j);
+          for (int j = 0; j < LPP; ++j)  // load j goes after exponential quad j * 8 / LPP
+            if ((j * 8) / LPP == 4 * jb + qd) hook(j);
         }
     };
     if (t >= w_full)
       exps(std::true_type{});
     else
       exps(std::false_type{});
+    if constexpr (F8) {
+      // Regroup to 8 consecutive keys per lane and 16-key chunk (the fp8 PV operand order):
+      // lane h32 = 0 trades its keys 8..11 of each chunk for keys 4..7 of lane l + 32.
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          auto r = __builtin_amdgcn_permlane32_swap(pk[jb][2 * m], pk[jb][2 * m + 1], false, false);
+          pk[jb][2 * m] = r[0];
+          pk[jb][2 * m + 1] = r[1];
+        }
+    }
     // Pin the results here: the compiler may otherwise sink the tail of this arithmetic past
     // the phase barrier, into the matrix phase that follows on this wave.
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
-      asm volatile("" : "+v"(pk[jb][0]), "+v"(pk[jb][1]), "+v"(pk[jb][2]), "+v"(pk[jb][3]), "+v"(pk[jb][4]),
-                   "+v"(pk[jb][5]), "+v"(pk[jb][6]), "+v"(pk[jb][7]));
+#pragma unroll
+      for (int q = 0; q < NPK; ++q) asm volatile("" : "+v"(pk[jb][q]));
     asm volatile("" : "+v"(l_run), "+v"(l_run2), "+v"(m_run));
+    if constexpr (F8) asm volatile("" : "+v"(l_fix));
   };
 
   // The matrix work runs at raised wave priority so the SIMD issues its MFMAs ahead of the
@@ -568,9 +670,16 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d = 32 * db + 8 * g + 4 * h32;
-      const i32x2 w = {(int)T::pack(acc_o[db][4 * g] * inv, acc_o[db][4 * g + 1] * inv),
-                       (int)T::pack(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv)};
-      *(i32x2*)(ot + l32 * OST + d * E) = w;
+      if constexpr (F8) {  // saturate to the largest finite e4m3 value, then round
+        float x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = __builtin_fminf(__builtin_fmaxf(acc_o[db][4 * g + u] * inv, -448.0f), 448.0f);
+        *(uint32_t*)(ot + l32 * OST + d) = pack_f8x4(x[0], x[1], x[2], x[3]);
+      } else {
+        const i32x2 w = {(int)T::pack(acc_o[db][4 * g] * inv, acc_o[db][4 * g + 1] * inv),
+                         (int)T::pack(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv)};
+        *(i32x2*)(ot + l32 * OST + d * E) = w;
+      }
     }
   constexpr int RPI = 64 / CPR;  // rows per store instruction
 #pragma unroll
@@ -579,8 +688,10 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     const i32x4 w = *(const i32x4*)(ot + row * OST + chunk * 16);
     __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)(qw0 + row) * qstride + chunk * 16, 0, 0);
   }
+  const float l_exact = F8 ? l_tot + wave_row_sum(l_fix) : l_tot;  // (all lanes: a lane swap)
   if (p.lse && h32 == 0 && qi < Sq_b) {
-    const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f
+    const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_exact) - (F8 ? kF8Shift : 0.0f)) *
+                                         0.69314718055994531f
                                    : -__builtin_inff();
     const size_t idx = p.cu_q ? (size_t)h * p.total_q + q_row0 + qi : ((size_t)b * p.H + h) * p.Sq + qi;
     p.lse[idx] = lse;
@@ -632,7 +743,7 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FMHA_ERR_MISALIGNED;
   if ((uintptr_t)lse & 3) return FMHA_ERR_MISALIGNED;
   if (!(scale > 0.0f) || !isfinite(scale) || !isfinite(o_scale)) return FMHA_ERR_INVALID_ARGUMENT;
-  if (dtype == FMHA_DTYPE_F8E4M3) return FMHA_ERR_UNSUPPORTED;
+  if (dtype == FMHA_DTYPE_F8E4M3 && D == 32) return FMHA_ERR_UNSUPPORTED;  // fp8 MFMA k-step is 64 deep
 
   const int64_t esz = dtype == FMHA_DTYPE_F8E4M3 ? 1 : 2;
   // every per-sequence byte offset must fit the 31-bit range of a buffer descriptor
@@ -640,6 +751,8 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
   const int64_t rows_k = packed ? varlen->total_length_k : Sk;
   const int64_t lim = (int64_t)1 << 31;
   if (rows_q * H * D * esz >= lim || rows_k * H_kv * D * esz >= lim) return FMHA_ERR_UNSUPPORTED;
+  // tiles requested one before and two past the keys must not wrap the 32-bit offset
+  if ((int64_t)3 * kBN * H_kv * D * esz >= lim) return FMHA_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || Sq == 0 || (packed && varlen->total_length_q == 0)) return FMHA_OK;
 
   Params p;
@@ -668,7 +781,10 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
   p.o_scale = o_scale;
 
   hipError_t err = hipSuccess;
-  if (dtype == FMHA_DTYPE_BF16) {
+  if (dtype == FMHA_DTYPE_F8E4M3) {
+    if (D == 64) err = launch<kF8, 64>(p, (int)grid, stream);
+    if (D == 128) err = launch<kF8, 128>(p, (int)grid, stream);
+  } else if (dtype == FMHA_DTYPE_BF16) {
     if (D == 32) err = launch<kBF16, 32>(p, (int)grid, stream);
     if (D == 64) err = launch<kBF16, 64>(p, (int)grid, stream);
     if (D == 128) err = launch<kBF16, 128>(p, (int)grid, stream);

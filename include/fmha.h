@@ -58,7 +58,9 @@ typedef enum {
   FMHA_ERR_NULL_POINTER = 1,     /* q, o, or (when there are keys) k or v is NULL, or only one
                                     cu_seqlens pointer is set */
   FMHA_ERR_INVALID_SHAPE = 2,    /* negative sizes, H % H_kv != 0, D not in {32, 64, 128}, totals < 0 */
-  FMHA_ERR_UNSUPPORTED = 3,      /* dtype/mask enum out of range, or a tensor too large for 32-bit offsets */
+  FMHA_ERR_UNSUPPORTED = 3,      /* dtype/mask enum out of range, fp8 with D == 32, or a tensor too
+                                    large for 32-bit offsets (any tensor of 2^31 bytes or more, or
+                                    192 K/V rows of 2^31 bytes or more) */
   FMHA_ERR_MISALIGNED = 4,       /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   FMHA_ERR_INVALID_ARGUMENT = 5, /* scale not finite and > 0, or o_scale not finite */
   FMHA_ERR_HIP = 6               /* the kernel launch failed (hipGetLastError) */
@@ -94,7 +96,7 @@ typedef struct {
  *          natural-log log-sum-exp of scale * q.k over the visible keys (-inf if none)
  *   B      number of sequences (>= 0);  Sq, Sk: lengths (packed: the maximum lengths)
  *   H, H_kv  query heads and key/value heads, H % H_kv == 0 (H_kv == 1 is MQA)
- *   D      head dimension: 32, 64 or 128
+ *   D      head dimension: 32, 64 or 128 (fp8: 64 or 128)
  *   scale  softmax scale (finite, > 0), applied to q.k in fp32.  For fp8 inputs the
  *          caller folds the per-tensor dequantisation scales of q and k into it.
  *   mask   see fmha_mask

@@ -48,6 +48,18 @@ def test_dense_masks_dims(dtype, D, mask):
     _dense_case(f"dense {dtype} D{D} {mask}", inp)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", MASKS)
+def test_fp8_masks_dims(D, mask):
+    inp = make_dense(2400 + D, 2, 200, 333, 4, 2, D, "f8e4m3", mask=mask, o_scale=0.5)
+    _dense_case(f"dense fp8 D{D} {mask}", inp)
+
+
+def test_fp8_gqa_more_queries_than_keys():
+    inp = make_dense(2450, 1, 333, 200, 4, 1, 128, "f8e4m3", mask="causal_qend", o_scale=0.5)
+    _dense_case("fp8 MQA Sq>Sk causal_qend", inp)
+
+
 @pytest.mark.parametrize("mask", ["causal_qbegin", "causal_qend", "none"])
 def test_more_queries_than_keys(mask):
     # under causal-qend the first Sq - Sk rows see no key: O = 0, LSE = -inf
@@ -143,6 +155,17 @@ def test_varlen_shapes(case, dtype):
     _varlen_case(f"varlen {lq}/{lk}", make_varlen(2600, lq, lk, H, H_kv, D, dtype, mask=mask))
 
 
+@pytest.mark.parametrize("case", [c for c in CMAKE_VARLEN if c[4] >= 64], ids=lambda c: f"q{c[0]}-k{c[1]}-{c[5]}-D{c[4]}")
+def test_varlen_shapes_fp8(case):
+    lq, lk, H, H_kv, D, mask = case
+    _varlen_case(f"varlen fp8 {lq}/{lk}", make_varlen(2650, lq, lk, H, H_kv, D, "f8e4m3", mask=mask, o_scale=0.5))
+
+
+def test_varlen_poisoned_padding_never_read_fp8():
+    inp = make_varlen(2750, [100, 37, 250], [90, 300, 5], 4, 2, 128, "f8e4m3", mask="causal_qend", poison_pads=True)
+    _varlen_case("varlen fp8 NaN pads", inp)
+
+
 def test_varlen_poisoned_padding_never_read():
     inp = make_varlen(2700, [100, 37, 250], [90, 300, 5], 4, 2, 64, "bf16", mask="causal_qend", poison_pads=True)
     _varlen_case("varlen NaN pads", inp)
@@ -173,7 +196,7 @@ def _sample_rows(rng, B, H, Sq, n_random=192):
     return picks
 
 
-@pytest.mark.parametrize("config_id", [2, 3])
+@pytest.mark.parametrize("config_id", [2, 3, 5])
 def test_full_size_config_sampled(config_id):
     inp = make_config(config_id)
     want_lse = config_id == 2
@@ -193,6 +216,20 @@ def test_full_size_config_sampled(config_id):
 # ----------------------------------------------------------------------------------------------
 # negative control: an oracle with a planted mistake must disagree with the HIP path
 # ----------------------------------------------------------------------------------------------
+def test_fp8_check_rejects_a_dropped_key_tile():
+    # the fp8 bound is loose at these output magnitudes; an oracle that drops the last 64
+    # keys must still fail the combined max-abs / relative-Frobenius check
+    inp = make_dense(2950, 1, 512, 1024, 2, 2, 128, "f8e4m3", mask="none", o_scale=0.5)
+    res = run_dense(inp)
+    assert res.status == 0
+    q, k, v = decoded(inp, "q"), decoded(inp, "k"), decoded(inp, "v")
+    wrong, _ = oracle.attention_dense(q, k[:, :-64], v[:, :-64], inp.scale, "none", o_scale=inp.o_scale)
+    right, _ = oracle.attention_dense(q, k, v, inp.scale, "none", o_scale=inp.o_scale)
+    compare("fp8 reference", res.o_bits, "f8e4m3", right)
+    with pytest.raises(AssertionError):
+        compare("fp8 against a dropped key tile", res.o_bits, "f8e4m3", wrong)
+
+
 def test_planted_oracle_mistake_is_detected():
     inp = make_dense(2900, 1, 256, 256, 2, 2, 64, "f16", mask="causal_qbegin")
     res = run_dense(inp)
