@@ -38,6 +38,9 @@
 //   1.0 would sum the rounded values in one operation, but on gfx950 the dot instructions
 //   wait behind the MFMAs of the wave that shares the SIMD: the softmax phase took 15%
 //   longer with them.)
+//   fp8 sums on the matrix cores instead (an all-ones operand against the probability
+//   operand of the PV product: one more MFMA per tile, exact sums of the rounded values),
+//   since its matrix phase is the short one; with an LSE it also keeps the fp32 sum.
 // * Tiles are split into fully visible ones, which run no mask code, and boundary tiles
 //   (causal diagonal, ragged tail), the trip-count split of the CUTLASS fusion point.
 // * Work order: heaviest q-tiles first (causal), and workgroups of one (sequence, head
@@ -240,7 +243,7 @@ __device__ inline int swz8(int j) {
 // ping-pong of the CUTLASS design, built here from the single workgroup barrier).
 // K(t+1) and V(t) are requested at the start of phase 2t and waited for at the end of phase
 // 2t+1, two phases ahead of their first use.
-template <int DT, int D>
+template <int DT, int D, bool LSE_SUM>
 __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   constexpr bool F8 = DT == kF8;
   constexpr int E = F8 ? 1 : 2;    // bytes per element
@@ -381,11 +384,15 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   constexpr int NPK = F8 ? 4 : 8;   // packed probability registers per 32-key block
   uint32_t pk[2][NPK] = {};         // probabilities of the tile between its softmax and PV phases
   float m_run = -__builtin_inff();  // running max of scale*log2(e)*s for query l32
-  float l_run = 0.0f;               // this lane's part of the row sum (l_run + l_run2)
+  // fp8 row sums on the matrix cores: an all-ones A operand against the probability
+  // operand of the PV product, so every element of acc_l holds the row sum of this lane's
+  // query over the rounded probabilities that O is built from (exact in fp32).  (The fp8
+  // matrix phase is half as long as the softmax, so the MFMA is the cheap place for it; the
+  // 16-bit paths keep it on the vector ALU, where their longer matrix phase hides it.)
+  f32x16 acc_l = {};
+  float l_run = 0.0f;  // this lane's part of the VALU row sum (l_run + l_run2)
   float l_run2 = 0.0f;
-  // fp8: what the rounded sums of masked tiles leave out of the exact row sum (the LSE uses
-  // the exact sum; a 3-bit-mantissa rounding would otherwise move it by up to ~0.03)
-  float l_fix = 0.0f;
+  constexpr bool VSUM = !F8 || LSE_SUM;  // keep the VALU row sum
   const float sl2 = p.scale_log2;
   // last key visible to this lane's query, less the lane's key offset 4 h32 inside a tile
   const int vis_last = (p.causal ? min(Sk_b - 1, qi + off) : Sk_b - 1) - 4 * h32;
@@ -436,6 +443,11 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       const i32x8 b = {(int)pk[0][0], (int)pk[0][1], (int)pk[0][2], (int)pk[0][3],
                        (int)pk[1][0], (int)pk[1][1], (int)pk[1][2], (int)pk[1][3]};
       acc_o[i] = mma_f8(a, b, acc_o[i]);
+      if (i == NDB - 1) {  // row sums: e4m3 1.0 = 0x38
+        const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                            0x38383838, 0x38383838, 0x38383838, 0x38383838};
+        acc_l = mma_f8(ones, b, acc_l);
+      }
       return;
     }
     const int db = i % NDB, jc = i / NDB, jb = jc >> 1, c = jc & 1;
@@ -488,7 +500,10 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RQK, 0);
       }
       if (i < NPV) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (F8 && i == NDB - 1)  // this step also adds the row sums
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPV, 0);
       }
     }
@@ -516,16 +531,19 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     if (__any(m_cand > m_run + (F8 ? kF8Threshold : kRescaleThreshold))) {
       const float m_new = __builtin_fmaxf(m_run, m_cand);
       const float alpha = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-      l_run2 *= alpha;
-      if constexpr (F8) l_fix *= alpha;
+      if constexpr (F8) acc_l[0] *= alpha;  // (the only element read)
+      if constexpr (VSUM) {
+        l_run *= alpha;
+        l_run2 *= alpha;
+      }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
       m_run = m_new;
     }
     const float m_use = (m_run == -__builtin_inff() ? 0.0f : m_run) - (F8 ? kF8Shift : 0.0f);
-    // exponentials, packing and row sums; ROUNDED: sum the 16-bit values the matrix cores
-    // see, else the fp32 ones (see the row-sum note at the top of this file)
+    // exponentials, packing and (VALU) row sums.  16-bit ROUNDED: sum the 16-bit values the
+    // matrix cores see, else the fp32 ones (see the row-sum note at the top of this file);
+    // fp8 with an LSE: the fp32 ones.
     auto exps = [&](auto rounded_tag) __attribute__((always_inline)) {
       constexpr bool ROUNDED = decltype(rounded_tag)::value;
 #pragma unroll
@@ -536,22 +554,15 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][4 * qd + u], sl2, -m_use));
           if constexpr (F8) {
-            const uint32_t w = pack_f8x4(e[0], e[1], e[2], e[3]);
-            pk[jb][qd] = w;
-            if constexpr (ROUNDED) {
-              const float r = (f8_byte<0>(w) + f8_byte<1>(w)) + (f8_byte<2>(w) + f8_byte<3>(w));
-              l_run += r;
-              l_fix += ((e[0] + e[1]) + (e[2] + e[3])) - r;
-            }
+            pk[jb][qd] = pack_f8x4(e[0], e[1], e[2], e[3]);
           } else {
             pk[jb][2 * qd] = T::pack(e[0], e[1]);
             pk[jb][2 * qd + 1] = T::pack(e[2], e[3]);
-            if constexpr (ROUNDED) {
-              l_run += T::lo(pk[jb][2 * qd]) + T::lo(pk[jb][2 * qd + 1]);
-              l_run2 += T::hi(pk[jb][2 * qd]) + T::hi(pk[jb][2 * qd + 1]);
-            }
           }
-          if constexpr (!ROUNDED) {
+          if constexpr (!F8 && ROUNDED) {
+            l_run += T::lo(pk[jb][2 * qd]) + T::lo(pk[jb][2 * qd + 1]);
+            l_run2 += T::hi(pk[jb][2 * qd]) + T::hi(pk[jb][2 * qd + 1]);
+          } else if constexpr (VSUM) {
             l_run += e[0] + e[2];
             l_run2 += e[1] + e[3];
           }
@@ -560,10 +571,14 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
             if ((j * 8) / LPP == 4 * jb + qd) hook(j);
         }
     };
-    if (t >= w_full)
-      exps(std::true_type{});
-    else
+    if constexpr (F8) {
       exps(std::false_type{});
+    } else {
+      if (t >= w_full)
+        exps(std::true_type{});
+      else
+        exps(std::false_type{});
+    }
     if constexpr (F8) {
       // Regroup to 8 consecutive keys per lane and 16-key chunk (the fp8 PV operand order):
       // lane h32 = 0 trades its keys 8..11 of each chunk for keys 4..7 of lane l + 32.
@@ -582,8 +597,8 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
       for (int q = 0; q < NPK; ++q) asm volatile("" : "+v"(pk[jb][q]));
-    asm volatile("" : "+v"(l_run), "+v"(l_run2), "+v"(m_run));
-    if constexpr (F8) asm volatile("" : "+v"(l_fix));
+    asm volatile("" : "+v"(m_run));
+    if constexpr (VSUM) asm volatile("" : "+v"(l_run), "+v"(l_run2));
   };
 
   // The matrix work runs at raised wave priority so the SIMD issues its MFMAs ahead of the
@@ -660,7 +675,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // (free now) so the stores write whole rows, 16 bytes per lane, instead of 16-byte pieces
   // of 32 rows.  Rows past the sequence fall outside the O descriptor and are dropped.
   phase_barrier();  // every wave's requests past the end have landed and its reads are done
-  const float l_tot = wave_row_sum(l_run + l_run2);
+  const float l_tot = F8 ? acc_l[0] : wave_row_sum(l_run + l_run2);
   const float inv = l_tot > 0.0f ? p.o_scale / l_tot : 0.0f;
   constexpr int OST = RB + 16;  // LDS bytes per staged O row (padded against bank conflicts)
   static_assert(kWaves * 32 * OST <= NSTAGE * STAGE, "O staging fits in the K/V stages");
@@ -688,7 +703,8 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     const i32x4 w = *(const i32x4*)(ot + row * OST + chunk * 16);
     __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)(qw0 + row) * qstride + chunk * 16, 0, 0);
   }
-  const float l_exact = F8 ? l_tot + wave_row_sum(l_fix) : l_tot;  // (all lanes: a lane swap)
+  // (fp8: the LSE takes the fp32 sum, which a 3-bit-mantissa rounding would move by up to ~0.06)
+  const float l_exact = F8 && LSE_SUM ? wave_row_sum(l_run + l_run2) : l_tot;  // (all lanes: a lane swap)
   if (p.lse && h32 == 0 && qi < Sq_b) {
     const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_exact) - (F8 ? kF8Shift : 0.0f)) *
                                          0.69314718055994531f
@@ -699,7 +715,14 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
 }
 template <int DT, int D>
 hipError_t launch(const Params& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fmha_fwd_kernel<DT, D>), dim3(grid), dim3(kThreads), 0, stream, p);
+  // fp8 keeps an fp32 row sum beside the matrix-core one when an LSE is wanted (see the kernel)
+  if constexpr (DT == kF8) {
+    if (p.lse) {
+      hipLaunchKernelGGL((fmha_fwd_kernel<DT, D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fmha_fwd_kernel<DT, D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
