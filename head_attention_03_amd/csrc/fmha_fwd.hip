@@ -10,15 +10,20 @@
 //
 // CDNA4 design (the pages' TMA / ldmatrix / mma.sync machinery has no counterpart here):
 //
-// * One workgroup = 4 waves of 64 lanes = 128 query rows (32 per wave) of one
-//   (sequence, head).  K/V tiles of 64 keys stream through LDS, double buffered, filled
-//   by buffer loads that write LDS directly (no VGPR staging).  The buffer descriptor
-//   bounds every load to the rows of the current sequence: rows past the end read as 0,
-//   which is how ragged tails and packed sequences are handled without touching
-//   neighbouring memory.
+// * One workgroup = 8 waves of 64 lanes; a q-tile is 256 query rows (32 per wave) of one
+//   (sequence, head).  The two halves of the workgroup ping-pong between the matrix cores
+//   and the vector ALU (the phase schedule above the kernel).  K/V tiles of 64 keys stream
+//   through three LDS stages, filled by buffer loads that write LDS directly (no VGPR
+//   staging).  The buffer descriptor bounds every load to the rows of the current
+//   sequence: rows past the end read as 0, which is how ragged tails and packed sequences
+//   are handled without touching neighbouring memory.
+// * A workgroup runs up to 8 q-tiles of one (sequence, head) back to back as a single K/V
+//   stream: the next q-tile's Q rows and first K/V tiles load while the current one still
+//   computes, and its output is written while the other half of the workgroup works the
+//   matrix cores, so no q-tile waits for its inputs from memory after the first.
 // * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_{bf16,f16}:
 //   A = 32 keys x 16 dims read from LDS, B = 16 dims x 32 queries held in VGPRs for the
-//   whole loop.  In the accumulator layout lane l then owns query l%32, and lanes l and
+//   whole q-tile.  In the accumulator layout lane l then owns query l%32, and lanes l and
 //   l^32 together own all 32 keys of the block, so a row max or sum is an in-lane reduction
 //   plus one v_permlane32_swap.
 // * The same accumulator layout is, key for key, the B operand layout of the second
@@ -43,13 +48,16 @@
 //   since its matrix phase is the short one; with an LSE it also keeps the fp32 sum.
 // * Tiles are split into fully visible ones, which run no mask code, and boundary tiles
 //   (causal diagonal, ragged tail), the trip-count split of the CUTLASS fusion point.
-// * Work order: heaviest q-tiles first (causal), and workgroups of one (sequence, head
-//   group) land on the same XCD so they share K/V in that XCD's L2.
+// * Work order: with several q-tiles per workgroup, causal q-tiles are paired heavy with
+//   light (n-1-j with j) so every workgroup gets the same number of K/V tiles; with one,
+//   heaviest first.  Workgroups of one (sequence, head group) land on the same XCD so they
+//   share K/V in that XCD's L2.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "fmha.h"
@@ -81,7 +89,6 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 buffer descriptor: raw 32-
 constexpr int kSchedMfma = 0x008;    // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedDsRead = 0x100;
 constexpr int kPrefetch = 6;         // LDS reads kept in flight ahead of the MFMAs
-constexpr int kWaitVmcnt0 = 0x0F70;           // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima
 
 enum : int { kF16 = 0, kBF16 = 1, kF8 = 2 };
 
@@ -95,7 +102,7 @@ struct Params {
   const int32_t* cu_k;
   int32_t B, Sq, Sk, H, H_kv, group;  // Sq / Sk: lengths (packed: maxima)
   int32_t total_q;                    // packed: rows of q (LSE row length)
-  int32_t n_qtiles;
+  int32_t ipw;      // q-tiles run by one workgroup, one after the other
   int32_t causal;   // 1 for both causal masks
   int32_t qend;     // causal aligned to the last key
   int32_t xcd_per;  // (sequence, head) pairs per XCD when B*H % 8 == 0, else 0
@@ -241,8 +248,8 @@ __device__ inline int swz8(int j) {
 // while group B runs the softmax of tile t-1; in phase 2t+1 the roles swap.  Each SIMD thus
 // always has one wave feeding its matrix core and one wave on the vector ALU (the two-tile
 // ping-pong of the CUTLASS design, built here from the single workgroup barrier).
-// K(t+1) and V(t) are requested at the start of phase 2t and waited for at the end of phase
-// 2t+1, two phases ahead of their first use.
+// K(t+2) and V(t+1) are requested during phases 2t and 2t+1 and waited for at the end of
+// phase 2t+3, before their first use in phase 2t+4.
 template <int DT, int D, bool LSE_SUM>
 __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   constexpr bool F8 = DT == kF8;
@@ -264,7 +271,8 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
 
   // The tile loads are inline assembly the compiler cannot see, so it inserts no waits for
   // them: every wait on them below is explicit.
-  __shared__ __attribute__((aligned(1024))) char kv_lds[NSTAGE * STAGE];
+  // LDS: the K/V stages, then one block of 32 Q rows per wave
+  __shared__ __attribute__((aligned(1024))) char kv_lds[NSTAGE * STAGE + kWaves * 32 * RB];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)kv_lds;  // LDS address of stage 0
 
   const int lane = threadIdx.x & 63;
@@ -278,19 +286,18 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   const int group = wave >> 2;             // 0 = A, 1 = B
   const int rblk = 2 * (wave & 3) + group; // 32-row block of the workgroup tile owned by this wave
 
-  // ---- which (sequence, head, q-tile) this workgroup owns ---------------------------
+  // ---- which (sequence, head) and which of its q-tiles this workgroup owns ------------
   const int BH = p.B * p.H;
   const int x = blockIdx.x;
-  int bh, qt_rev;
+  int bh, grp;
   if (p.xcd_per) {  // round-robin dispatch puts workgroup x on XCD x % 8
     const int slot = x >> 3;
-    qt_rev = slot / p.xcd_per;
+    grp = slot / p.xcd_per;
     bh = (x & 7) * p.xcd_per + slot % p.xcd_per;
   } else {
-    qt_rev = x / BH;
+    grp = x / BH;
     bh = x % BH;
   }
-  const int qt = p.n_qtiles - 1 - qt_rev;  // heaviest causal tiles first
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int kvh = h / p.group;
@@ -307,21 +314,32 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     k_row0 = b * p.Sk;
     Sk_b = p.Sk;
   }
-  const int q0 = qt * kBM;
-  if (q0 >= Sq_b) return;
+  // The workgroup runs the q-tiles ("items") in slots grp * ipw .. of its sequence one after
+  // the other, as one stream of K/V tiles: the first tiles of an item are requested during
+  // the last steps of the one before, its Q rows are loaded while that one still runs, and
+  // the output of an item is written during the next item's first softmax phase, while the
+  // other wave group keeps the matrix cores busy.  Slot order: one item per workgroup,
+  // heaviest causal tile first; several, pairs of q-tiles n-1-j and j, whose causal tile
+  // counts add up to the same total for every pair.
+  const int nq_b = (Sq_b + kBM - 1) / kBM;  // q-tiles of this sequence
+  const int slot0 = grp * p.ipw;
+  if (slot0 >= nq_b) return;
+  const int n_items = min(p.ipw, nq_b - slot0);
   const int off = p.qend ? Sk_b - Sq_b : 0;
   // keys visible to the last valid row of a row range, as an exclusive end
   auto key_end = [&](int last_row) { return p.causal ? min(Sk_b, last_row + off + 1) : Sk_b; };
-  const int wg_end = key_end(min(Sq_b, q0 + kBM) - 1);
-  const int n_tiles = wg_end > 0 ? (wg_end + kBN - 1) / kBN : 0;
-  // per wave: the first tile that some row of the wave does not see completely (the mask
-  // is applied from there on)
-  const int qw0 = q0 + 32 * rblk;
-  int w_full = 0;
-  if (qw0 < Sq_b) {
-    const int first_sees = p.causal ? min(Sk_b, qw0 + off + 1) : Sk_b;
-    w_full = first_sees > 0 ? first_sees / kBN : 0;
-  }
+  auto item_q0 = [&](int k) __attribute__((always_inline)) {  // first query row of item k
+    const int s = slot0 + k;
+    return kBM * (p.ipw == 1 ? nq_b - 1 - s : (s & 1) ? s >> 1 : nq_b - 1 - (s >> 1));
+  };
+  // K/V tiles of item k: those some row of it sees, and at least one (a row that sees no key
+  // gets a tile of masked scores, hence O = 0 and LSE = -inf)
+  auto item_tiles = [&](int k) __attribute__((always_inline)) {
+    const int e = key_end(min(Sq_b, item_q0(k) + kBM) - 1);
+    return e > 0 ? (e + kBN - 1) / kBN : 1;
+  };
+  int n_stream = 0;  // K/V tiles of the whole stream
+  for (int k = 0; k < n_items; ++k) n_stream += item_tiles(k);
 
   const uint32_t qstride = (uint32_t)p.H * D * E;     // bytes between rows of one head
   const uint32_t kstride = (uint32_t)p.H_kv * D * E;
@@ -329,34 +347,85 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   const size_t k_base = ((size_t)k_row0 * p.H_kv + kvh) * D * E;
   const uint32_t q_bytes = Sq_b > 0 ? (uint32_t)(Sq_b - 1) * qstride + RB : 0;
   const uint32_t k_bytes = Sk_b > 0 ? (uint32_t)(Sk_b - 1) * kstride + RB : 0;
-  const auto rq = make_rsrc((const char*)p.q + q_base, q_bytes);
+  const i32x4 rq = make_rsrc_words((const char*)p.q + q_base, q_bytes);
   const i32x4 rk = make_rsrc_words((const char*)p.k + k_base, k_bytes);
   const i32x4 rv = make_rsrc_words((const char*)p.v + k_base, k_bytes);
   const auto ro = make_rsrc((const char*)p.o + q_base, q_bytes);
 
-  // ---- Q fragment: B operand of S^T = K Q^T, lane owns query l32, dims 8*h32.. of each k-step
-  const int qi = qw0 + l32;  // query row inside the sequence
-  // (fp8: 32 bytes, dims 64 ks + 32 h32 .., per 64-deep k-step, in qf[2 ks], qf[2 ks + 1])
+  // per item and wave: first row, this lane's query row, the first tile that some row of
+  // the wave does not see completely (the mask is applied from there on), and the last key
+  // visible to this lane's query, less the lane's key offset 4 h32 inside a tile
+  int qw0, qi, w_full, vis_last;
+  auto set_rows = [&](int k) __attribute__((always_inline)) {
+    qw0 = item_q0(k) + 32 * rblk;
+    qi = qw0 + l32;
+    w_full = 0;
+    if (qw0 < Sq_b) {
+      const int first_sees = p.causal ? min(Sk_b, qw0 + off + 1) : Sk_b;
+      w_full = first_sees > 0 ? first_sees / kBN : 0;
+    }
+    vis_last = (p.causal ? min(Sk_b - 1, qi + off) : Sk_b - 1) - 4 * h32;
+  };
+  set_rows(0);
+
+  // ---- Q: each wave's 32 rows of an item land in its own LDS block (LDS-direct loads,
+  // swizzled like a K tile) and are read from there into the B operand of S^T = K Q^T: lane
+  // owns query l32, dims 8 h32.. of each k-step (fp8: 32 bytes, dims 64 ks + 32 h32 .., per
+  // 64-deep k-step, in qf[2 ks], qf[2 ks + 1]).  The block then takes the next item's rows.
   constexpr int NQF = F8 ? 2 * KS : KS;
-  i32x4 qf[NQF];
+  constexpr int QBLK = 32 * RB / 1024;  // 1 KiB loads per wave for its rows of an item
+  static_assert(QBLK * 1024 == 32 * RB, "a wave's Q rows are whole 1 KiB loads");
+  const uint32_t q_lds = lds0 + (uint32_t)(NSTAGE * STAGE + wave_u * 32 * RB);
+  const int rblk_u = 2 * (wave_u & 3) + (wave_u >> 2);  // rblk, in a scalar register
+  auto load_q = [&](int k) __attribute__((always_inline)) {
+    const uint32_t row0 = (uint32_t)(item_q0(k) + 32 * rblk_u) * qstride;
 #pragma unroll
-  for (int i = 0; i < NQF; ++i)
-    qf[i] = __builtin_amdgcn_raw_buffer_load_b128(
-        rq, (uint32_t)qi * qstride + (F8 ? 64 * (i >> 1) + 32 * h32 + 16 * (i & 1) : (16 * i + 8 * h32) * E), 0, 0);
-  // (Q is waited for in the prologue below, together with the first two K/V tiles.)
+    for (int i = 0; i < QBLK; ++i) {
+      const int pos = 64 * i + lane;  // 16-byte chunk position inside the wave's block
+      const int j = pos / CPR;
+      lds_load16(rq, row0 + (uint32_t)j * qstride + (((pos % CPR) ^ sw(j)) * 16), q_lds + 1024 * i);
+    }
+  };
+  i32x4 qf[NQF];
 
   // ---- K/V tile loads straight into LDS, one 1 KiB block (64 lanes x 16 B) per instruction.
   // Block b of a tile covers rows 64b/CPR.. of it; lane l fills LDS chunk (64b + l) % CPR of
   // its row j with memory chunk ((64b + l) % CPR) ^ swz(j).
   //
-  // Step t consumes L(t) = {K(t), V(t-1)} from LDS stage t % 3.  L(t+2) is requested during
-  // phases 2t and 2t+1 by all 8 waves: block b of its NBLK blocks (K first, then V) by wave
-  // b % 8 in the phase of parity (b / 8) % 2, spread over that wave's MFMA or softmax work.
-  // (Issued in bursts, or by fewer waves, the loads queue at the CU's vector-memory path and
-  // stall the issuing waves for hundreds of cycles.)  A load of a tile past either end of
-  // the sequence reads zeros, so each wave issues the same NBLK / 8 loads every step, and
-  // the number it has in flight at a step's end is that constant.
-  auto tile_off = [&](int t) __attribute__((always_inline)) -> uint32_t { return (uint32_t)(t * kBN) * kstride; };
+  // Step u of the stream consumes L(u) = {K tile of stream tile u, V tile of stream tile u-1}
+  // from LDS stage u % 3 (so the step that starts an item also holds the last V tile of the
+  // item before).  L(u+2) is requested during phases 2u and 2u+1 by all 8 waves: block b of
+  // its NBLK blocks (K first, then V) by wave b % 8 in the phase of parity (b / 8) % 2, spread
+  // over that wave's MFMA or softmax work.  (Issued in bursts, or by fewer waves, the loads
+  // queue at the CU's vector-memory path and stall the issuing waves for hundreds of
+  // cycles.)  A load of a tile past either end of the sequence reads zeros, so each wave
+  // issues the same NBLK / 8 loads every step.  The waits count this wave's requests: "at
+  // most N in flight" covers every request older than the N newest, so the Q loads and O
+  // stores that some steps add can only make a wait stricter, never looser.
+  // Request cursor, at L(c): K tile lt of item litem (ln tiles), V tile of the item of L(c-1)
+  // (tile -1 before the first; past the last item the K tile index runs on past its end), as
+  // byte offsets in the K/V rows, and the LDS address of stage c % 3 plus this wave's first
+  // block.  Kept as running sums: the loop carries no multiplies or remainders for them.
+  const uint32_t tile_bytes = (uint32_t)kBN * kstride;
+  constexpr uint32_t kStages = NSTAGE * STAGE;
+  static_assert(7 * 1024 < STAGE, "a wave's block offset stays inside the first stage");
+  int lt = 0, ln = item_tiles(0), litem = 0;
+  uint32_t lk_off = 0, lv_off = 0u - tile_bytes;
+  uint32_t l_st = lds0 + (uint32_t)wave_u * 1024;
+  auto advance = [&]() __attribute__((always_inline)) {
+    lv_off = lk_off;
+    l_st += STAGE;
+    if (l_st >= lds0 + kStages) l_st -= kStages;
+    if ((lt + 1 < ln) | (litem + 1 >= n_items)) {
+      ++lt;
+      lk_off += tile_bytes;
+    } else {
+      ++litem;
+      lt = 0;
+      lk_off = 0;
+      ln = item_tiles(litem);
+    }
+  };
   uint32_t ld_off[2][LPP];  // per-lane byte offsets inside a tile of this wave's blocks
 #pragma unroll
   for (int pp = 0; pp < 2; ++pp)
@@ -367,14 +436,13 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       const int j = pos / CPR;
       ld_off[pp][i] = (uint32_t)j * kstride + (((pos % CPR) ^ sw(j)) * 16);
     }
-  // load i of phase parity pp for L(tl), tl >= 0, into stage tl % 3
-  auto load_unit = [&](int tl, int pp, int i) __attribute__((always_inline)) {
+  // load i of phase parity pp for the cursor's L(c) into stage c % 3
+  auto load_unit = [&](int pp, int i) __attribute__((always_inline)) {
     const int b0 = 16 * i + 8 * pp;  // first block of this (pp, i) over the 8 waves
     if (b0 >= NBLK) return;          // compile-time after unrolling
     const bool is_k = b0 + 8 <= KBLK ? true : b0 >= KBLK ? false : b0 + wave_u < KBLK;
-    const uint32_t goff = (is_k ? tile_off(tl) : tile_off(tl - 1)) + ld_off[pp][i];
-    const uint32_t lds_addr = lds0 + (uint32_t)((tl % NSTAGE) * STAGE + (b0 + wave_u) * 1024);
-    lds_load16(is_k ? rk : rv, goff, __builtin_amdgcn_readfirstlane(lds_addr));
+    const uint32_t goff = (is_k ? lk_off : lv_off) + ld_off[pp][i];
+    lds_load16(is_k ? rk : rv, goff, __builtin_amdgcn_readfirstlane(l_st + b0 * 1024));
   };
 
   f32x16 acc_o[NDB];
@@ -394,8 +462,6 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   float l_run2 = 0.0f;
   constexpr bool VSUM = !F8 || LSE_SUM;  // keep the VALU row sum
   const float sl2 = p.scale_log2;
-  // last key visible to this lane's query, less the lane's key offset 4 h32 inside a tile
-  const int vis_last = (p.causal ? min(Sk_b - 1, qi + off) : Sk_b - 1) - 4 * h32;
 
   // Per-lane LDS byte offsets.  The swizzle only touches chunk bits that the k-step (K) or
   // the d-block (V) index leaves clear, so every read address is one of these bases XOR a
@@ -414,6 +480,20 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   const int v_part = F8 ? g16 : 2 * g16 + ((s16 & 3) >> 1);
   const int v_lane0 = TILE + v_row0 * RB + ((v_part ^ sw(v_row0)) * 16) + 8 * (s16 & 1);
   const int v_lane1 = TILE + (v_row0 + 8) * RB + ((v_part ^ sw(v_row0 + 8)) * 16) + 8 * (s16 & 1);
+
+  // Q fragment from the wave's LDS block (the K read addresses: the rows are swizzled alike).
+  // The values are pinned before the block may take the next item's rows.
+  auto read_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NQF; ++i) {
+      if constexpr (F8)
+        qf[i] = *(const lds_i32x4*)(uintptr_t)(((i & 1) ? q_lds + k_lane2 : q_lds + k_lane) ^ (64 * (i >> 1)));
+      else
+        qf[i] = *(const lds_i32x4*)(uintptr_t)((q_lds + k_lane) ^ (32 * i));
+    }
+#pragma unroll
+    for (int i = 0; i < NQF; ++i) asm volatile("" : "+v"(qf[i]));
+  };
 
   // one QK^T MFMA of the tile: k-step ks of key block jb (ka, kb: k_lane, k_lane2 + the
   // stage's address)
@@ -466,13 +546,15 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   constexpr int RQK = F8 ? 2 : 1;            // LDS reads per S^T MFMA
   constexpr int RPV = F8 ? 4 : 2;            // LDS reads per O^T MFMA
 
-  // matrix phase of tile t: S(t) = K(t) Q^T and O += V(t-1) P(t-1), from LDS stage t % 3;
-  // hook(j), j < LPP, issues this wave's loads of the phase.  Every wave runs every tile of
+  auto pin_l = [&]() __attribute__((always_inline)) {
+    if constexpr (F8) asm volatile("" : "+v"(acc_l));
+  };
+  // matrix phase of stream tile u: S(u) = K(u) Q^T and O += V(u-1) P(u-1), from the LDS stage
+  // at st (stage u % 3); hook(j), j < LPP, issues this wave's loads of the phase.  Every wave runs every tile of
   // the workgroup: past a wave's last visible tile its probabilities are zero, and the
   // phase takes as long as the busiest wave of the group anyway.
-  auto matrix_phase = [&](int t, auto& hook) __attribute__((always_inline)) {
+  auto matrix_phase = [&](uint32_t st, auto& hook) __attribute__((always_inline)) {
     constexpr int N = NQK > NPV ? NQK : NPV;
-    const uint32_t st = lds0 + (uint32_t)((t % NSTAGE) * STAGE);
     uint32_t ka = k_lane + st, kb = k_lane2 + st, va0 = v_lane0 + st, va1 = v_lane1 + st;
     // keep derived addresses out of loop-invariant code
     if constexpr (F8)
@@ -507,6 +589,12 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPV, 0);
       }
     }
+    // Pin the products here: the compiler may otherwise sink MFMAs past the phase barrier,
+    // into the softmax or the epilogue of an item that follows on this wave.
+    asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(acc_o[db]));
+    pin_l();
   };
 
   // softmax phase of tile t: mask, running max, lazy rescale, probabilities; hook(j), j <
@@ -603,9 +691,9 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
 
   // The matrix work runs at raised wave priority so the SIMD issues its MFMAs ahead of the
   // softmax VALU work of the other group's wave.
-  auto matrix_prio = [&](int t, auto& hook) __attribute__((always_inline)) {
+  auto matrix_prio = [&](uint32_t st, auto& hook) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
-    matrix_phase(t, hook);
+    matrix_phase(st, hook);
     __builtin_amdgcn_s_setprio(0);
   };
   // The loads of phase ph request part ph % 2 of L(ph / 2 + 2).  At the end of an odd phase
@@ -616,103 +704,229 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     wait_vmcnt<NBLK / 8>();
     phase_barrier();
   };
-  auto no_work = [&](int tl, auto pp_tag) __attribute__((always_inline)) {
+  auto no_work = [&](auto pp_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < LPP; ++i) load_unit(tl, decltype(pp_tag)::value, i);
+    for (int i = 0; i < LPP; ++i) load_unit(decltype(pp_tag)::value, i);
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
 
-  // prologue: L(0) (K(0) and the zero V(-1)) and L(1) into stages 0 and 1
-  no_work(0, P0{});
-  no_work(0, P1{});
-  no_work(1, P0{});
-  no_work(1, P1{});
-  // Wait for Q and the tiles with the builtin (whose effect the compiler tracks): otherwise
-  // it keeps partial vmcnt waits for Q inside the loop, and those would also stall on the
-  // K/V loads.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  phase_barrier();
-  // Phases 0 .. 2 n_tiles + 1.  Group A: matrix(t) in phase 2t, softmax(t) in 2t+1.  Group B:
-  // softmax(t-1) in phase 2t, matrix(t) in 2t+1.  Each group runs its own straight loop
-  // (the two meet at the same barriers), so no phase body branches on the group.
-  if (group == 0) {
-    for (int t = 0; t < n_tiles; ++t) {
-      auto h0 = [&](int i) __attribute__((always_inline)) { load_unit(t + 2, 0, i); };
-      auto h1 = [&](int i) __attribute__((always_inline)) { load_unit(t + 2, 1, i); };
-      matrix_prio(t, h0);
-      even_end();
-      softmax_phase(t, h1);
-      odd_end();
+  // ---- epilogue of an item: normalise, scale, convert, store; LSE.  A lane swap with lane
+  // l^32 gives every lane 8 consecutive head dims of its row (16 bytes for 16-bit O).  Rows
+  // past the sequence fall outside the O descriptor and are dropped.  Issues NST stores of O
+  // (and one LSE store where due) and clears the item state.
+  constexpr int NST = 2 * NDB;
+  auto epilogue = [&]() __attribute__((always_inline)) {
+    const float l_tot = F8 ? acc_l[0] : wave_row_sum(l_run + l_run2);
+    const float inv = l_tot > 0.0f ? p.o_scale / l_tot : 0.0f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        // quads g = 2 gp (dims 16 gp + 4 h32 ..) and 2 gp + 1 (dims 16 gp + 8 + 4 h32 ..): after
+        // the swap the lane holds dims 32 db + 16 gp + 8 h32 + 0..7
+        const int g0 = 2 * gp, g1 = 2 * gp + 1;
+        const uint32_t byte = (uint32_t)(32 * db + 16 * gp + 8 * h32) * E;
+        if constexpr (F8) {  // saturate to the largest finite e4m3 value, then round
+          float x0[4], x1[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            x0[u] = __builtin_fminf(__builtin_fmaxf(acc_o[db][4 * g0 + u] * inv, -448.0f), 448.0f);
+            x1[u] = __builtin_fminf(__builtin_fmaxf(acc_o[db][4 * g1 + u] * inv, -448.0f), 448.0f);
+          }
+          auto r = __builtin_amdgcn_permlane32_swap(pack_f8x4(x0[0], x0[1], x0[2], x0[3]),
+                                                    pack_f8x4(x1[0], x1[1], x1[2], x1[3]), false, false);
+          const i32x2 w = {(int)r[0], (int)r[1]};
+          __builtin_amdgcn_raw_buffer_store_b64(w, ro, (uint32_t)qi * qstride + byte, 0, 0);
+        } else {
+          auto r0 = __builtin_amdgcn_permlane32_swap(T::pack(acc_o[db][4 * g0] * inv, acc_o[db][4 * g0 + 1] * inv),
+                                                     T::pack(acc_o[db][4 * g1] * inv, acc_o[db][4 * g1 + 1] * inv),
+                                                     false, false);
+          auto r1 = __builtin_amdgcn_permlane32_swap(
+              T::pack(acc_o[db][4 * g0 + 2] * inv, acc_o[db][4 * g0 + 3] * inv),
+              T::pack(acc_o[db][4 * g1 + 2] * inv, acc_o[db][4 * g1 + 3] * inv), false, false);
+          const i32x4 w = {(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]};
+          __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)qi * qstride + byte, 0, 0);
+        }
+      }
+    // (fp8: the LSE takes the fp32 sum, which a 3-bit-mantissa rounding would move by up to ~0.06)
+    const float l_exact = F8 && LSE_SUM ? wave_row_sum(l_run + l_run2) : l_tot;  // (all lanes: a lane swap)
+    if (p.lse && h32 == 0 && qi < Sq_b) {
+      const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_exact) - (F8 ? kF8Shift : 0.0f)) *
+                                           0.69314718055994531f
+                                     : -__builtin_inff();
+      const size_t idx = p.cu_q ? (size_t)h * p.total_q + q_row0 + qi : ((size_t)b * p.H + h) * p.Sq + qi;
+      p.lse[idx] = lse;
     }
-    {
-      auto h0 = [&](int i) __attribute__((always_inline)) { load_unit(n_tiles + 2, 0, i); };
-      matrix_prio(n_tiles, h0);  // O += V(n-1) P(n-1)
-      even_end();
-      no_work(n_tiles + 2, P1{});
-      odd_end();
-    }
-  } else {
-    no_work(2, P0{});
-    even_end();
-    for (int t = 0; t < n_tiles; ++t) {
-      auto h1 = [&](int i) __attribute__((always_inline)) { load_unit(t + 2, 1, i); };
-      auto h0 = [&](int i) __attribute__((always_inline)) { load_unit(t + 3, 0, i); };
-      matrix_prio(t, h1);
-      odd_end();
-      softmax_phase(t, h0);
-      even_end();
-    }
-    {
-      auto h1 = [&](int i) __attribute__((always_inline)) { load_unit(n_tiles + 2, 1, i); };
-      matrix_prio(n_tiles, h1);
-      odd_end();
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the requests past the end (they write LDS)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
+    if constexpr (F8) acc_l = f32x16{};
+    l_run = 0.0f;
+    l_run2 = 0.0f;
+    m_run = -__builtin_inff();
+  };
 
-  // ---- epilogue: normalise, scale, convert; stage each wave's 32 x D tile of O through LDS
-  // (free now) so the stores write whole rows, 16 bytes per lane, instead of 16-byte pieces
-  // of 32 rows.  Rows past the sequence fall outside the O descriptor and are dropped.
-  phase_barrier();  // every wave's requests past the end have landed and its reads are done
-  const float l_tot = F8 ? acc_l[0] : wave_row_sum(l_run + l_run2);
-  const float inv = l_tot > 0.0f ? p.o_scale / l_tot : 0.0f;
-  constexpr int OST = RB + 16;  // LDS bytes per staged O row (padded against bank conflicts)
-  static_assert(kWaves * 32 * OST <= NSTAGE * STAGE, "O staging fits in the K/V stages");
-  char* const ot = kv_lds + wave * 32 * OST;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d = 32 * db + 8 * g + 4 * h32;
-      if constexpr (F8) {  // saturate to the largest finite e4m3 value, then round
-        float x[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = __builtin_fminf(__builtin_fmaxf(acc_o[db][4 * g + u] * inv, -448.0f), 448.0f);
-        *(uint32_t*)(ot + l32 * OST + d) = pack_f8x4(x[0], x[1], x[2], x[3]);
+  // ---- prologue: Q of the first item, L(0) (K of its first tile and the zero V(-1)) and L(1)
+  // into stages 0 and 1; the phases start once Q and L(0) are in (L(1) is waited for at the
+  // end of phase 1, like every later tile).  Then the block takes the second item's Q rows.
+  load_q(0);
+  no_work(P0{});
+  no_work(P1{});
+  advance();
+  no_work(P0{});
+  no_work(P1{});
+  advance();
+  wait_vmcnt<NBLK / 8>();
+  phase_barrier();
+  read_q();
+  if (n_items > 1) load_q(1);
+
+  // Phases 0 .. 2 n_stream + 1.  Group A: matrix(u) in phase 2u, softmax(u) in 2u+1.  Group
+  // B: softmax(u-1) in phase 2u, matrix(u) in 2u+1.  Each group runs its own straight loop
+  // (the two meet at the same barriers), so no phase body branches on the group.  Item
+  // changes: matrix(u) of the first tile u of item k multiplies item k's Q and adds the last
+  // PV product of item k-1, so item k-1 is written out at the start of softmax(u); item k's Q
+  // is read from LDS at the end of softmax(u-1) (its rows were requested at least one step
+  // earlier, so at least NBLK / 8 newer requests stand behind them there).
+  // compute cursor: item, tile inside it, its tiles, LDS address of stage u % 3
+  int k = 0, t = 0, nt = item_tiles(0);
+  uint32_t c_st = lds0;
+  auto next_tile = [&]() __attribute__((always_inline)) {
+    c_st += STAGE;
+    if (c_st >= lds0 + kStages) c_st -= kStages;
+    if (++t == nt) {
+      ++k;
+      t = 0;
+      nt = item_tiles(k);
+    }
+  };
+  // Steps come in two builds.  A plain step neither starts nor ends an item, and neither of
+  // its requests moves the cursor into the next item: it runs without any of that control
+  // code (in the softmax phase every extra instruction costs issue time).  The others, the
+  // first tile of an item after the first and the last three tiles of an item before the
+  // last, are special steps with the full bookkeeping.  plain_end() is the end of the run of
+  // plain steps that starts at step u (u itself when step u is special).
+  auto plain_end = [&](int u) __attribute__((always_inline)) {
+    if ((t == 0) & (k > 0)) return u;
+    const int lim = k + 1 == n_items ? n_stream : u - t + nt - 3;
+    return lim > u ? lim : u;
+  };
+  auto plain_advance = [&]() __attribute__((always_inline)) {
+    lv_off = lk_off;
+    lk_off += tile_bytes;
+    ++lt;
+    l_st += STAGE;
+    if (l_st >= lds0 + kStages) l_st -= kStages;
+  };
+  auto plain_next_tile = [&]() __attribute__((always_inline)) {
+    ++t;
+    c_st += STAGE;
+    if (c_st >= lds0 + kStages) c_st -= kStages;
+  };
+  auto h0 = [&](int i) __attribute__((always_inline)) { load_unit(0, i); };
+  auto h1 = [&](int i) __attribute__((always_inline)) { load_unit(1, i); };
+  if (group == 0) {
+    auto step = [&](auto special_tag) __attribute__((always_inline)) {
+      constexpr bool SPECIAL = decltype(special_tag)::value;
+      matrix_prio(c_st, h0);
+      even_end();
+      const bool first = SPECIAL && (t == 0) & (k > 0);
+      if (first) {
+        epilogue();
+        set_rows(k);
+      }
+      softmax_phase(t, h1);
+      // At the end of the phase L(u+1) must have landed.  The newest requests are this step's
+      // NBLK / 8 for L(u+2), and after an epilogue also its NST stores of O.
+      if (first)
+        wait_vmcnt<NBLK / 8 + NST>();
+      else
+        wait_vmcnt<NBLK / 8>();
+      if (SPECIAL && (t == nt - 1) & (k + 1 < n_items)) {
+        read_q();
+        if (k + 2 < n_items) load_q(k + 2);
+      }
+      phase_barrier();
+      if constexpr (SPECIAL) {
+        advance();
+        next_tile();
       } else {
-        const i32x2 w = {(int)T::pack(acc_o[db][4 * g] * inv, acc_o[db][4 * g + 1] * inv),
-                         (int)T::pack(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv)};
-        *(i32x2*)(ot + l32 * OST + d * E) = w;
+        plain_advance();
+        plain_next_tile();
+      }
+    };
+    for (int u = 0; u < n_stream;) {
+      for (const int e = plain_end(u); u < e; ++u) step(std::false_type{});
+      if (u < n_stream) {
+        step(std::true_type{});
+        ++u;
       }
     }
-  constexpr int RPI = 64 / CPR;  // rows per store instruction
-#pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    const int row = i * RPI + lane / CPR, chunk = lane % CPR;
-    const i32x4 w = *(const i32x4*)(ot + row * OST + chunk * 16);
-    __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)(qw0 + row) * qstride + chunk * 16, 0, 0);
+    matrix_prio(c_st, h0);  // O += V P of the last tile
+    even_end();
+    no_work(P1{});
+    odd_end();
+  } else {
+    no_work(P0{});
+    even_end();
+    auto step = [&](auto special_tag) __attribute__((always_inline)) {
+      constexpr bool SPECIAL = decltype(special_tag)::value;
+      matrix_prio(c_st, h1);
+      odd_end();
+      if constexpr (SPECIAL) {
+        advance();
+        if ((t == 0) & (k > 0)) {
+          epilogue();
+          set_rows(k);
+          if (k + 1 < n_items) load_q(k + 1);
+        }
+      } else {
+        plain_advance();
+      }
+      softmax_phase(t, h0);
+      if (SPECIAL && (t == nt - 1) & (k + 1 < n_items)) {
+        // item k+1's rows were requested at the start of this phase (a one-tile item k > 0:
+        // only this phase's LPP loads are newer) or at least one step earlier
+        if (nt == 1)
+          wait_vmcnt<LPP>();
+        else
+          wait_vmcnt<NBLK / 8>();
+        read_q();
+      }
+      even_end();
+      if constexpr (SPECIAL)
+        next_tile();
+      else
+        plain_next_tile();
+    };
+    for (int u = 0; u < n_stream;) {
+      for (const int e = plain_end(u); u < e; ++u) step(std::false_type{});
+      if (u < n_stream) {
+        step(std::true_type{});
+        ++u;
+      }
+    }
+    matrix_prio(c_st, h1);
+    odd_end();
   }
-  // (fp8: the LSE takes the fp32 sum, which a 3-bit-mantissa rounding would move by up to ~0.06)
-  const float l_exact = F8 && LSE_SUM ? wave_row_sum(l_run + l_run2) : l_tot;  // (all lanes: a lane swap)
-  if (p.lse && h32 == 0 && qi < Sq_b) {
-    const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_exact) - (F8 ? kF8Shift : 0.0f)) *
-                                         0.69314718055994531f
-                                   : -__builtin_inff();
-    const size_t idx = p.cu_q ? (size_t)h * p.total_q + q_row0 + qi : ((size_t)b * p.H + h) * p.Sq + qi;
-    p.lse[idx] = lse;
-  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the requests past the end (they write LDS)
+  epilogue();
 }
+// compute units of the current device (cached per device; 0 if the query fails)
+int compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 template <int DT, int D>
 hipError_t launch(const Params& p, int grid, hipStream_t stream) {
   // fp8 keeps an fp32 row sum beside the matrix-core one when an LSE is wanted (see the kernel)
@@ -774,8 +988,9 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
   const int64_t rows_k = packed ? varlen->total_length_k : Sk;
   const int64_t lim = (int64_t)1 << 31;
   if (rows_q * H * D * esz >= lim || rows_k * H_kv * D * esz >= lim) return FMHA_ERR_UNSUPPORTED;
-  // tiles requested one before and two past the keys must not wrap the 32-bit offset
-  if ((int64_t)3 * kBN * H_kv * D * esz >= lim) return FMHA_ERR_UNSUPPORTED;
+  // tiles requested one before and two past the keys, and the rows of a partial last q-tile
+  // past the end of a sequence, must not wrap the 32-bit offset
+  if ((int64_t)3 * kBN * H_kv * D * esz >= lim || (int64_t)kBM * H * D * esz >= lim) return FMHA_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || Sq == 0 || (packed && varlen->total_length_q == 0)) return FMHA_OK;
 
   Params p;
@@ -793,11 +1008,20 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
   p.H_kv = H_kv;
   p.group = H / H_kv;
   p.total_q = packed ? varlen->total_length_q : 0;
-  p.n_qtiles = (Sq + kBM - 1) / kBM;
   p.causal = mask == FMHA_MASK_CAUSAL_QBEGIN || mask == FMHA_MASK_CAUSAL_QEND;
   p.qend = mask == FMHA_MASK_CAUSAL_QEND;
   const int64_t BH = (int64_t)B * H;
-  const int64_t grid = BH * p.n_qtiles;
+  const int64_t n_qtiles = (Sq + kBM - 1) / kBM;  // per sequence (packed: of the longest)
+  // q-tiles per workgroup: as many as leave one workgroup per compute unit or more, at most 8,
+  // even when causal (pairs of a heavy and a light tile); one when there is less work
+  const int cus = compute_units();
+  if (cus < 1) return FMHA_ERR_HIP;
+  int64_t ipw = BH * n_qtiles / cus;
+  ipw = ipw < 1 ? 1 : ipw > 8 ? 8 : ipw;
+  if (ipw > n_qtiles) ipw = n_qtiles;
+  if (p.causal && ipw > 1) ipw &= ~(int64_t)1;
+  p.ipw = (int32_t)ipw;
+  const int64_t grid = BH * ((n_qtiles + ipw - 1) / ipw);
   if (grid >= lim) return FMHA_ERR_UNSUPPORTED;
   p.xcd_per = (BH % 8 == 0) ? (int32_t)(BH / 8) : 0;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);

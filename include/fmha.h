@@ -59,8 +59,8 @@ typedef enum {
                                     cu_seqlens pointer is set */
   FMHA_ERR_INVALID_SHAPE = 2,    /* negative sizes, H % H_kv != 0, D not in {32, 64, 128}, totals < 0 */
   FMHA_ERR_UNSUPPORTED = 3,      /* dtype/mask enum out of range, fp8 with D == 32, or a tensor too
-                                    large for 32-bit offsets (any tensor of 2^31 bytes or more, or
-                                    192 K/V rows of 2^31 bytes or more) */
+                                    large for 32-bit offsets (any tensor of 2^31 bytes or more,
+                                    192 K/V rows or 256 Q rows of 2^31 bytes or more) */
   FMHA_ERR_MISALIGNED = 4,       /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   FMHA_ERR_INVALID_ARGUMENT = 5, /* scale not finite and > 0, or o_scale not finite */
   FMHA_ERR_HIP = 6               /* the kernel launch failed (hipGetLastError) */

@@ -53,6 +53,7 @@ def call(**kw):
     (dict(dtype=3), 3), (dict(dtype=-1), 3), (dict(mask=4), 3), (dict(mask=-1), 3),
     (dict(Sq=1 << 22, H=64, H_kv=64, D=128), 3),
     (dict(dtype="f8e4m3", D=32), 3), (dict(H=1 << 16, H_kv=1 << 16, D=128, Sq=1, Sk=1), 3),
+    (dict(H=1 << 15, H_kv=1, D=128, Sq=1, Sk=1), 3),
     (dict(q=P + 2), 4), (dict(o=P + 8), 4), (dict(lse=P + 2), 4),
     (dict(scale=0.0), 5), (dict(scale=-0.1), 5), (dict(scale=float("inf")), 5), (dict(scale=float("nan")), 5),
     (dict(o_scale=float("inf")), 5), (dict(o_scale=float("nan")), 5),

@@ -113,6 +113,54 @@ def test_bitwise_repeatable():
 
 
 # ----------------------------------------------------------------------------------------------
+# several q-tiles per workgroup: enough (sequence, head, q-tile) items that every workgroup runs
+# two or more of them as one K/V stream (item changes, one- and two-tile items, ragged tiles)
+# ----------------------------------------------------------------------------------------------
+def _items_per_workgroup(B, H, Sq, mask):
+    """The launch rule of the library: q-tiles of 256 rows, about one workgroup per compute unit,
+    at most 8 per workgroup, pairs when causal."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_qt = (Sq + 255) // 256
+    ipw = max(1, min(8, B * H * n_qt // cus, n_qt))
+    if mask.startswith("causal") and ipw > 1:
+        ipw &= ~1
+    return ipw
+
+
+MULTI_ITEM = [
+    # (B, Sq, Sk, H, H_kv, D, dtype, mask)
+    (1, 1000, 1000, 128, 128, 64, "bf16", "causal_qbegin"),   # heavy/light pairs, ragged last q-tile
+    (2, 1024, 50, 128, 32, 128, "f16", "causal_qend"),        # one-tile items (rows without keys too)
+    (1, 1024, 100, 256, 64, 64, "bf16", "residual"),          # two-tile items: every step special
+    (1, 1030, 230, 256, 256, 32, "f16", "causal_qbegin"),     # four-tile items, D 32
+    (1, 1100, 300, 128, 8, 128, "bf16", "none"),              # five q-tiles: a lone last item
+]
+
+
+@pytest.mark.parametrize("case", MULTI_ITEM, ids=lambda c: f"S{c[1]}x{c[2]}-H{c[3]}/{c[4]}-D{c[5]}-{c[6]}-{c[7]}")
+def test_several_qtiles_per_workgroup(case):
+    B, Sq, Sk, H, H_kv, D, dtype, mask = case
+    ipw = _items_per_workgroup(B, H, Sq, mask)
+    log(f"[multi-item] {ipw} q-tiles per workgroup")
+    assert ipw >= 2, "the case no longer covers several q-tiles per workgroup"
+    _dense_case(f"multi-item {case}", make_dense(2900 + Sq + Sk, B, Sq, Sk, H, H_kv, D, dtype, mask=mask))
+
+
+@pytest.mark.parametrize("mask", ["none", "causal_qend"])
+def test_several_qtiles_per_workgroup_fp8(mask):
+    assert _items_per_workgroup(1, 128, 1100, mask) >= 2
+    inp = make_dense(2950, 1, 1100, 300, 128, 16, 128, "f8e4m3", mask=mask, o_scale=0.5)
+    _dense_case(f"multi-item fp8 {mask}", inp)
+
+
+def test_several_qtiles_per_workgroup_repeatable():
+    inp = make_dense(2960, 1, 1000, 700, 128, 32, 128, "bf16", mask="causal_qend")
+    assert _items_per_workgroup(1, 128, 1000, "causal_qend") >= 2
+    runs = [run_dense(inp, want_lse=True) for _ in range(2)]
+    assert np.array_equal(runs[1].o_bits, runs[0].o_bits) and np.array_equal(runs[1].lse, runs[0].lse)
+
+
+# ----------------------------------------------------------------------------------------------
 # packed variable-length batches
 # ----------------------------------------------------------------------------------------------
 def _varlen_case(name, inp, want_lse=True):
@@ -169,6 +217,16 @@ def test_varlen_poisoned_padding_never_read_fp8():
 def test_varlen_poisoned_padding_never_read():
     inp = make_varlen(2700, [100, 37, 250], [90, 300, 5], 4, 2, 64, "bf16", mask="causal_qend", poison_pads=True)
     _varlen_case("varlen NaN pads", inp)
+
+
+def test_varlen_several_qtiles_per_workgroup():
+    # q-tiles per sequence from 0 to 4 under one launch rule (4 per workgroup): workgroups of the
+    # short sequences run fewer items, or none
+    lq = [1000, 300, 64, 1, 0, 513, 777, 256]
+    lk = [900, 310, 64, 1, 5, 600, 1000, 40]
+    inp = make_varlen(2970, lq, lk, 128, 16, 64, "bf16", mask="causal_qend", poison_pads=True)
+    assert _items_per_workgroup(len(lq), 128, max(lq), "causal_qend") >= 2
+    _varlen_case("varlen multi-item", inp)
 
 
 def test_varlen_equals_dense_runs():
