@@ -35,19 +35,19 @@
 //   raised when a tile's maximum exceeds it by more than 2^8 (a lazy rescale in the spirit
 //   of the article's section "lazy rescale": probabilities stay <= 256, far inside the
 //   range of the 16-bit and fp8 operand types, and the O rescale is skipped for most tiles).
-// * The row sum l: on tiles that need the mask (the causal diagonal, the ragged tail) it
-//   adds the rounded 16-bit probabilities the matrix cores see, so a row with few visible
-//   keys is normalised by exactly the weights of its numerator; on fully visible tiles it
-//   adds the fp32 probabilities (as the FlashAttention papers do), two VALU operations
-//   cheaper per pair.  Both use two independent partial sums per lane.  (v_dot2 against
-//   1.0 would sum the rounded values in one operation, but on gfx950 the dot instructions
-//   wait behind the MFMAs of the wave that shares the SIMD: the softmax phase took 15%
-//   longer with them.)
-//   fp8 sums on the matrix cores instead (an all-ones operand against the probability
-//   operand of the PV product: one more MFMA per tile, exact sums of the rounded values),
-//   since its matrix phase is the short one; with an LSE it also keeps the fp32 sum.
-// * Tiles are split into fully visible ones, which run no mask code, and boundary tiles
-//   (causal diagonal, ragged tail), the trip-count split of the CUTLASS fusion point.
+// * The row sum l: on tiles that need the mask (the causal diagonal, the ragged tail) the
+//   matrix cores add the rounded probabilities they multiply (an all-ones operand against
+//   the probability operand of the PV product: 4 more MFMAs per 64-key tile, exact in
+//   fp32), so a row with few visible keys is normalised by exactly the weights of its
+//   numerator; on fully visible tiles the vector ALU adds the fp32 probabilities (as the
+//   FlashAttention papers do), with two independent partial sums per lane.  Summing every
+//   tile on the matrix cores cost more than it saved once the VALU and MFMA phases are
+//   balanced; v_dot2 against 1.0 waits behind the other wave's MFMAs on gfx950.  fp8 sums
+//   every tile on the matrix cores (one MFMA per tile), since its matrix phase is the
+//   short one; with an LSE it also keeps the fp32 sum.
+// * Steps over tiles that every row sees completely run a build with no mask code at all;
+//   boundary tiles (causal diagonal, ragged tail) run the masked build, the trip-count
+//   split of the CUTLASS fusion point.
 // * Work order: with several q-tiles per workgroup, causal q-tiles are paired heavy with
 //   light (n-1-j with j) so every workgroup gets the same number of K/V tiles; with one,
 //   heaviest first.  Workgroups of one (sequence, head group) land on the same XCD so they
@@ -354,12 +354,14 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
 
   // per item and wave: first row, this lane's query row, the first tile that some row of
   // the wave does not see completely (the mask is applied from there on), and the last key
-  // visible to this lane's query, less the lane's key offset 4 h32 inside a tile
+  // visible to this lane's query, less the lane's key offset 4 h32 inside a tile.  The first
+  // row of an item sees the fewest keys, so item_full(k), the first tile that some row of
+  // the item does not see completely, is the least w_full of its waves.
   int qw0, qi, w_full, vis_last;
   auto set_rows = [&](int k) __attribute__((always_inline)) {
     qw0 = item_q0(k) + 32 * rblk;
     qi = qw0 + l32;
-    w_full = 0;
+    w_full = 0x7fffffff;  // a wave with no row in the sequence: its output is dropped anyway
     if (qw0 < Sq_b) {
       const int first_sees = p.causal ? min(Sk_b, qw0 + off + 1) : Sk_b;
       w_full = first_sees > 0 ? first_sees / kBN : 0;
@@ -367,6 +369,10 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     vis_last = (p.causal ? min(Sk_b - 1, qi + off) : Sk_b - 1) - 4 * h32;
   };
   set_rows(0);
+  auto item_full = [&](int k) __attribute__((always_inline)) {
+    const int first_sees = p.causal ? min(Sk_b, item_q0(k) + off + 1) : Sk_b;
+    return first_sees > 0 ? first_sees / kBN : 0;
+  };
 
   // ---- Q: each wave's 32 rows of an item land in its own LDS block (LDS-direct loads,
   // swizzled like a K tile) and are read from there into the B operand of S^T = K Q^T: lane
@@ -451,12 +457,16 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   f32x16 s[2];                      // scores of the tile between its matrix and softmax phases
   constexpr int NPK = F8 ? 4 : 8;   // packed probability registers per 32-key block
   uint32_t pk[2][NPK] = {};         // probabilities of the tile between its softmax and PV phases
+  bool pk_masked = false;           // 16-bit: pk holds a masked tile, whose row sum the matrix cores add
   float m_run = -__builtin_inff();  // running max of scale*log2(e)*s for query l32
-  // fp8 row sums on the matrix cores: an all-ones A operand against the probability
-  // operand of the PV product, so every element of acc_l holds the row sum of this lane's
-  // query over the rounded probabilities that O is built from (exact in fp32).  (The fp8
-  // matrix phase is half as long as the softmax, so the MFMA is the cheap place for it; the
-  // 16-bit paths keep it on the vector ALU, where their longer matrix phase hides it.)
+  // Row sums on the matrix cores: an all-ones A operand against the probability operand of
+  // the PV product, so every element of acc_l holds the row sum of this lane's query over the
+  // rounded probabilities that O is built from (exact in fp32).  fp8 sums every tile there
+  // (its matrix phase is half as long as the softmax, so the MFMA is the cheap place); the
+  // 16-bit paths only the tiles that needed the mask (4 MFMAs after the tile's PV product),
+  // where a row with few visible keys must be normalised by exactly the weights of its
+  // numerator, and add the fp32 probabilities of fully visible tiles on the vector ALU
+  // (l_run + l_run2), where the longer 16-bit matrix phase hides them.
   f32x16 acc_l = {};
   float l_run = 0.0f;  // this lane's part of the VALU row sum (l_run + l_run2)
   float l_run2 = 0.0f;
@@ -547,13 +557,16 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   constexpr int RPV = F8 ? 4 : 2;            // LDS reads per O^T MFMA
 
   auto pin_l = [&]() __attribute__((always_inline)) {
-    if constexpr (F8) asm volatile("" : "+v"(acc_l));
+    asm volatile("" : "+v"(acc_l));
   };
   // matrix phase of stream tile u: S(u) = K(u) Q^T and O += V(u-1) P(u-1), from the LDS stage
   // at st (stage u % 3); hook(j), j < LPP, issues this wave's loads of the phase.  Every wave runs every tile of
   // the workgroup: past a wave's last visible tile its probabilities are zero, and the
   // phase takes as long as the busiest wave of the group anyway.
-  auto matrix_phase = [&](uint32_t st, auto& hook) __attribute__((always_inline)) {
+  // MASKABLE (special steps): the previous tile may have been masked, and then its row sums
+  // are added here.
+  auto matrix_phase = [&](uint32_t st, auto& hook, auto maskable_tag) __attribute__((always_inline)) {
+    constexpr bool MASKABLE = decltype(maskable_tag)::value;
     constexpr int N = NQK > NPV ? NQK : NPV;
     uint32_t ka = k_lane + st, kb = k_lane2 + st, va0 = v_lane0 + st, va1 = v_lane1 + st;
     // keep derived addresses out of loop-invariant code
@@ -594,13 +607,27 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     asm volatile("" : "+v"(s[0]), "+v"(s[1]));
 #pragma unroll
     for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(acc_o[db]));
+    if constexpr (!F8 && MASKABLE) {
+      if (pk_masked) {
+        constexpr int one = DT == kBF16 ? 0x3F803F80 : 0x3C003C00;
+        const i32x4 ones = {one, one, one, one};
+#pragma unroll
+        for (int jc = 0; jc < 4; ++jc) {
+          const i32x4 bp = {(int)pk[jc >> 1][4 * (jc & 1)], (int)pk[jc >> 1][4 * (jc & 1) + 1],
+                            (int)pk[jc >> 1][4 * (jc & 1) + 2], (int)pk[jc >> 1][4 * (jc & 1) + 3]};
+          acc_l = T::mma(ones, bp, acc_l);
+        }
+      }
+    }
     pin_l();
   };
 
   // softmax phase of tile t: mask, running max, lazy rescale, probabilities; hook(j), j <
-  // LPP, issues this wave's loads of the phase, spread over the exponentials
-  auto softmax_phase = [&](int t, auto& hook) __attribute__((always_inline)) {
-    if (t >= w_full) {  // some key of the tile is hidden from some row of the wave
+  // LPP, issues this wave's loads of the phase, spread over the exponentials.  Not MASKABLE
+  // (plain steps): every row of every wave sees the whole tile.
+  auto softmax_phase = [&](int t, auto& hook, auto maskable_tag) __attribute__((always_inline)) {
+    constexpr bool MASKABLE = decltype(maskable_tag)::value;
+    if (MASKABLE && t >= w_full) {  // some key of the tile is hidden from some row of the wave
       // score (jb, r) belongs to key t kBN + 4 h32 + 32 jb + 8 (r / 4) + r % 4
       const int lim = vis_last - t * kBN;
 #pragma unroll
@@ -619,7 +646,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     if (__any(m_cand > m_run + (F8 ? kF8Threshold : kRescaleThreshold))) {
       const float m_new = __builtin_fmaxf(m_run, m_cand);
       const float alpha = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      if constexpr (F8) acc_l[0] *= alpha;  // (the only element read)
+      acc_l[0] *= alpha;  // (the only element read)
       if constexpr (VSUM) {
         l_run *= alpha;
         l_run2 *= alpha;
@@ -629,11 +656,10 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       m_run = m_new;
     }
     const float m_use = (m_run == -__builtin_inff() ? 0.0f : m_run) - (F8 ? kF8Shift : 0.0f);
-    // exponentials, packing and (VALU) row sums.  16-bit ROUNDED: sum the 16-bit values the
-    // matrix cores see, else the fp32 ones (see the row-sum note at the top of this file);
-    // fp8 with an LSE: the fp32 ones.
-    auto exps = [&](auto rounded_tag) __attribute__((always_inline)) {
-      constexpr bool ROUNDED = decltype(rounded_tag)::value;
+    // exponentials, packing and VALU row sums (fp32; none for a masked 16-bit tile, which the
+    // matrix cores sum; fp8: only for an LSE)
+    auto exps = [&](auto masked_tag) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
@@ -647,10 +673,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
             pk[jb][2 * qd] = T::pack(e[0], e[1]);
             pk[jb][2 * qd + 1] = T::pack(e[2], e[3]);
           }
-          if constexpr (!F8 && ROUNDED) {
-            l_run += T::lo(pk[jb][2 * qd]) + T::lo(pk[jb][2 * qd + 1]);
-            l_run2 += T::hi(pk[jb][2 * qd]) + T::hi(pk[jb][2 * qd + 1]);
-          } else if constexpr (VSUM) {
+          if constexpr (VSUM && !(!F8 && MASKED)) {
             l_run += e[0] + e[2];
             l_run2 += e[1] + e[3];
           }
@@ -661,11 +684,15 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     };
     if constexpr (F8) {
       exps(std::false_type{});
-    } else {
-      if (t >= w_full)
+    } else if constexpr (MASKABLE) {
+      pk_masked = __builtin_amdgcn_readfirstlane(t >= w_full);
+      if (pk_masked)
         exps(std::true_type{});
       else
         exps(std::false_type{});
+    } else {
+      pk_masked = false;
+      exps(std::false_type{});
     }
     if constexpr (F8) {
       // Regroup to 8 consecutive keys per lane and 16-key chunk (the fp8 PV operand order):
@@ -691,9 +718,9 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
 
   // The matrix work runs at raised wave priority so the SIMD issues its MFMAs ahead of the
   // softmax VALU work of the other group's wave.
-  auto matrix_prio = [&](uint32_t st, auto& hook) __attribute__((always_inline)) {
+  auto matrix_prio = [&](uint32_t st, auto& hook, auto maskable_tag) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
-    matrix_phase(st, hook);
+    matrix_phase(st, hook, maskable_tag);
     __builtin_amdgcn_s_setprio(0);
   };
   // The loads of phase ph request part ph % 2 of L(ph / 2 + 2).  At the end of an odd phase
@@ -717,7 +744,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // (and one LSE store where due) and clears the item state.
   constexpr int NST = 2 * NDB;
   auto epilogue = [&]() __attribute__((always_inline)) {
-    const float l_tot = F8 ? acc_l[0] : wave_row_sum(l_run + l_run2);
+    const float l_tot = F8 ? acc_l[0] : acc_l[0] + wave_row_sum(l_run + l_run2);
     const float inv = l_tot > 0.0f ? p.o_scale / l_tot : 0.0f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -760,7 +787,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
-    if constexpr (F8) acc_l = f32x16{};
+    acc_l = f32x16{};
     l_run = 0.0f;
     l_run2 = 0.0f;
     m_run = -__builtin_inff();
@@ -789,7 +816,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // is read from LDS at the end of softmax(u-1) (its rows were requested at least one step
   // earlier, so at least NBLK / 8 newer requests stand behind them there).
   // compute cursor: item, tile inside it, its tiles, LDS address of stage u % 3
-  int k = 0, t = 0, nt = item_tiles(0);
+  int k = 0, t = 0, nt = item_tiles(0), nfull = item_full(0);
   uint32_t c_st = lds0;
   auto next_tile = [&]() __attribute__((always_inline)) {
     c_st += STAGE;
@@ -798,17 +825,20 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       ++k;
       t = 0;
       nt = item_tiles(k);
+      nfull = item_full(k);
     }
   };
-  // Steps come in two builds.  A plain step neither starts nor ends an item, and neither of
-  // its requests moves the cursor into the next item: it runs without any of that control
-  // code (in the softmax phase every extra instruction costs issue time).  The others, the
-  // first tile of an item after the first and the last three tiles of an item before the
-  // last, are special steps with the full bookkeeping.  plain_end() is the end of the run of
-  // plain steps that starts at step u (u itself when step u is special).
+  // Steps come in two builds.  A plain step neither starts nor ends an item, neither of its
+  // requests moves the cursor into the next item, and every row of the item sees its whole
+  // tile: it runs without any of that control and mask code (in the softmax phase every
+  // extra instruction costs issue time).  The others (the first tile of an item after the
+  // first, the last three tiles of an item before the last, and tiles from item_full on) are
+  // special steps with the full bookkeeping.  plain_end() is the end of the run of plain
+  // steps that starts at step u (u itself when step u is special).
   auto plain_end = [&](int u) __attribute__((always_inline)) {
     if ((t == 0) & (k > 0)) return u;
-    const int lim = k + 1 == n_items ? n_stream : u - t + nt - 3;
+    int lim = k + 1 == n_items ? n_stream : u - t + nt - 3;
+    lim = min(lim, u - t + nfull);
     return lim > u ? lim : u;
   };
   auto plain_advance = [&]() __attribute__((always_inline)) {
@@ -828,14 +858,14 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   if (group == 0) {
     auto step = [&](auto special_tag) __attribute__((always_inline)) {
       constexpr bool SPECIAL = decltype(special_tag)::value;
-      matrix_prio(c_st, h0);
+      matrix_prio(c_st, h0, special_tag);
       even_end();
       const bool first = SPECIAL && (t == 0) & (k > 0);
       if (first) {
         epilogue();
         set_rows(k);
       }
-      softmax_phase(t, h1);
+      softmax_phase(t, h1, special_tag);
       // At the end of the phase L(u+1) must have landed.  The newest requests are this step's
       // NBLK / 8 for L(u+2), and after an epilogue also its NST stores of O.
       if (first)
@@ -862,7 +892,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
         ++u;
       }
     }
-    matrix_prio(c_st, h0);  // O += V P of the last tile
+    matrix_prio(c_st, h0, std::true_type{});  // O += V P of the last tile
     even_end();
     no_work(P1{});
     odd_end();
@@ -871,7 +901,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     even_end();
     auto step = [&](auto special_tag) __attribute__((always_inline)) {
       constexpr bool SPECIAL = decltype(special_tag)::value;
-      matrix_prio(c_st, h1);
+      matrix_prio(c_st, h1, special_tag);
       odd_end();
       if constexpr (SPECIAL) {
         advance();
@@ -883,7 +913,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       } else {
         plain_advance();
       }
-      softmax_phase(t, h0);
+      softmax_phase(t, h0, special_tag);
       if (SPECIAL && (t == nt - 1) & (k + 1 < n_items)) {
         // item k+1's rows were requested at the start of this phase (a one-tile item k > 0:
         // only this phase's LPP loads are newer) or at least one step earlier
@@ -906,7 +936,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
         ++u;
       }
     }
-    matrix_prio(c_st, h1);
+    matrix_prio(c_st, h1, std::true_type{});
     odd_end();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the requests past the end (they write LDS)
