@@ -17,10 +17,13 @@
  * README, "FMHA for Blackwell: Forward").
  *
  * Ownership: every pointer is device memory owned by the caller.  The library
- * allocates nothing, keeps no pointer after a call returns and holds no mutable
- * global state, so calls from several host threads are safe.  Work is enqueued on
- * `stream` and runs asynchronously; errors inside the kernel surface at the
- * caller's next synchronisation.
+ * allocates nothing and keeps no pointer after a call returns.  Its only global
+ * state is a per-device cache of the compute-unit count (written once, atomically,
+ * with the value the runtime reports; it sizes the grid), so calls from several
+ * host threads are safe.  Work is enqueued on `stream` and runs asynchronously;
+ * errors inside the kernel surface at the caller's next synchronisation.  The grid
+ * is sized from the current device's (hipGetDevice) compute-unit count; results do
+ * not depend on it.
  */
 #ifndef FMHA_H_
 #define FMHA_H_
