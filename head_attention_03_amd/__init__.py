@@ -11,6 +11,8 @@ from ._lib import (  # noqa: F401
     FmhaError,
     check,
     fmha_fwd,
+    fmha_fwd_splitkv,
+    fmha_fwd_splitkv_workspace_size,
     fmha_status_string,
     fmha_varlen,
     fmha_version,

@@ -1,0 +1,528 @@
+// Split-KV attention forward for few query rows per head (generation / decode) on gfx950.
+//
+// The same O = softmax(scale * Q K^T + mask) V and LSE as fmha_fwd, for shapes where every
+// head has only a few query rows and a long key range: the keys of each (sequence, K/V head)
+// are cut into splits that run on different workgroups, each writing a partial result
+// (O_s normalised, LSE_s) to a caller-provided workspace, and a second kernel merges the
+// splits, O = sum_s exp(LSE_s - LSE) O_s with LSE = log sum_s exp(LSE_s).  This is the
+// generation kernel with its split-KV reduction that the trdm.cn walk-through "CUTLASS
+// Blackwell FMHA 示例完全解析" describes (sections on the generation kernel and the
+// reduction), with the query heads of a GQA group packed into the rows of one MFMA tile, as
+// the CUTLASS examples/77_blackwell_fmha README does for generation ("FMHA for Blackwell:
+// Generation").
+//
+// CDNA4 design:
+// * The work is bound by HBM bandwidth (each K/V byte meets only the few query rows of its
+//   group), so the kernel is built to keep loads in flight rather than to share K/V tiles:
+//   a workgroup has 2 waves, and each wave streams every other 32-key tile of the split
+//   through a private ring of 4 LDS stages (LDS-direct loads, three tiles in flight, no
+//   barrier inside the loop).  The two waves' online-softmax states are merged in LDS at
+//   the end.
+// * A workgroup covers 32 packed query rows (row r: head kv_h * group + r / Sq, query r % Sq)
+//   of one (sequence, K/V head).  S^T = K Q^T and O^T += V^T P^T run on the same
+//   v_mfma_f32_32x32x16 operand layouts as fmha_fwd (K and V rows XOR-swizzled in LDS, V^T
+//   from ds_read_b64_tr_b16); rows past the group are zero and their output is dropped.
+// * Masks, varlen and GQA follow fmha_fwd: per-row last visible key, buffer descriptors
+//   bounded to the sequence (rows past either end read 0), and the causal alignment offset
+//   Sk_b - Sq_b for causal-qend.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include <type_traits>
+
+#include "fmha.h"
+#include "fmha_device.h"
+
+namespace fmha {
+namespace skv {
+
+constexpr int kWaves = 2;       // waves per workgroup, each streaming its own K/V tiles
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTN = 32;         // keys per tile: one 32-key block of the MFMA
+constexpr int kStages = 4;      // tiles in a wave's LDS ring (three in flight)
+constexpr int kRows = 32;       // packed query rows per workgroup (the MFMA N dimension)
+constexpr int kMinChunk = 256;  // fewest keys per split
+constexpr int kTargetWgs = 512; // split until about this many workgroups (two per compute unit)
+
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o_part;    // workspace: [n_splits][rows][D], each split's O normalised by its own sum
+  float* lse_part;  // workspace: [n_splits][rows], natural log (-inf: the split saw no key)
+  const int32_t* cu_q;  // null for dense batches
+  const int32_t* cu_k;
+  int32_t Sq, H, H_kv, group;  // Sq: query rows per sequence (packed: maximum)
+  int32_t Sk;                  // dense: keys per sequence
+  int32_t M;                   // packed rows per K/V head: group * Sq
+  int32_t mblks;               // ceil(M / kRows)
+  int32_t n_splits, chunk;     // splits per (sequence, K/V head) and keys per split
+  int32_t rows;                // rows of the partial arrays: query rows * H
+  int32_t causal, qend;
+  float scale_log2;            // scale * log2(e)
+};
+
+struct MergeParams {
+  const float* o_part;
+  const float* lse_part;
+  void* o;
+  float* lse;
+  int32_t rows, n_splits, H, Sq, total_q;  // total_q > 0: packed LSE layout [H, total_q]
+  float o_scale;
+};
+
+// split kernel: grid = B * H_kv * mblks * n_splits workgroups of kThreads
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
+  constexpr int E = 2;
+  constexpr int RB = D * E;          // bytes per K/V/Q row
+  constexpr int CPR = RB / 16;       // 16-byte chunks per row
+  constexpr int TILE = kTN * RB;     // bytes per K or V tile
+  constexpr int TBLK = TILE / 1024;  // 1 KiB LDS-direct loads per K or V tile
+  constexpr int NLD = 2 * TBLK;      // loads per tile
+  constexpr int STAGE = 2 * TILE;    // K tile, then V tile
+  constexpr int QB = kRows * RB;     // a wave's copy of the query rows
+  constexpr int QBLK = QB / 1024;
+  constexpr int KS = D / 16;         // MFMA k-steps over the head dimension
+  constexpr int NDB = D / 32;        // 32-wide blocks of the head dimension in O
+  static_assert(TILE % 1024 == 0 && QB % 1024 == 0, "whole 1 KiB loads");
+  static_assert(3 * NLD < 64, "vmcnt range");
+  typedef Elem<DT> T;
+
+  // LDS: per wave a ring of kStages {K, V} stages, then per wave a copy of the Q rows
+  __shared__ __attribute__((aligned(1024))) char lds[kWaves * (kStages * STAGE + QB)];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
+
+  const int lane = threadIdx.x & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int l32 = lane & 31;
+  const int h32 = lane >> 5;
+
+  // ---- work unit: (sequence, K/V head, row block, split) ------------------------------
+  int x = blockIdx.x;
+  const int split = x % p.n_splits;
+  x /= p.n_splits;
+  const int mblk = x % p.mblks;
+  x /= p.mblks;
+  const int kvh = x % p.H_kv;
+  const int b = x / p.H_kv;
+  int q_row0, Sq_b, k_row0, Sk_b;
+  if (p.cu_q) {
+    q_row0 = p.cu_q[b];
+    Sq_b = p.cu_q[b + 1] - q_row0;
+    k_row0 = p.cu_k[b];
+    Sk_b = p.cu_k[b + 1] - k_row0;
+  } else {
+    q_row0 = b * p.Sq;
+    Sq_b = p.Sq;
+    k_row0 = b * p.Sk;
+    Sk_b = p.Sk;
+  }
+  const int off = p.qend ? Sk_b - Sq_b : 0;
+
+  // this lane's packed row: head hq, query qi of the sequence; the keys it sees are [0, vis_end)
+  const int r = mblk * kRows + l32;
+  const int hq = kvh * p.group + r / p.Sq;
+  const int qi = r % p.Sq;
+  const bool row_ok = r < p.M && qi < Sq_b;
+  const int vis_end = row_ok ? (p.causal ? min(Sk_b, qi + off + 1) : Sk_b) : 0;
+  // keys of this split that some row sees, and the first key that some row does not see
+  int wg_end = vis_end, wg_min = row_ok ? vis_end : 0x7fffffff;
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) {
+    wg_end = max(wg_end, __shfl_xor(wg_end, o));
+    wg_min = min(wg_min, __shfl_xor(wg_min, o));
+  }
+  const int k0 = split * p.chunk;
+  const int k1 = min(min(Sk_b, k0 + p.chunk), __builtin_amdgcn_readfirstlane(wg_end));
+  const int n_tiles = k1 > k0 ? (k1 - k0 + kTN - 1) / kTN : 0;
+  const int n_w = n_tiles > wave_u ? (n_tiles - wave_u + kWaves - 1) / kWaves : 0;  // this wave's tiles
+  // tiles from here on need the mask (some row does not see all their keys, or they run past k1)
+  const int mask_from = min(__builtin_amdgcn_readfirstlane(wg_min), k1);
+  const int lim_row = min(vis_end, k1) - 1 - 4 * h32;  // last key this lane keeps, less its key offset
+
+  // ---- descriptors: bounded to the rows of this sequence ------------------------------
+  const uint32_t qstride = (uint32_t)p.H * D * E;
+  const uint32_t kstride = (uint32_t)p.H_kv * D * E;
+  const size_t q_base = (size_t)q_row0 * p.H * D * E;
+  const size_t k_base = ((size_t)k_row0 * p.H_kv + kvh) * D * E;
+  const uint32_t q_bytes = Sq_b > 0 ? (uint32_t)Sq_b * qstride : 0;
+  const uint32_t k_bytes = Sk_b > 0 ? (uint32_t)(Sk_b - 1) * kstride + RB : 0;
+  const i32x4 rq = make_rsrc_words((const char*)p.q + q_base, q_bytes);
+  const i32x4 rk = make_rsrc_words((const char*)p.k + k_base, k_bytes);
+  const i32x4 rv = make_rsrc_words((const char*)p.v + k_base, k_bytes);
+
+  const uint32_t ring = lds0 + (uint32_t)(wave_u * kStages * STAGE);
+  const uint32_t q_lds = lds0 + (uint32_t)(kWaves * kStages * STAGE + wave_u * QB);
+
+  // ---- Q rows into this wave's LDS copy (swizzled like a K tile), then the B operand ----
+#pragma unroll
+  for (int i = 0; i < QBLK; ++i) {
+    const int pos = 64 * i + lane;  // 16-byte chunk of the 32 x D block
+    const int j = pos / CPR;        // packed row
+    const int rj = mblk * kRows + j;
+    const int hj = kvh * p.group + rj / p.Sq, qj = rj % p.Sq;
+    // rows past the group, or past the sequence, fall outside the descriptor and read 0
+    const uint32_t src = rj < p.M ? (uint32_t)qj * qstride + (uint32_t)hj * RB + (((pos % CPR) ^ swz<CPR>(j)) * 16)
+                                  : q_bytes;
+    lds_load16(rq, src, q_lds + 1024 * i);
+  }
+
+  // per-lane LDS offsets: K row l32, chunk h32 of each k-step; V^T transpose read (as fmha_fwd)
+  const int k_lane = l32 * RB + ((h32 ^ swz<CPR>(l32)) * 16);
+  const int g16 = (lane >> 4) & 1;
+  const int s16 = lane & 15;
+  const int v_row0 = 4 * h32 + (s16 >> 2);
+  const int v_part = 2 * g16 + ((s16 & 3) >> 1);
+  const int v_lane0 = TILE + v_row0 * RB + ((v_part ^ swz<CPR>(v_row0)) * 16) + 8 * (s16 & 1);
+  const int v_lane1 = TILE + (v_row0 + 8) * RB + ((v_part ^ swz<CPR>(v_row0 + 8)) * 16) + 8 * (s16 & 1);
+
+  // loads of this wave's tile n (keys k0 + (wave + n kWaves) kTN ..) into stage n % kStages
+  uint32_t ld_off[TBLK];
+#pragma unroll
+  for (int i = 0; i < TBLK; ++i) {
+    const int pos = 64 * i + lane;
+    const int j = pos / CPR;
+    ld_off[i] = (uint32_t)j * kstride + (((pos % CPR) ^ swz<CPR>(j)) * 16);
+  }
+  auto load_tile = [&](int n) __attribute__((always_inline)) {
+    const uint32_t key0 = (uint32_t)(k0 + (wave_u + n * kWaves) * kTN) * kstride;
+    const uint32_t st = ring + (uint32_t)((n % kStages) * STAGE);
+#pragma unroll
+    for (int i = 0; i < TBLK; ++i) lds_load16(rk, key0 + ld_off[i], st + 1024 * i);
+#pragma unroll
+    for (int i = 0; i < TBLK; ++i) lds_load16(rv, key0 + ld_off[i], st + TILE + 1024 * i);
+  };
+#pragma unroll
+  for (int n = 0; n < kStages - 1; ++n)
+    if (n < n_w) load_tile(n);
+
+  // Q landed (it is older than every tile load): read the B operand, dims 16 ks + 8 h32 ..
+  if (n_w >= 3)
+    wait_vmcnt<3 * NLD>();
+  else if (n_w == 2)
+    wait_vmcnt<2 * NLD>();
+  else if (n_w == 1)
+    wait_vmcnt<NLD>();
+  else
+    wait_vmcnt<0>();
+  i32x4 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const lds_i32x4*)(uintptr_t)((q_lds + k_lane) ^ (32 * ks));
+
+  f32x16 acc_o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
+  float m_run = -__builtin_inff();  // running max of scale*log2(e)*s for row l32
+  float l_run = 0.0f;               // this lane's part of the row sum
+  const float sl2 = p.scale_log2;
+
+  for (int n = 0; n < n_w; ++n) {
+    // tile n must have landed; the tiles requested after it may still be in flight
+    if (n + 2 < n_w)
+      wait_vmcnt<2 * NLD>();
+    else if (n + 1 < n_w)
+      wait_vmcnt<NLD>();
+    else
+      wait_vmcnt<0>();
+    const uint32_t st = ring + (uint32_t)((n % kStages) * STAGE);
+    const int kb = k0 + (wave_u + n * kWaves) * kTN;  // first key of the tile
+
+    // S^T = K Q^T: score r of this lane is key kb + 4 h32 + 8 (r / 4) + r % 4, row l32
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const i32x4 a = *(const lds_i32x4*)(uintptr_t)((st + k_lane) ^ (32 * ks));
+      s = T::mma(a, qf[ks], s);
+    }
+    if (kb + kTN > mask_from) {
+      const int lim = lim_row - kb;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 8 * (e >> 2) + (e & 3) <= lim ? s[e] : -__builtin_inff();
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = __builtin_fmaxf(mx, s[e]);
+    mx = wave_row_max(mx);
+    const float m_cand = mx * sl2;
+    if (__any(m_cand > m_run + kRescaleThreshold)) {
+      const float m_new = __builtin_fmaxf(m_run, m_cand);
+      const float alpha = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
+    uint32_t pk[8];
+    float l2 = 0.0f;
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      float e4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) e4[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * qd + u], sl2, -m_use));
+      pk[2 * qd] = T::pack(e4[0], e4[1]);
+      pk[2 * qd + 1] = T::pack(e4[2], e4[3]);
+      // the row sum takes the rounded probabilities the matrix cores multiply
+      l_run += T::lo(pk[2 * qd]) + T::hi(pk[2 * qd]);
+      l2 += T::lo(pk[2 * qd + 1]) + T::hi(pk[2 * qd + 1]);
+    }
+    l_run += l2;
+
+    // O^T += V^T P^T: 16-key chunk c, d-block db
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const i32x4 bp = {(int)pk[4 * c], (int)pk[4 * c + 1], (int)pk[4 * c + 2], (int)pk[4 * c + 3]};
+      const uint32_t rows = (uint32_t)(16 * c * RB);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const i16x4 v0 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(((st + v_lane0) ^ (64 * db)) + rows));
+        const i16x4 v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(((st + v_lane1) ^ (64 * db)) + rows));
+        const i32x4 a = {__builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 0, 1)),
+                         __builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 2, 3)),
+                         __builtin_bit_cast(int, __builtin_shufflevector(v1, v1, 0, 1)),
+                         __builtin_bit_cast(int, __builtin_shufflevector(v1, v1, 2, 3))};
+        acc_o[db] = T::mma(a, bp, acc_o[db]);
+      }
+    }
+    // stage (n - 1) % kStages was read in the previous iteration: refill it with tile n + 3
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (n + kStages - 1 < n_w) load_tile(n + kStages - 1);
+  }
+
+  // ---- merge the waves' states in LDS (the rings are free now), then write the partial --
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const float l_tot = wave_row_sum(l_run);
+  __syncthreads();
+  float* xm = (float*)lds;                  // [kWaves][64] running maxima
+  float* xl = xm + kWaves * 64;             // [kWaves][64] row sums
+  float* xo = xl + kWaves * 64;             // [kWaves][NDB * 16][64] accumulators, lane-major
+  xm[wave_u * 64 + lane] = m_run;
+  xl[wave_u * 64 + lane] = l_tot;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xo[(wave_u * NDB * 16 + db * 16 + e) * 64 + lane] = acc_o[db][e];
+  __syncthreads();
+  if (wave_u != 0) return;
+  float m_all = xm[lane];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) m_all = __builtin_fmaxf(m_all, xm[w * 64 + lane]);
+  float l_all = 0.0f;
+  f32x16 o_all[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o_all[db] = f32x16{};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float mw = xm[w * 64 + lane];
+    const float a = mw == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mw - m_all);
+    l_all += a * xl[w * 64 + lane];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o_all[db][e] += a * xo[(w * NDB * 16 + db * 16 + e) * 64 + lane];
+  }
+  if (!row_ok) return;
+  const size_t row = (size_t)(q_row0 + qi) * p.H + hq;
+  const size_t part = (size_t)split * p.rows + row;
+  const float inv = l_all > 0.0f ? 1.0f / l_all : 0.0f;
+  float* op = p.o_part + part * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {  // dims 32 db + 8 g + 4 h32 + 0..3
+      const float4 w = {o_all[db][4 * g] * inv, o_all[db][4 * g + 1] * inv, o_all[db][4 * g + 2] * inv,
+                        o_all[db][4 * g + 3] * inv};
+      *(float4*)(op + 32 * db + 8 * g + 4 * h32) = w;
+    }
+  if (h32 == 0)
+    p.lse_part[part] = l_all > 0.0f ? (m_all + __builtin_amdgcn_logf(l_all)) * 0.69314718055994531f : -__builtin_inff();
+}
+
+// merge kernel: D / 4 threads per row, each 4 consecutive dims
+template <int DT, int D>
+__global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
+  constexpr int TPR = D / 4;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int row = t / TPR;
+  const int part = t % TPR;
+  if (row >= p.rows) return;
+  float mx = -__builtin_inff();
+  for (int s = 0; s < p.n_splits; ++s) mx = __builtin_fmaxf(mx, p.lse_part[(size_t)s * p.rows + row]);
+  float wsum = 0.0f;
+  float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (mx != -__builtin_inff()) {
+    for (int s = 0; s < p.n_splits; ++s) {
+      const float ls = p.lse_part[(size_t)s * p.rows + row];
+      if (ls == -__builtin_inff()) continue;  // a split that saw no key of this row
+      const float w = __expf(ls - mx);
+      const float4 os = *(const float4*)(p.o_part + ((size_t)s * p.rows + row) * D + 4 * part);
+      wsum += w;
+      acc.x += w * os.x;
+      acc.y += w * os.y;
+      acc.z += w * os.z;
+      acc.w += w * os.w;
+    }
+  }
+  const float f = wsum > 0.0f ? p.o_scale / wsum : 0.0f;
+  typedef Elem<DT> T;
+  const uint32_t lo = T::pack(acc.x * f, acc.y * f), hi = T::pack(acc.z * f, acc.w * f);
+  *(i32x2*)((char*)p.o + ((size_t)row * D + 4 * part) * 2) = i32x2{(int)lo, (int)hi};
+  if (p.lse && part == 0) {
+    const int q = row / p.H, h = row - q * p.H;  // row = (query row) * H + head
+    const size_t idx = p.total_q > 0 ? (size_t)h * p.total_q + q : ((size_t)(q / p.Sq) * p.H + h) * p.Sq + q % p.Sq;
+    p.lse[idx] = wsum > 0.0f ? mx + __logf(wsum) : -__builtin_inff();
+  }
+}
+
+// Splits per (sequence, K/V head) and keys per split: split until about kTargetWgs
+// workgroups, but never below kMinChunk keys per split; chunks are whole wave-tile rounds.
+inline void plan(int64_t units, int64_t Sk, int32_t* n_splits, int32_t* chunk) {
+  int64_t n = units > 0 ? (kTargetWgs + units - 1) / units : 1;
+  const int64_t n_max = Sk > kMinChunk ? (Sk + kMinChunk - 1) / kMinChunk : 1;
+  n = n < 1 ? 1 : n > n_max ? n_max : n;
+  constexpr int64_t round = kWaves * kTN;
+  int64_t c = Sk > 0 ? (Sk + n - 1) / n : round;
+  c = (c + round - 1) / round * round;
+  *chunk = (int32_t)c;
+  *n_splits = (int32_t)(Sk > 0 ? (Sk + c - 1) / c : 1);
+}
+
+template <int DT, int D>
+hipError_t launch(const Params& p, const MergeParams& mp, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((split_kernel<DT, D>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t threads = (int64_t)mp.rows * (D / 4);
+  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, mp);
+  return hipGetLastError();
+}
+
+}  // namespace skv
+}  // namespace fmha
+
+// --------------------------------------------------------------------------------------
+// C ABI
+// --------------------------------------------------------------------------------------
+namespace {
+
+// The shape checks fmha_fwd makes, and the split plan.  Returns FMHA_OK with the plan filled.
+fmha_status splitkv_plan(const void* q, const void* k, const void* v, const void* o, const float* lse, int32_t B,
+                         int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D, fmha_mask mask, fmha_dtype dtype,
+                         const fmha_varlen* varlen, fmha::skv::Params* p, int64_t* grid, size_t* ws_bytes) {
+  using namespace fmha::skv;
+  const bool packed = varlen != nullptr;
+  if (B < 0 || Sq < 0 || Sk < 0 || H < 0 || H_kv < 0) return FMHA_ERR_INVALID_SHAPE;
+  if (H > 0 && (H_kv < 1 || H % H_kv != 0)) return FMHA_ERR_INVALID_SHAPE;
+  if (D != 32 && D != 64 && D != 128) return FMHA_ERR_INVALID_SHAPE;
+  if (packed && (varlen->total_length_q < 0 || varlen->total_length_k < 0)) return FMHA_ERR_INVALID_SHAPE;
+  if ((int)dtype < 0 || (int)dtype > 2) return FMHA_ERR_UNSUPPORTED;
+  if ((int)mask < 0 || (int)mask > 3) return FMHA_ERR_UNSUPPORTED;
+  if (dtype == FMHA_DTYPE_F8E4M3) return FMHA_ERR_UNSUPPORTED;  // 16-bit types only
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FMHA_ERR_MISALIGNED;
+  if ((uintptr_t)lse & 3) return FMHA_ERR_MISALIGNED;
+  const int64_t rows_q = packed ? varlen->total_length_q : Sq;
+  const int64_t rows_k = packed ? varlen->total_length_k : Sk;
+  const int64_t lim = (int64_t)1 << 31;
+  // per-sequence byte offsets (tiles run up to one wave-tile round past a split) fit 31 bits
+  if (rows_q * H * D * 2 >= lim || (rows_k + kWaves * kTN * kStages) * H_kv * D * 2 >= lim)
+    return FMHA_ERR_UNSUPPORTED;
+  const int64_t q_rows = packed ? (int64_t)varlen->total_length_q : (int64_t)B * Sq;
+  const int64_t group = H > 0 ? H / H_kv : 1;
+  const int64_t M = group * Sq;
+  const int64_t mblks = (M + kRows - 1) / kRows;
+  int32_t n_splits = 1, chunk = kWaves * kTN;
+  plan((int64_t)B * H_kv * mblks, Sk, &n_splits, &chunk);
+  const int64_t rows = q_rows * H;
+  if (rows >= lim || (int64_t)n_splits * rows * D >= lim * 2) return FMHA_ERR_UNSUPPORTED;
+  *grid = (int64_t)B * H_kv * mblks * n_splits;
+  if (*grid >= lim) return FMHA_ERR_UNSUPPORTED;
+  *ws_bytes = (size_t)n_splits * (size_t)rows * (size_t)(D + 1) * sizeof(float);
+  p->Sq = Sq;
+  p->Sk = Sk;
+  p->H = H;
+  p->H_kv = H_kv;
+  p->group = (int32_t)group;
+  p->M = (int32_t)M;
+  p->mblks = (int32_t)mblks;
+  p->n_splits = n_splits;
+  p->chunk = chunk;
+  p->rows = (int32_t)rows;
+  p->causal = mask == FMHA_MASK_CAUSAL_QBEGIN || mask == FMHA_MASK_CAUSAL_QEND;
+  p->qend = mask == FMHA_MASK_CAUSAL_QEND;
+  return FMHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
+                                       const fmha_varlen* varlen) {
+  fmha::skv::Params p;
+  int64_t grid = 0;
+  size_t bytes = 0;
+  const fmha_status st = splitkv_plan(nullptr, nullptr, nullptr, nullptr, nullptr, B, Sq, Sk, H, H_kv, D,
+                                      FMHA_MASK_NONE, FMHA_DTYPE_BF16, varlen, &p, &grid, &bytes);
+  return st == FMHA_OK ? bytes : 0;
+}
+
+fmha_status fmha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Sq,
+                             int32_t Sk, int32_t H, int32_t H_kv, int32_t D, float scale, fmha_mask mask,
+                             fmha_dtype dtype, float o_scale, const fmha_varlen* varlen, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  using namespace fmha::skv;
+  const bool packed = varlen != nullptr;
+  const bool no_keys = packed ? varlen->total_length_k == 0 : Sk == 0;  // k and v may then be NULL
+  if (!q || !o || (!no_keys && (!k || !v))) return FMHA_ERR_NULL_POINTER;
+  if (packed && (!varlen->cu_seqlens_q != !varlen->cu_seqlens_k)) return FMHA_ERR_NULL_POINTER;
+  if (packed && !varlen->cu_seqlens_q) return FMHA_ERR_NULL_POINTER;
+  Params p;
+  int64_t grid = 0;
+  size_t need = 0;
+  const fmha_status st = splitkv_plan(q, k, v, o, lse, B, Sq, Sk, H, H_kv, D, mask, dtype, varlen, &p, &grid, &need);
+  if (st != FMHA_OK) return st;
+  if (!(scale > 0.0f) || !isfinite(scale) || !isfinite(o_scale)) return FMHA_ERR_INVALID_ARGUMENT;
+  if (B == 0 || H == 0 || Sq == 0 || (packed && varlen->total_length_q == 0)) return FMHA_OK;
+  if (!workspace) return FMHA_ERR_NULL_POINTER;
+  if ((uintptr_t)workspace & 15) return FMHA_ERR_MISALIGNED;
+  if (workspace_bytes < need) return FMHA_ERR_INVALID_ARGUMENT;
+
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o_part = (float*)workspace;
+  p.lse_part = p.o_part + (size_t)p.n_splits * p.rows * D;
+  p.cu_q = packed ? varlen->cu_seqlens_q : nullptr;
+  p.cu_k = packed ? varlen->cu_seqlens_k : nullptr;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  MergeParams mp;
+  mp.o_part = p.o_part;
+  mp.lse_part = p.lse_part;
+  mp.o = o;
+  mp.lse = lse;
+  mp.rows = p.rows;
+  mp.n_splits = p.n_splits;
+  mp.H = H;
+  mp.Sq = Sq;
+  mp.total_q = packed ? varlen->total_length_q : 0;
+  mp.o_scale = o_scale;
+
+  hipError_t err = hipSuccess;
+  if (dtype == FMHA_DTYPE_BF16) {
+    if (D == 32) err = fmha::skv::launch<fmha::kBF16, 32>(p, mp, (int)grid, stream);
+    if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64>(p, mp, (int)grid, stream);
+    if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128>(p, mp, (int)grid, stream);
+  } else {
+    if (D == 32) err = fmha::skv::launch<fmha::kF16, 32>(p, mp, (int)grid, stream);
+    if (D == 64) err = fmha::skv::launch<fmha::kF16, 64>(p, mp, (int)grid, stream);
+    if (D == 128) err = fmha::skv::launch<fmha::kF16, 128>(p, mp, (int)grid, stream);
+  }
+  return err == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
+}
+
+}  // extern "C"

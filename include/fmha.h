@@ -28,6 +28,7 @@
 #ifndef FMHA_H_
 #define FMHA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -118,6 +119,42 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
                      int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
                      float scale, fmha_mask mask, fmha_dtype dtype, float o_scale,
                      const fmha_varlen* varlen, hipStream_t stream);
+
+/*
+ * fmha_fwd_splitkv -- the same attention forward pass as fmha_fwd (same arguments, masks,
+ * layouts, LSE and results up to rounding), built for generation / decode: few query rows
+ * per head (Sq small, e.g. 1 to 16 new tokens) against a long key range.  The keys of each
+ * (sequence, K/V head) are cut into splits that run on different workgroups; each writes
+ * its partial O (normalised by its own row sums, fp32) and partial LSE into `workspace`,
+ * and a second kernel merges them as O = sum_s exp(LSE_s - LSE) O_s, LSE = log sum_s
+ * exp(LSE_s) -- the split-KV reduction of the CUTLASS generation kernel (trdm.cn
+ * walk-through "CUTLASS Blackwell FMHA 示例完全解析", sections on the generation kernel and
+ * the reduction; examples/77_blackwell_fmha README, "FMHA for Blackwell: Generation").  The
+ * query heads of a GQA group share one K/V stream (they are packed into the rows of one
+ * matrix tile).  Correct for any Sq, but fmha_fwd is the faster choice once Sq * H / H_kv
+ * reaches a few hundred rows.
+ *
+ *   workspace        device memory owned by the caller, 16-byte aligned, at least
+ *                    fmha_fwd_splitkv_workspace_size(...) bytes for the same shape; its
+ *                    contents on entry do not matter and are overwritten (calls that
+ *                    overlap in time must not share it)
+ *   workspace_bytes  its size
+ *   dtype            FMHA_DTYPE_F16 or FMHA_DTYPE_BF16 (fp8: FMHA_ERR_UNSUPPORTED)
+ * Errors as fmha_fwd, and: workspace NULL -> FMHA_ERR_NULL_POINTER, not 16-byte aligned
+ * -> FMHA_ERR_MISALIGNED, smaller than needed -> FMHA_ERR_INVALID_ARGUMENT (checked only
+ * when there is work).
+ */
+fmha_status fmha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
+                             float scale, fmha_mask mask, fmha_dtype dtype, float o_scale,
+                             const fmha_varlen* varlen, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Workspace bytes fmha_fwd_splitkv needs for this shape (host arithmetic only: no device
+ * call; the packed form reads only varlen->total_length_q).  Returns 0 for an invalid
+ * shape, or a shape too large for the kernel's 32-bit offsets. */
+size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
+                                       const fmha_varlen* varlen);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fmha_status_string(fmha_status status);

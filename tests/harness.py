@@ -39,7 +39,23 @@ class GpuResult:
     status: int
 
 
-def run_dense(inp: DenseInputs, want_lse: bool = False, stream=None, o_init_bits: Optional[int] = None) -> GpuResult:
+def _workspace(need: int):
+    """Split-KV workspace, filled with NaN bit patterns: no result may depend on its contents."""
+    return torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device=torch.device("cuda:0"))
+
+
+def _entry(splitkv: bool, varlen, shape):
+    """The C entry point to call: fmha_fwd, or fmha_fwd_splitkv with a poisoned workspace."""
+    if not splitkv:
+        return lambda *a: fmha.fmha_fwd(*a)
+    need = fmha.fmha_fwd_splitkv_workspace_size(*shape, varlen)
+    assert need > 0, "shape rejected by the split-KV plan"
+    ws = _workspace(need)
+    return lambda *a: fmha.fmha_fwd_splitkv(*a[:-1], ws, need, a[-1])
+
+
+def run_dense(inp: DenseInputs, want_lse: bool = False, stream=None, o_init_bits: Optional[int] = None,
+              splitkv: bool = False) -> GpuResult:
     dev = torch.device("cuda:0")
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     if o_init_bits is None:
@@ -48,14 +64,14 @@ def run_dense(inp: DenseInputs, want_lse: bool = False, stream=None, o_init_bits
         raw = torch.full(q.shape, o_init_bits, dtype=torch.uint8 if ELEM_BYTES[inp.dtype] == 1 else torch.int16)
         o = raw.view(TORCH_DTYPES[inp.dtype]).to(dev)
     lse = torch.empty((inp.B, inp.H, inp.Sq), dtype=torch.float32, device=dev) if want_lse else None
-    st = fmha.fmha_fwd(q, k, v, o, lse, inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D, inp.kernel_scale, inp.mask,
-                       inp.dtype, inp.kernel_o_scale, None,
-                       stream if stream is not None else torch.cuda.current_stream())
+    call = _entry(splitkv, None, (inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D))
+    st = call(q, k, v, o, lse, inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D, inp.kernel_scale, inp.mask,
+              inp.dtype, inp.kernel_o_scale, None, stream if stream is not None else torch.cuda.current_stream())
     torch.cuda.synchronize()
     return GpuResult(o_bits=to_bits(o.cpu()), lse=lse.cpu().numpy() if want_lse else None, status=st)
 
 
-def run_varlen(inp: VarlenInputs, want_lse: bool = False, stream=None) -> GpuResult:
+def run_varlen(inp: VarlenInputs, want_lse: bool = False, stream=None, splitkv: bool = False) -> GpuResult:
     dev = torch.device("cuda:0")
     q_buf, k_buf, v_buf = inp.q_buf.to(dev), inp.k_buf.to(dev), inp.v_buf.to(dev)
     o_buf = inp.new_output_buffer().to(dev)
@@ -63,9 +79,10 @@ def run_varlen(inp: VarlenInputs, want_lse: bool = False, stream=None) -> GpuRes
     cu_k = torch.from_numpy(inp.cu_k).to(dev)
     lse = torch.empty((inp.H, max(inp.total_q, 1)), dtype=torch.float32, device=dev) if want_lse else None
     vl = fmha.make_varlen(cu_q, cu_k, inp.total_q, inp.total_k)
-    st = fmha.fmha_fwd(q_buf[inp.pad_q:], k_buf[inp.pad_k:], v_buf[inp.pad_k:], o_buf[inp.pad_q:], lse, inp.B,
-                       inp.max_q, inp.max_k, inp.H, inp.H_kv, inp.D, inp.kernel_scale, inp.mask, inp.dtype,
-                       inp.kernel_o_scale, vl, stream if stream is not None else torch.cuda.current_stream())
+    call = _entry(splitkv, vl, (inp.B, inp.max_q, inp.max_k, inp.H, inp.H_kv, inp.D))
+    st = call(q_buf[inp.pad_q:], k_buf[inp.pad_k:], v_buf[inp.pad_k:], o_buf[inp.pad_q:], lse, inp.B, inp.max_q,
+              inp.max_k, inp.H, inp.H_kv, inp.D, inp.kernel_scale, inp.mask, inp.dtype, inp.kernel_o_scale, vl,
+              stream if stream is not None else torch.cuda.current_stream())
     torch.cuda.synchronize()
     return GpuResult(o_bits=to_bits(o_buf.cpu()), lse=lse.cpu().numpy()[:, :inp.total_q] if want_lse else None,
                      status=st)

@@ -71,3 +71,55 @@ def test_empty_problems_return_ok_without_launch(kw):
 def test_check_raises_with_status_name():
     with pytest.raises(fmha.FmhaError, match="FMHA_ERR_INVALID_SHAPE"):
         fmha.check(call(D=48))
+
+
+# ---- split-KV entry point ----------------------------------------------------------------
+def call_skv(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Sq=1, Sk=300, H=4, H_kv=2, D=64, scale=0.125, mask="none",
+             dtype="f16", o_scale=1.0, varlen=None, workspace=P, workspace_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return fmha.fmha_fwd_splitkv(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(workspace=None), 1),
+    (dict(varlen=fmha.make_varlen(P, None, 1, 300)), 1),
+    (dict(B=-1), 2), (dict(H=3, H_kv=2), 2), (dict(D=96), 2),
+    (dict(dtype="f8e4m3", D=128), 3), (dict(dtype=7), 3), (dict(mask=9), 3),
+    (dict(Sk=1 << 22, H=64, H_kv=64, D=128), 3),
+    (dict(q=P + 4), 4), (dict(lse=P + 1), 4), (dict(workspace=P + 8), 4),
+    (dict(scale=0.0), 5), (dict(o_scale=float("nan")), 5), (dict(workspace_bytes=100), 5),
+])
+def test_splitkv_invalid_arguments_are_rejected(kw, status):
+    assert call_skv(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Sq=0), dict(B=0, workspace=None, workspace_bytes=0)])
+def test_splitkv_empty_problems_return_ok_without_launch(kw):
+    assert call_skv(**kw) == 0
+
+
+def test_splitkv_workspace_is_rejected_one_byte_short():
+    need = fmha.fmha_fwd_splitkv_workspace_size(1, 1, 300, 4, 2, 64)
+    assert need > 0
+    assert call_skv(workspace_bytes=need - 1) == 5
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1, 1, 32), (16, 1, 8192, 32, 8, 128), (2, 4, 1000, 16, 2, 64),
+                                   (3, 16, 70000, 8, 8, 128), (64, 1, 300, 8, 1, 64), (1, 300, 5, 4, 4, 32)])
+def test_splitkv_workspace_size_holds_whole_splits(shape):
+    # n_splits partial rows of D fp32 values and one fp32 LSE per (query row, head), n_splits >= 1,
+    # and no split shorter than the 256-key minimum unless there is only one
+    B, Sq, Sk, H, H_kv, D = shape
+    rows = B * Sq * H
+    need = fmha.fmha_fwd_splitkv_workspace_size(B, Sq, Sk, H, H_kv, D)
+    assert need % (rows * (D + 1) * 4) == 0
+    n_splits = need // (rows * (D + 1) * 4)
+    assert 1 <= n_splits <= max(1, -(-Sk // 256))
+
+
+def test_splitkv_workspace_size_packed_uses_total_rows():
+    vl = fmha.make_varlen(P, P, 7, 5000)
+    need = fmha.fmha_fwd_splitkv_workspace_size(3, 4, 3000, 8, 2, 64, vl)
+    assert need > 0 and need % (7 * 8 * 65 * 4) == 0
+    assert fmha.fmha_fwd_splitkv_workspace_size(3, 4, 3000, 6, 4, 64) == 0  # H % H_kv != 0
