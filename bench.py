@@ -10,6 +10,10 @@ JSON line with the throughput in TFLOP/s (4*B*H*Sq*Sk*D, halved for causal masks
 roofline of the kernel (FLOPs per launch over the average launch duration measured with
 HIP events on the launch stream, against MI355X's dense MFMA peak for the dtype), and the
 fp64 CPU oracle timed on a bounded sample of the same workload.
+
+--config 6 is the generation / decode workload of fmha_fwd_splitkv (one split-KV call per
+step, both of its kernels): bound by HBM, so its line reports GB/s of algorithmic bytes
+(|Q| + |K| + |V| + |O| + |LSE|) against MI355X's 8 TB/s.
 """
 from __future__ import annotations
 
@@ -32,18 +36,26 @@ from workloads import CONFIGS, make_config, to_bits  # noqa: E402
 
 # MI355X published dense peaks (TFLOP/s): 256 CUs x 2.4 GHz x {4096 fp16/bf16, 8192 fp8} FLOP/clk/CU
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f8e4m3": 5033.2}
-KERNEL_SOURCE = os.path.join(ROOT, "head_attention_03_amd", "csrc", "fmha_fwd.hip")
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+CSRC = os.path.join(ROOT, "head_attention_03_amd", "csrc")
+KERNEL_SOURCES = {"fwd": ("fmha_fwd.hip", "fmha_device.h"), "splitkv": ("fmha_splitkv.hip", "fmha_device.h")}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(entry: str = "fwd") -> str:
+    """Hash of the sources a workload's kernels are compiled from."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[entry]:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def workload_slug(c: dict) -> str:
     """File-name tag of a workload: dtype, head dim, mask, sizes."""
+    heads = f"h{c['H']}" if c["H"] == c["H_kv"] else f"h{c['H']}kv{c['H_kv']}"
+    if c.get("entry") == "splitkv":
+        return f"splitkv_{c['dtype']}_d{c['D']}_{c['mask']}_b{c['B']}_{heads}_q{c['Sq']}_k{c['Sk']}"
     if c["kind"] == "dense":
-        heads = f"h{c['H']}" if c["H"] == c["H_kv"] else f"h{c['H']}kv{c['H_kv']}"
         return f"{c['dtype']}_d{c['D']}_{c['mask']}_b{c['B']}_{heads}_s{c['Sq']}"
     return f"{c['dtype']}_d{c['D']}_varlen{c['nseq']}_h{c['H']}"
 
@@ -55,9 +67,17 @@ def measured_traffic(c: dict):
         rec = json.load(open(os.path.join(PROFILES, f"fmha_fwd_{workload_slug(c)}_traffic.json")))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(c.get("entry", "fwd")):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def algorithmic_bytes(inp, want_lse: bool) -> float:
+    """|Q| + |K| + |V| + |O| (+ |LSE|) of a dense workload: what the path must move at least."""
+    e = 1 if inp.dtype == "f8e4m3" else 2
+    qo = 2.0 * inp.B * inp.Sq * inp.H * inp.D * e
+    kv = 2.0 * inp.B * inp.Sk * inp.H_kv * inp.D * e
+    return qo + kv + (4.0 * inp.B * inp.H * inp.Sq if want_lse else 0.0)
 
 
 def cpu_baseline(config_id: int, budget_s: float):
@@ -82,6 +102,11 @@ def cpu_baseline(config_id: int, budget_s: float):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
+    if CONFIGS[config_id].get("entry") == "splitkv":  # the same unit as the GPU line: GB/s of the workload's bytes
+        gbs = algorithmic_bytes(inp, bool(CONFIGS[config_id]["lse"])) * done / len(units) / dt / 1e9
+        return {"value": round(gbs, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"{done} of {len(units)} (sequence, head) units of the same workload, fp64 numpy, "
+                          f"{dt:.1f} s on {platform.processor() or platform.machine()}"}
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {len(units)} (sequence, head) units of the same workload, fp64 numpy, "
                       f"{dt:.1f} s on {platform.processor() or platform.machine()}"}
@@ -141,12 +166,21 @@ def main():
             flops_step += inp.flops_convention()
 
     stream = torch.cuda.Stream(device=dev)  # default priority
+    splitkv = c.get("entry") == "splitkv"
+    ws_bytes = fmha.fmha_fwd_splitkv_workspace_size(B, Sq, Sk, inp.H, inp.H_kv, inp.D, None) if splitkv else 0
+    # one workspace serves every set: the launches run one after another on one stream
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev) if splitkv else None
 
     def launch(i):
         s = sets[i % len(sets)]
         for m in masks:
-            st = fmha.fmha_fwd(s["q"], s["k"], s["v"], s["o"], s["lse"], B, Sq, Sk, inp.H, inp.H_kv, inp.D,
-                               inp.kernel_scale, m, inp.dtype, inp.kernel_o_scale, s["varlen"], stream)
+            if splitkv:
+                st = fmha.fmha_fwd_splitkv(s["q"], s["k"], s["v"], s["o"], s["lse"], B, Sq, Sk, inp.H, inp.H_kv,
+                                           inp.D, inp.kernel_scale, m, inp.dtype, inp.kernel_o_scale, s["varlen"],
+                                           ws, ws_bytes, stream)
+            else:
+                st = fmha.fmha_fwd(s["q"], s["k"], s["v"], s["o"], s["lse"], B, Sq, Sk, inp.H, inp.H_kv, inp.D,
+                                   inp.kernel_scale, m, inp.dtype, inp.kernel_o_scale, s["varlen"], stream)
             if st != 0:
                 raise fmha.FmhaError(st)
 
@@ -172,13 +206,23 @@ def main():
     achieved = flops_step / len(masks) / avg_launch_s / 1e12
     peak = PEAK_TFLOPS[inp.dtype]
     traffic = measured_traffic(c)
+    metric, unit, bound = "FMHA fwd TFLOP/s and % of MI355X dense MFMA peak (bf16, D=128, causal)", "TFLOP/s", "mfma"
+    tflops = value
+    if splitkv:  # HBM-bound: GB/s of algorithmic bytes
+        bytes_step = algorithmic_bytes(inp, want_lse)
+        metric, unit, bound = "FMHA split-KV decode GB/s of algorithmic HBM bytes and % of MI355X HBM peak", "GB/s", "hbm"
+        value = bytes_step * args.steps / elapsed / 1e9
+        achieved = bytes_step / avg_launch_s / 1e9
+        peak = PEAK_HBM_GBS
     cfg = {"workload": c["name"], "config_id": cid, "B": B, "Sq": Sq, "Sk": Sk, "H": inp.H, "H_kv": inp.H_kv,
            "D": inp.D, "dtype": inp.dtype, "mask": "+".join(masks), "lse": want_lse, "seed": inp.seed,
            "rotate_buffers": len(sets), "flop_per_step": flops_step}
+    if splitkv:
+        cfg.update(entry="fmha_fwd_splitkv", tflops=round(tflops, 3), workspace_bytes=ws_bytes)
     out = {
-        "metric": "FMHA fwd TFLOP/s and % of MI355X dense MFMA peak (bf16, D=128, causal)",
+        "metric": metric,
         "value": round(value, 3),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -190,7 +234,7 @@ def main():
         "data": "synthetic (seeded N(0,1))",
         "config": cfg,
         "pct_of_peak": round(100.0 * value / peak, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_avg_us": round(avg_launch_s * 1e6, 3)},
         "cpu_baseline": None,

@@ -14,10 +14,13 @@
 // CDNA4 design:
 // * The work is bound by HBM bandwidth (each K/V byte meets only the few query rows of its
 //   group), so the kernel is built to keep loads in flight rather than to share K/V tiles:
-//   a workgroup has 2 waves, and each wave streams every other 32-key tile of the split
-//   through a private ring of 4 LDS stages (LDS-direct loads, three tiles in flight, no
-//   barrier inside the loop).  The two waves' online-softmax states are merged in LDS at
-//   the end.
+//   each wave streams its 32-key tiles through a private ring of 4 LDS stages (LDS-direct
+//   loads, three tiles = 48 KiB in flight, no barrier inside the loop).  A workgroup is one
+//   wave (kWaves; with more, the waves take turns over the tiles and merge their states in
+//   LDS at the end), so two workgroups share a compute unit (72 KiB of LDS each) and one's
+//   start-up latency overlaps the other's stream: 3.5% faster than two waves sharing one
+//   workgroup's 144 KiB.  The vector-memory counter caps a wave at 63 loads in flight, so a
+//   deeper ring would need more waves, and the LDS rings cap those.
 // * A workgroup covers 32 packed query rows (row r: head kv_h * group + r / Sq, query r % Sq)
 //   of one (sequence, K/V head).  S^T = K Q^T and O^T += V^T P^T run on the same
 //   v_mfma_f32_32x32x16 operand layouts as fmha_fwd (K and V rows XOR-swizzled in LDS, V^T
@@ -38,7 +41,7 @@
 namespace fmha {
 namespace skv {
 
-constexpr int kWaves = 2;       // waves per workgroup, each streaming its own K/V tiles
+constexpr int kWaves = 1;       // waves per workgroup, each streaming its own K/V tiles
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTN = 32;         // keys per tile: one 32-key block of the MFMA
 constexpr int kStages = 4;      // tiles in a wave's LDS ring (three in flight)
@@ -297,34 +300,39 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
   // ---- merge the waves' states in LDS (the rings are free now), then write the partial --
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   const float l_tot = wave_row_sum(l_run);
-  __syncthreads();
-  float* xm = (float*)lds;                  // [kWaves][64] running maxima
-  float* xl = xm + kWaves * 64;             // [kWaves][64] row sums
-  float* xo = xl + kWaves * 64;             // [kWaves][NDB * 16][64] accumulators, lane-major
-  xm[wave_u * 64 + lane] = m_run;
-  xl[wave_u * 64 + lane] = l_tot;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) xo[(wave_u * NDB * 16 + db * 16 + e) * 64 + lane] = acc_o[db][e];
-  __syncthreads();
-  if (wave_u != 0) return;
-  float m_all = xm[lane];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) m_all = __builtin_fmaxf(m_all, xm[w * 64 + lane]);
-  float l_all = 0.0f;
+  float m_all = m_run, l_all = l_tot;
   f32x16 o_all[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) o_all[db] = f32x16{};
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float mw = xm[w * 64 + lane];
-    const float a = mw == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mw - m_all);
-    l_all += a * xl[w * 64 + lane];
+  for (int db = 0; db < NDB; ++db) o_all[db] = acc_o[db];
+  if constexpr (kWaves > 1) {
+    __syncthreads();
+    float* xm = (float*)lds;                  // [kWaves][64] running maxima
+    float* xl = xm + kWaves * 64;             // [kWaves][64] row sums
+    float* xo = xl + kWaves * 64;             // [kWaves][NDB * 16][64] accumulators, lane-major
+    xm[wave_u * 64 + lane] = m_run;
+    xl[wave_u * 64 + lane] = l_tot;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o_all[db][e] += a * xo[(w * NDB * 16 + db * 16 + e) * 64 + lane];
+      for (int e = 0; e < 16; ++e) xo[(wave_u * NDB * 16 + db * 16 + e) * 64 + lane] = acc_o[db][e];
+    __syncthreads();
+    if (wave_u != 0) return;
+    m_all = xm[lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m_all = __builtin_fmaxf(m_all, xm[w * 64 + lane]);
+    l_all = 0.0f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o_all[db] = f32x16{};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = xm[w * 64 + lane];
+      const float a = mw == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mw - m_all);
+      l_all += a * xl[w * 64 + lane];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o_all[db][e] += a * xo[(w * NDB * 16 + db * 16 + e) * 64 + lane];
+    }
   }
   if (!row_ok) return;
   const size_t row = (size_t)(q_row0 + qi) * p.H + hq;

@@ -259,7 +259,8 @@ def make_varlen(seed: int, seqlens_q: Sequence[int], seqlens_k: Sequence[int], H
                         scale=float(scale), o_scale=float(o_scale), seed=seed, q_scale=sq, k_scale=sk, v_scale=sv)
 
 
-# The five measured workloads.  Config 4 is run twice on the same inputs (residual, then causal-qend).
+# The measured workloads.  Config 4 is run twice on the same inputs (residual, then causal-qend);
+# config 6 is the split-KV (decode) entry point's workload.
 CONFIGS = {
     1: dict(name="tiny dense fp16 D64 no mask", kind="dense", B=1, H=2, H_kv=2, Sq=128, Sk=128, D=64,
             dtype="f16", mask="none", lse=False, o_scale=1.0),
@@ -272,6 +273,10 @@ CONFIGS = {
             o_scale=1.0),
     5: dict(name="fp8 e4m3 D128 no mask, output scale 0.5", kind="dense", B=8, H=16, H_kv=16, Sq=4096, Sk=4096,
             D=128, dtype="f8e4m3", mask="none", lse=False, o_scale=0.5),
+    # Generation / decode, run through fmha_fwd_splitkv: one new token per sequence against an
+    # 8192-key cache, GQA 32/8 (one query row per head: no mask and causal-qend coincide).
+    6: dict(name="decode GQA bf16 D128, 1 token vs 8192 keys (split-KV)", kind="dense", entry="splitkv", B=16,
+            H=32, H_kv=8, Sq=1, Sk=8192, D=128, dtype="bf16", mask="none", lse=True, o_scale=1.0),
 }
 
 
