@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the fused multi-head attention forward pass.
+"""fp64 CPU oracle of the fused multi-head attention forward and backward passes.
 
 TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only ``tests/``,
 ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
@@ -25,6 +25,15 @@ Pins (tests/test_oracle.py, run with ``-m "not gpu"``):
   offset, wrong GQA head, missing scale, transposed operand) fail the pins;
 * the FLOP convention reproduces the TFLOP/s column printed by the sm120 article.
 
+Backward pins (tests/test_oracle_backward.py): torch autograd through a materialised fp64
+attention and through torch's scaled_dot_product_attention (GQA batches, every mask); central
+finite differences of the forward oracle; closed forms (one key: dQ = dK = 0 and dV = sum of
+dO; Q = 0: uniform weights); invariants (sum of dK over the keys is 0, sum of dV equals the
+sum of dO over rows with a key, unseen keys get no gradient, linearity in dO, sum_d O dO =
+sum_j P dP, GQA == MHA on repeated heads summed, packed == per-sequence); planted mistakes
+(dropped or sign-flipped softmax term, untransposed operands, missing or doubled scale, dP
+from K, GQA overwrite or wrong head, varlen key offset) fail the pins.
+
 No function is "parity unpinned" except the two choices the pages leave open:
 rows with no visible key (O = 0, LSE = -inf) and fp8 saturation at +-448, which
 are pinned only by those stated choices.
@@ -38,3 +47,9 @@ from .attention import (  # noqa: F401
     visible_keys,
 )
 from .formats import decode, decode_minifloat  # noqa: F401
+from .backward import (  # noqa: F401
+    attention_backward_dense,
+    attention_backward_varlen,
+    attention_head_backward,
+    sum_o_do,
+)
