@@ -14,6 +14,11 @@ fp64 CPU oracle timed on a bounded sample of the same workload.
 --config 6 is the generation / decode workload of fmha_fwd_splitkv (one split-KV call per
 step, both of its kernels): bound by HBM, so its line reports GB/s of algorithmic bytes
 (|Q| + |K| + |V| + |O| + |LSE|) against MI355X's 8 TB/s.
+
+--config 7 is the backward pass (one fmha_bwd call per step: its statistics, dQ and dK/dV
+kernels) of the prefill shape, with O and LSE from fmha_fwd computed once before timing.  Its
+FLOPs follow the 5-matmul count (S, dP, dV, dQ, dK: 2.5 times the forward's 4*B*H*Sq*Sk*D,
+halved for causal masks); the roofline is taken over the whole call.
 """
 from __future__ import annotations
 
@@ -38,7 +43,9 @@ from workloads import CONFIGS, make_config, to_bits  # noqa: E402
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f8e4m3": 5033.2}
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 CSRC = os.path.join(ROOT, "head_attention_03_amd", "csrc")
-KERNEL_SOURCES = {"fwd": ("fmha_fwd.hip", "fmha_device.h"), "splitkv": ("fmha_splitkv.hip", "fmha_device.h")}
+KERNEL_SOURCES = {"fwd": ("fmha_fwd.hip", "fmha_device.h"), "splitkv": ("fmha_splitkv.hip", "fmha_device.h"),
+                  "bwd": ("fmha_bwd.hip", "fmha_device.h")}
+BWD_FLOP_FACTOR = 2.5  # backward matmuls (S, dP, dV, dQ, dK) per forward matmul pair
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -53,6 +60,8 @@ def kernel_source_hash(entry: str = "fwd") -> str:
 def workload_slug(c: dict) -> str:
     """File-name tag of a workload: dtype, head dim, mask, sizes."""
     heads = f"h{c['H']}" if c["H"] == c["H_kv"] else f"h{c['H']}kv{c['H_kv']}"
+    if c.get("entry") == "bwd":
+        return f"bwd_{c['dtype']}_d{c['D']}_{c['mask']}_b{c['B']}_{heads}_s{c['Sq']}"
     if c.get("entry") == "splitkv":
         return f"splitkv_{c['dtype']}_d{c['D']}_{c['mask']}_b{c['B']}_{heads}_q{c['Sq']}_k{c['Sk']}"
     if c["kind"] == "dense":
@@ -64,7 +73,8 @@ def measured_traffic(c: dict):
     """HBM bytes per launch from the committed rocprofv3 counter summary of this workload,
     if it was taken on the current kernel source (else None)."""
     try:
-        rec = json.load(open(os.path.join(PROFILES, f"fmha_fwd_{workload_slug(c)}_traffic.json")))
+        prefix = "fmha_" if c.get("entry") == "bwd" else "fmha_fwd_"
+        rec = json.load(open(os.path.join(PROFILES, f"{prefix}{workload_slug(c)}_traffic.json")))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256_16") != kernel_source_hash(c.get("entry", "fwd")):
@@ -94,11 +104,20 @@ def cpu_baseline(config_id: int, budget_s: float):
     v = oracle.decode(to_bits(inp.v), inp.dtype) * inp.v_scale
     group = inp.H // inp.H_kv
     units = [(b, h) for b in range(inp.B) for h in range(inp.H)]
+    bwd = CONFIGS[config_id].get("entry") == "bwd"
+    if bwd:
+        from workloads import make_grad
+        do = oracle.decode(to_bits(make_grad(inp.seed + 1, (inp.B, inp.Sq, inp.H, inp.D), inp.dtype)), inp.dtype)
     done, flops, t0 = 0, 0.0, time.perf_counter()
     for b, h in units:
-        oracle.attention_head(q[b, :, h], k[b, :, h // group], v[b, :, h // group], inp.scale, inp.mask)
+        if bwd:
+            oracle.attention_head_backward(q[b, :, h], k[b, :, h // group], v[b, :, h // group], do[b, :, h],
+                                           inp.scale, inp.mask)
+            flops += BWD_FLOP_FACTOR * inp.flops() / len(units)
+        else:
+            oracle.attention_head(q[b, :, h], k[b, :, h // group], v[b, :, h // group], inp.scale, inp.mask)
+            flops += inp.flops() / len(units)
         done += 1
-        flops += inp.flops() / len(units)
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
@@ -167,6 +186,21 @@ def main():
 
     stream = torch.cuda.Stream(device=dev)  # default priority
     splitkv = c.get("entry") == "splitkv"
+    bwd = c.get("entry") == "bwd"
+    if bwd:
+        # the backward's inputs: dO (seeded), and O and LSE of the forward, computed once here
+        from workloads import make_grad
+        do_cpu = make_grad(inp.seed + 1, (inp.B, inp.Sq, inp.H, inp.D), inp.dtype)
+        bws = fmha.fmha_bwd_workspace_size(B, Sq, Sk, inp.H, inp.H_kv, inp.D, None)
+        for s_ in sets:
+            lse = s_["lse"] if s_["lse"] is not None else torch.empty((B, inp.H, Sq), dtype=torch.float32, device=dev)
+            fmha.check(fmha.fmha_fwd(s_["q"], s_["k"], s_["v"], s_["o"], lse, B, Sq, Sk, inp.H, inp.H_kv, inp.D,
+                                     inp.kernel_scale, inp.mask, inp.dtype, 1.0, None, stream))
+            s_.update(lse=lse, do=do_cpu.to(dev), dq=torch.empty_like(s_["q"]), dk=torch.empty_like(s_["k"]),
+                      dv=torch.empty_like(s_["v"]))
+        bw = torch.empty(max(bws, 16), dtype=torch.uint8, device=dev)
+        flops_step = BWD_FLOP_FACTOR * flops_step
+        torch.cuda.synchronize()
     ws_bytes = fmha.fmha_fwd_splitkv_workspace_size(B, Sq, Sk, inp.H, inp.H_kv, inp.D, None) if splitkv else 0
     # one workspace serves every set: the launches run one after another on one stream
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev) if splitkv else None
@@ -174,7 +208,10 @@ def main():
     def launch(i):
         s = sets[i % len(sets)]
         for m in masks:
-            if splitkv:
+            if bwd:
+                st = fmha.fmha_bwd(s["q"], s["k"], s["v"], s["o"], s["do"], s["lse"], s["dq"], s["dk"], s["dv"], B, Sq,
+                                   Sk, inp.H, inp.H_kv, inp.D, inp.kernel_scale, m, inp.dtype, None, bw, bws, stream)
+            elif splitkv:
                 st = fmha.fmha_fwd_splitkv(s["q"], s["k"], s["v"], s["o"], s["lse"], B, Sq, Sk, inp.H, inp.H_kv,
                                            inp.D, inp.kernel_scale, m, inp.dtype, inp.kernel_o_scale, s["varlen"],
                                            ws, ws_bytes, stream)
@@ -207,6 +244,8 @@ def main():
     peak = PEAK_TFLOPS[inp.dtype]
     traffic = measured_traffic(c)
     metric, unit, bound = "FMHA fwd TFLOP/s and % of MI355X dense MFMA peak (bf16, D=128, causal)", "TFLOP/s", "mfma"
+    if bwd:
+        metric = "FMHA bwd TFLOP/s (5-matmul count) and % of MI355X dense MFMA peak (bf16, D=128, causal)"
     tflops = value
     if splitkv:  # HBM-bound: GB/s of algorithmic bytes
         bytes_step = algorithmic_bytes(inp, want_lse)
@@ -219,6 +258,8 @@ def main():
            "rotate_buffers": len(sets), "flop_per_step": flops_step}
     if splitkv:
         cfg.update(entry="fmha_fwd_splitkv", tflops=round(tflops, 3), workspace_bytes=ws_bytes)
+    if bwd:
+        cfg.update(entry="fmha_bwd", workspace_bytes=bws, flop_convention="2.5 x forward (S, dP, dV, dQ, dK)")
     out = {
         "metric": metric,
         "value": round(value, 3),

@@ -1,4 +1,4 @@
-"""MI355X (gfx950) fused multi-head attention forward pass.
+"""MI355X (gfx950) fused multi-head attention: forward pass (dense and split-KV) and backward pass.
 
 The computation lives in libfmha.so (hand-written HIP, C ABI in include/fmha.h); this
 package only loads it and marshals arguments.
@@ -10,6 +10,8 @@ from ._lib import (  # noqa: F401
     MASKS,
     FmhaError,
     check,
+    fmha_bwd,
+    fmha_bwd_workspace_size,
     fmha_fwd,
     fmha_fwd_splitkv,
     fmha_fwd_splitkv_workspace_size,

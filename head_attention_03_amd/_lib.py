@@ -19,7 +19,8 @@ MASKS = {"none": 0, "residual": 1, "causal_qbegin": 2, "causal_qend": 3}
 STATUS = {0: "FMHA_OK", 1: "FMHA_ERR_NULL_POINTER", 2: "FMHA_ERR_INVALID_SHAPE", 3: "FMHA_ERR_UNSUPPORTED",
           4: "FMHA_ERR_MISALIGNED", 5: "FMHA_ERR_INVALID_ARGUMENT", 6: "FMHA_ERR_HIP"}
 # every symbol include/fmha.h declares
-EXPORTS = ("fmha_fwd", "fmha_fwd_splitkv", "fmha_fwd_splitkv_workspace_size", "fmha_status_string", "fmha_version")
+EXPORTS = ("fmha_fwd", "fmha_fwd_splitkv", "fmha_fwd_splitkv_workspace_size", "fmha_bwd", "fmha_bwd_workspace_size",
+           "fmha_status_string", "fmha_version")
 
 
 class FmhaError(RuntimeError):
@@ -53,6 +54,12 @@ def load() -> ctypes.CDLL:
         ctypes.c_size_t, ctypes.c_void_p]
     lib.fmha_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fmha_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int32] * 6 + [ctypes.POINTER(fmha_varlen)]
+    lib.fmha_bwd.restype = ctypes.c_int
+    lib.fmha_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int32] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.POINTER(fmha_varlen), ctypes.c_void_p, ctypes.c_size_t,
+        ctypes.c_void_p]
+    lib.fmha_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fmha_bwd_workspace_size.argtypes = [ctypes.c_int32] * 6 + [ctypes.POINTER(fmha_varlen)]
     lib.fmha_status_string.restype = ctypes.c_char_p
     lib.fmha_status_string.argtypes = [ctypes.c_int]
     lib.fmha_version.restype = ctypes.c_int32
@@ -109,6 +116,25 @@ def fmha_fwd_splitkv_workspace_size(B: int, Sq: int, Sk: int, H: int, H_kv: int,
                                     varlen: Optional[fmha_varlen] = None) -> int:
     vl = ctypes.byref(varlen) if varlen is not None else None
     return int(load().fmha_fwd_splitkv_workspace_size(int(B), int(Sq), int(Sk), int(H), int(H_kv), int(D), vl))
+
+
+def fmha_bwd(q, k, v, o, dout, lse, dq, dk, dv, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int, scale: float,
+             mask, dtype, varlen: Optional[fmha_varlen] = None, workspace=None, workspace_bytes: int = 0,
+             stream=None) -> int:
+    """Call the backward C entry point; returns the fmha_status code."""
+    lib = load()
+    mask = MASKS[mask] if isinstance(mask, str) else int(mask)
+    dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    vl = ctypes.byref(varlen) if varlen is not None else None
+    return int(lib.fmha_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                            int(B), int(Sq), int(Sk), int(H), int(H_kv), int(D), float(scale), mask, dtype, vl,
+                            _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def fmha_bwd_workspace_size(B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int,
+                            varlen: Optional[fmha_varlen] = None) -> int:
+    vl = ctypes.byref(varlen) if varlen is not None else None
+    return int(load().fmha_bwd_workspace_size(int(B), int(Sq), int(Sk), int(H), int(H_kv), int(D), vl))
 
 
 def fmha_status_string(status: int) -> str:

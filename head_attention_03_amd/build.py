@@ -13,7 +13,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "fmha_fwd.hip"), os.path.join(HERE, "csrc", "fmha_splitkv.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "fmha_fwd.hip"), os.path.join(HERE, "csrc", "fmha_splitkv.hip"),
+           os.path.join(HERE, "csrc", "fmha_bwd.hip")]
 LIB = os.path.join(HERE, "libfmha.so")
 ARCH = "gfx950"
 

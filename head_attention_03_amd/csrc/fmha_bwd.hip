@@ -1,0 +1,734 @@
+// Backward of the fused attention forward pass on gfx950: dQ, dK and dV of
+// O = softmax(scale * Q K^T + mask) V for an upstream gradient dO.
+//
+// The CUTLASS Blackwell FMHA walk-through (trdm.cn, "CUTLASS Blackwell FMHA 示例完全解析",
+// section "FMHA for Blackwell: Backward") splits the backward into a row sum of O * dO, a main
+// pass that recomputes the probabilities from the forward's LSE and forms dQ, dK and dV (in a
+// dK/dV kernel and a dQ kernel), and a conversion of dQ from fp32 to the output type.  With
+// P = exp(scale * S - LSE) recomputed tile by tile:
+//
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - delta),   delta_i = sum_d O_id dO_id,
+//     dQ = scale * dS K,   dK = scale * dS^T Q,
+//
+// masked positions carrying P = 0 (the backward mask of the walk-through's fusion-point
+// section: the forward masks with the causal offset 0 or Sk - Sq).
+//
+// CDNA4 design (three kernels, no atomics, deterministic):
+// * stats_kernel: delta_i and LSE_i * log2(e) (+inf for a row with no key) into a workspace of
+//   64-row blocks [lse2[64], delta[64]]; the rows past a sequence's end in its last block get
+//   +inf and 0, so the kernels below read whole blocks and padding rows yield P = 0.
+// * dq_kernel: a workgroup owns 256 query rows of one (sequence, head), 32 per wave, with its Q
+//   and dO rows held as MFMA B operands in registers; 64-key K/V tiles stream through a 3-stage
+//   LDS ring (LDS-direct loads, one barrier per tile).  S^T = K Q^T and dP^T = V dO^T run on
+//   v_mfma_f32_32x32x16 with K and V read row-wise from LDS; the accumulator layout of dS^T is
+//   the B operand of dQ^T += K^T dS^T, whose A operand is K read transposed with
+//   ds_read_b64_tr_b16 (the key order of the accumulator rows).  dQ is owned by one wave, so it
+//   is scaled and converted in registers and stored once: the fp32 conversion step of the
+//   walk-through folds into the epilogue.
+// * dkdv_kernel: a workgroup owns 128 keys of one (sequence, K/V head), 32 per wave, with K and
+//   V held as B operands in registers; 64-row Q/dO tiles (and their row statistics) stream
+//   through the ring for every query head of the GQA group.  S = Q K^T and dP = dO V^T put the
+//   wave's keys in the accumulator columns, so P and dS are directly the B operands of
+//   dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read transposed from LDS.  dK and dV
+//   of a K/V head sum over its group's query heads inside one workgroup.
+// Masks, varlen and GQA follow fmha_fwd: buffer descriptors bounded to the sequence (rows past
+// either end read 0 and are not written), the causal offset Sk_b - Sq_b for causal-qend, and
+// tiles that no row of a wave sees skipped by that wave.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fmha.h"
+#include "fmha_device.h"
+
+namespace fmha {
+namespace bwd {
+
+constexpr int kAuxRows = 64;                 // rows per block of the row-statistics workspace
+constexpr int kAuxBlock = 2 * kAuxRows * 4;  // bytes per block: lse2[64], then delta[64]
+constexpr int kStages = 3;                   // LDS ring depth of both main kernels
+
+constexpr int kKvWaves = 4;             // dK/dV kernel: waves per workgroup, 32 keys each
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKvN = 32 * kKvWaves;     // keys per workgroup
+constexpr int kKvM = kAuxRows;          // query rows per streamed tile
+
+constexpr int kQWaves = 8;              // dQ kernel: waves per workgroup, 32 query rows each
+constexpr int kQThreads = 64 * kQWaves;
+constexpr int kQM = 32 * kQWaves;       // query rows per workgroup
+constexpr int kQN = 64;                 // keys per streamed tile
+
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* aux;            // workspace: row-statistics blocks
+  uint32_t aux_bytes;
+  const int32_t* cu_q;   // null for dense batches
+  const int32_t* cu_k;
+  int32_t B, Sq, Sk, H, H_kv, group;
+  int32_t total_q;       // packed: LSE row length; dense: 0
+  int32_t aux_bstride;   // dense: blocks per sequence (H * ceil(Sq / 64)); packed: 0
+  int32_t aux_hstride;   // blocks between consecutive heads of one sequence
+  int32_t n_tiles;       // stats: 64-row blocks per sequence; dq: q tiles; dkdv: key tiles
+  int32_t xcd_per;       // (sequence, head) pairs per XCD when their count is a multiple of 8
+  int32_t causal, qend;
+  float scale, scale_log2;
+};
+
+struct Seq {
+  int q_row0, Sq_b, k_row0, Sk_b;
+};
+
+__device__ inline Seq seq_bounds(const Params& p, int b) {
+  Seq s;
+  if (p.cu_q) {
+    s.q_row0 = p.cu_q[b];
+    s.Sq_b = p.cu_q[b + 1] - s.q_row0;
+    s.k_row0 = p.cu_k[b];
+    s.Sk_b = p.cu_k[b + 1] - s.k_row0;
+  } else {
+    s.q_row0 = b * p.Sq;
+    s.Sq_b = p.Sq;
+    s.k_row0 = b * p.Sk;
+    s.Sk_b = p.Sk;
+  }
+  return s;
+}
+
+// First statistics block of sequence b (head 0).  Packed batches give sequence b the blocks
+// from floor(cu_q[b] / 64) + b on, which never overlap the next sequence's.
+__device__ inline int aux_seq_base(const Params& p, int b, int q_row0) {
+  return p.cu_q ? (q_row0 >> 6) + b : b * p.aux_bstride;
+}
+
+// (pair, group) of a workgroup: round-robin dispatch puts workgroup x on XCD x % 8, so the
+// pairs are dealt out per XCD and the workgroups of one pair share that XCD's L2.
+__device__ inline void decode_unit(const Params& p, int npairs, int* pair, int* grp) {
+  const int x = blockIdx.x;
+  if (p.xcd_per) {
+    const int slot = x >> 3;
+    *grp = slot / p.xcd_per;
+    *pair = (x & 7) * p.xcd_per + slot % p.xcd_per;
+  } else {
+    *grp = x / npairs;
+    *pair = x % npairs;
+  }
+}
+
+__device__ inline i32x4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// A operand of v_mfma_f32_32x32x16 read transposed from a row-major LDS tile: element
+// (m = dim 32 db + l32, k = one of 16 tile rows starting at `rows`), the rows in the order of a
+// 32x32 accumulator's rows (4 h32 + 0..3, then 8 + 4 h32 + 0..3).
+__device__ inline i32x4 read_tr(uint32_t lane0, uint32_t lane1, int db, uint32_t rows) {
+  const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)((lane0 ^ (64 * db)) + rows));
+  const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)((lane1 ^ (64 * db)) + rows));
+  const i32x4 a = {__builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 0, 1)),
+                   __builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 2, 3)),
+                   __builtin_bit_cast(int, __builtin_shufflevector(v1, v1, 0, 1)),
+                   __builtin_bit_cast(int, __builtin_shufflevector(v1, v1, 2, 3))};
+  return a;
+}
+
+// Stores a 32x32 accumulator block times f as 16-bit values, 16 bytes per lane: the block's
+// rows are 32 consecutive dims of the output row given by the lane's column (lane l32, h32 holds
+// rows 8 g + 4 h32 + 0..3).  A lane swap across the halves gives each lane dims 16 gp + 8 h32 ..
+// + 7, which it writes at at + 2 * that dim; rows outside the descriptor are dropped.
+template <int DT>
+__device__ inline void store_block(const f32x16& a, float f, __amdgpu_buffer_rsrc_t r, uint32_t at, int h32) {
+  typedef Elem<DT> T;
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp) {
+    const int g0 = 2 * gp, g1 = 2 * gp + 1;
+    auto r0 = __builtin_amdgcn_permlane32_swap(T::pack(a[4 * g0] * f, a[4 * g0 + 1] * f),
+                                               T::pack(a[4 * g1] * f, a[4 * g1 + 1] * f), false, false);
+    auto r1 = __builtin_amdgcn_permlane32_swap(T::pack(a[4 * g0 + 2] * f, a[4 * g0 + 3] * f),
+                                               T::pack(a[4 * g1 + 2] * f, a[4 * g1 + 3] * f), false, false);
+    const i32x4 w = {(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, at + (uint32_t)(16 * gp + 8 * h32) * 2, 0, 0);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// stats kernel: one 64-row block of one (sequence, head) per workgroup of 256 threads
+// ------------------------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(256) void stats_kernel(const Params p) {
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int RPP = 256 / CPR;  // rows per pass
+  typedef Elem<DT> T;
+  const int h = blockIdx.y;
+  const int b = blockIdx.x / p.n_tiles;
+  const int qt = blockIdx.x - b * p.n_tiles;
+  const Seq sq = seq_bounds(p, b);
+  if (qt * kAuxRows >= sq.Sq_b) return;
+  float* blk = p.aux + (size_t)(aux_seq_base(p, b, sq.q_row0) + h * p.aux_hstride + qt) * (kAuxBlock / 4);
+  const int c = threadIdx.x % CPR;
+  const int rr = threadIdx.x / CPR;
+#pragma unroll
+  for (int pass = 0; pass < kAuxRows / RPP; ++pass) {
+    const int row = pass * RPP + rr;
+    const int qi = qt * kAuxRows + row;
+    float s = 0.0f;
+    if (qi < sq.Sq_b) {
+      const size_t e = ((size_t)(sq.q_row0 + qi) * p.H + h) * D + 8 * c;
+      const i32x4 o = *(const i32x4*)((const char*)p.o + 2 * e);
+      const i32x4 g = *(const i32x4*)((const char*)p.dout + 2 * e);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s = __builtin_fmaf(T::lo((uint32_t)o[u]), T::lo((uint32_t)g[u]), s);
+        s = __builtin_fmaf(T::hi((uint32_t)o[u]), T::hi((uint32_t)g[u]), s);
+      }
+    }
+#pragma unroll
+    for (int m = CPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    if (c == 0) {
+      float l2 = __builtin_inff(), dl = 0.0f;
+      if (qi < sq.Sq_b) {
+        const float L = p.lse[p.cu_q ? (size_t)h * p.total_q + sq.q_row0 + qi
+                                     : ((size_t)b * p.H + h) * p.Sq + qi];
+        l2 = L == -__builtin_inff() ? __builtin_inff() : L * 1.4426950408889634f;
+        dl = s;
+      }
+      blk[row] = l2;
+      blk[kAuxRows + row] = dl;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// dQ kernel: grid = B * H * n_tiles workgroups of kQThreads
+// ------------------------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(kQThreads, 1) void dq_kernel(const Params p) {
+  constexpr int E = 2;
+  constexpr int RB = D * E;          // bytes per row
+  constexpr int CPR = RB / 16;       // 16-byte chunks per row
+  constexpr int TILE = kQN * RB;     // bytes per K or V tile
+  constexpr int TBLK = TILE / 1024;  // 1 KiB LDS-direct loads per tile
+  constexpr int LPW = 2 * TBLK / kQWaves;  // loads per wave per step (K and V)
+  constexpr int STAGE = 2 * TILE;
+  constexpr int KS = D / 16;
+  constexpr int NDB = D / 32;
+  static_assert(TILE % 1024 == 0 && (2 * TBLK) % kQWaves == 0 && LPW >= 1, "whole loads per wave");
+  static_assert(LPW < 32, "vmcnt range");
+  typedef Elem<DT> T;
+
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * STAGE];
+  const uint32_t ring = (uint32_t)(uintptr_t)(lds_void*)lds;
+
+  const int lane = threadIdx.x & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int l32 = lane & 31;
+  const int h32 = lane >> 5;
+
+  int bh, grp;
+  decode_unit(p, p.B * p.H, &bh, &grp);
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int kvh = h / p.group;
+  const Seq sq = seq_bounds(p, b);
+  const int qt0 = (p.n_tiles - 1 - grp) * kQM;  // heaviest (latest rows) first
+  if (qt0 >= sq.Sq_b) return;
+  const int off = p.qend ? sq.Sk_b - sq.Sq_b : 0;
+  const int q_last = min(qt0 + kQM, sq.Sq_b) - 1;
+  const int k_end = p.causal ? min(sq.Sk_b, q_last + off + 1) : sq.Sk_b;
+  const int n_steps = k_end > 0 ? (k_end + kQN - 1) / kQN : 0;
+
+  const int qw0 = qt0 + 32 * wave_u;  // this wave's rows
+  const int qi = qw0 + l32;           // this lane's row
+  const bool wave_on = qw0 < sq.Sq_b;
+  // last visible key of this lane's row, of the wave's first row, and of its last row
+  const int lim_q = p.causal ? min(sq.Sk_b - 1, qi + off) : sq.Sk_b - 1;
+  const int wave_lim = p.causal ? min(sq.Sk_b - 1, qw0 + off) : sq.Sk_b - 1;
+  const int wave_max = p.causal ? min(sq.Sk_b - 1, qw0 + 31 + off) : sq.Sk_b - 1;
+
+  const uint32_t qstride = (uint32_t)p.H * RB;
+  const uint32_t kstride = (uint32_t)p.H_kv * RB;
+  const size_t q_base = (size_t)sq.q_row0 * qstride;
+  const size_t k_base = ((size_t)sq.k_row0 * p.H_kv + kvh) * RB;
+  const uint32_t q_bytes = sq.Sq_b > 0 ? (uint32_t)sq.Sq_b * qstride : 0;
+  const uint32_t k_bytes = sq.Sk_b > 0 ? (uint32_t)(sq.Sk_b - 1) * kstride + RB : 0;
+  const auto rq = make_rsrc((const char*)p.q + q_base, q_bytes);
+  const auto rdo = make_rsrc((const char*)p.dout + q_base, q_bytes);
+  const auto rdq = make_rsrc((const char*)p.dq + q_base, q_bytes);
+  const i32x4 rk = make_rsrc_words((const char*)p.k + k_base, k_bytes);
+  const i32x4 rv = make_rsrc_words((const char*)p.v + k_base, k_bytes);
+
+  // the wave's Q and dO rows as B operands (row l32, dims 16 ks + 8 h32 ..); rows past the
+  // sequence read 0
+  i32x4 qf[KS], dof[KS];
+  const uint32_t frag = (uint32_t)qi * qstride + (uint32_t)h * RB + 16 * h32;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = load_b128(rq, frag + 32 * ks);
+    dof[ks] = load_b128(rdo, frag + 32 * ks);
+  }
+  float lse2 = __builtin_inff(), delta = 0.0f;
+  if (qi < sq.Sq_b) {
+    const float* blk = p.aux + (size_t)(aux_seq_base(p, b, sq.q_row0) + h * p.aux_hstride + (qi >> 6)) * (kAuxBlock / 4);
+    lse2 = blk[qi & 63];
+    delta = blk[kAuxRows + (qi & 63)];
+  }
+
+  // tile loads: load g of a step (0 .. 2 TBLK - 1; K first, then V) is wave g % kQWaves's
+  uint32_t ld_off[LPW], ld_dst[LPW];
+  bool ld_v[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int g = wave_u + kQWaves * i;
+    const int gi = g % TBLK;
+    const int pos = 64 * gi + lane;
+    const int j = pos / CPR;
+    ld_off[i] = (uint32_t)j * kstride + (((pos % CPR) ^ swz<CPR>(j)) * 16);
+    ld_v[i] = g >= TBLK;
+    ld_dst[i] = (uint32_t)((g >= TBLK ? TILE : 0) + 1024 * gi);
+  }
+  auto load_step = [&](int n) __attribute__((always_inline)) {
+    const uint32_t key0 = (uint32_t)(n * kQN) * kstride;
+    const uint32_t st = ring + (uint32_t)((n % kStages) * STAGE);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) lds_load16(ld_v[i] ? rv : rk, key0 + ld_off[i], st + ld_dst[i]);
+  };
+  if (n_steps > 0) load_step(0);
+  if (n_steps > 1) load_step(1);
+
+  // per-lane LDS offsets: row-wise A reads of K and V (row l32, chunk 2 ks + h32), and the
+  // transposed K reads (as the V^T reads of the forward kernel)
+  const uint32_t k_lane = l32 * RB + ((h32 ^ swz<CPR>(l32)) * 16);
+  const int g16 = (lane >> 4) & 1;
+  const int s16 = lane & 15;
+  const int t_row0 = 4 * h32 + (s16 >> 2);
+  const int t_part = 2 * g16 + ((s16 & 3) >> 1);
+  const uint32_t t_lane0 = t_row0 * RB + ((t_part ^ swz<CPR>(t_row0)) * 16) + 8 * (s16 & 1);
+  const uint32_t t_lane1 = (t_row0 + 8) * RB + ((t_part ^ swz<CPR>(t_row0 + 8)) * 16) + 8 * (s16 & 1);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  const float sl2 = p.scale_log2;
+
+  for (int n = 0; n < n_steps; ++n) {
+    if (n + 1 < n_steps)
+      wait_vmcnt<LPW>();
+    else
+      wait_vmcnt<0>();
+    phase_barrier();  // tile n is in LDS for every wave; stage (n + 2) % 3 is free
+    if (n + 2 < n_steps) load_step(n + 2);
+    const int kb = n * kQN;
+    if (!wave_on || kb > wave_max) continue;  // no row of this wave sees a key of the tile
+    const uint32_t st = ring + (uint32_t)((n % kStages) * STAGE);
+
+    // S^T = K Q^T and dP^T = V dO^T: element r of block kb2 is key kb + 32 kb2 + 4 h32 +
+    // 8 (r / 4) + r % 4, row qi
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      s[kb2] = f32x16{};
+      dp[kb2] = f32x16{};
+      const uint32_t kr = st + k_lane + (uint32_t)(32 * kb2 * RB);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const i32x4 a = *(const lds_i32x4*)(uintptr_t)(kr ^ (32 * ks));
+        s[kb2] = T::mma(a, qf[ks], s[kb2]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const i32x4 a = *(const lds_i32x4*)(uintptr_t)((kr + TILE) ^ (32 * ks));
+        dp[kb2] = T::mma(a, dof[ks], dp[kb2]);
+      }
+    }
+    // P = exp2(scale log2(e) s - lse2) (0 where masked), dS = P (dP - delta), packed
+    const bool special = kb + kQN - 1 > wave_lim;
+    const int lim = lim_q - kb - 4 * h32;
+    uint32_t pk[8 * 2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      float d[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][e], sl2, -lse2));
+        if (special) pr = 32 * kb2 + 8 * (e >> 2) + (e & 3) <= lim ? pr : 0.0f;
+        d[e] = pr * (dp[kb2][e] - delta);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pk[8 * kb2 + i] = T::pack(d[2 * i], d[2 * i + 1]);
+    }
+    // dQ^T += K^T dS^T, 16 keys per MFMA
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const i32x4 bp = {(int)pk[4 * c], (int)pk[4 * c + 1], (int)pk[4 * c + 2], (int)pk[4 * c + 3]};
+      const uint32_t rows = (uint32_t)(16 * c * RB);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] = T::mma(read_tr(st + t_lane0, st + t_lane1, db, rows), bp, acc[db]);
+    }
+  }
+
+  // dQ = scale * acc: lane holds row qi (rows past the sequence are dropped by the descriptor)
+  if (!wave_on) return;
+  const uint32_t at = (uint32_t)qi * qstride + (uint32_t)h * RB;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) store_block<DT>(acc[db], p.scale, rdq, at + 64 * db, h32);
+}
+
+// ------------------------------------------------------------------------------------------
+// dK/dV kernel: grid = B * H_kv * n_tiles workgroups of kKvThreads
+// ------------------------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
+  constexpr int E = 2;
+  constexpr int RB = D * E;
+  constexpr int CPR = RB / 16;
+  constexpr int TILE = kKvM * RB;    // bytes per Q or dO tile
+  constexpr int TBLK = TILE / 1024;
+  constexpr int LPW = 2 * TBLK / kKvWaves;  // Q and dO loads per wave per step
+  constexpr int AUXW = 1024;                // a wave's copy of the step's statistics block
+  constexpr int STAGE = 2 * TILE + kKvWaves * AUXW;
+  constexpr int NLD = LPW + 1;              // loads per wave per step
+  constexpr int KS = D / 16;
+  constexpr int NDB = D / 32;
+  static_assert(TILE % 1024 == 0 && (2 * TBLK) % kKvWaves == 0 && LPW >= 1, "whole loads per wave");
+  static_assert(NLD < 32, "vmcnt range");
+  typedef Elem<DT> T;
+
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * STAGE];
+  const uint32_t ring = (uint32_t)(uintptr_t)(lds_void*)lds;
+
+  const int lane = threadIdx.x & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int l32 = lane & 31;
+  const int h32 = lane >> 5;
+
+  int bkv, grp;
+  decode_unit(p, p.B * p.H_kv, &bkv, &grp);
+  const int b = bkv / p.H_kv;
+  const int kvh = bkv - b * p.H_kv;
+  const Seq sq = seq_bounds(p, b);
+  const int kb0 = grp * kKvN;  // key tile 0 sees the most rows: heaviest first
+  if (kb0 >= sq.Sk_b) return;
+  const int off = p.qend ? sq.Sk_b - sq.Sq_b : 0;
+  const int kw0 = kb0 + 32 * wave_u;  // this wave's keys
+  const int key = kw0 + l32;          // this lane's key
+  // rows below kb0 - off see no key of the workgroup
+  const int qt_first = p.causal ? max(0, kb0 - off) / kKvM : 0;
+  const int n_qt = (sq.Sq_b + kKvM - 1) / kKvM;
+  const int nq = max(0, n_qt - qt_first);
+  const int n_steps = nq * p.group;
+
+  const uint32_t qstride = (uint32_t)p.H * RB;
+  const uint32_t kstride = (uint32_t)p.H_kv * RB;
+  const size_t q_base = (size_t)sq.q_row0 * qstride;
+  const size_t k_base = ((size_t)sq.k_row0 * p.H_kv + kvh) * RB;
+  const uint32_t q_bytes = sq.Sq_b > 0 ? (uint32_t)sq.Sq_b * qstride : 0;
+  const uint32_t k_bytes = sq.Sk_b > 0 ? (uint32_t)(sq.Sk_b - 1) * kstride + RB : 0;
+  const i32x4 rq = make_rsrc_words((const char*)p.q + q_base, q_bytes);
+  const i32x4 rdo = make_rsrc_words((const char*)p.dout + q_base, q_bytes);
+  const i32x4 raux = make_rsrc_words(p.aux, p.aux_bytes);
+  const auto rk = make_rsrc((const char*)p.k + k_base, k_bytes);
+  const auto rv = make_rsrc((const char*)p.v + k_base, k_bytes);
+  const auto rdk = make_rsrc((const char*)p.dk + k_base, k_bytes);
+  const auto rdv = make_rsrc((const char*)p.dv + k_base, k_bytes);
+
+  // the wave's K and V rows as B operands (key l32, dims 16 ks + 8 h32 ..); keys past the
+  // sequence read 0 (their columns are never stored)
+  i32x4 kf[KS], vf[KS];
+  const uint32_t frag = (uint32_t)key * kstride + 16 * h32;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = load_b128(rk, frag + 32 * ks);
+    vf[ks] = load_b128(rv, frag + 32 * ks);
+  }
+
+  // tile loads: load g of a step (0 .. 2 TBLK - 1; Q first, then dO) is wave g % kKvWaves's;
+  // each wave also copies the step's statistics block into its own 1 KiB of the stage
+  uint32_t ld_off[LPW], ld_dst[LPW];
+  bool ld_do[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int g = wave_u + kKvWaves * i;
+    const int gi = g % TBLK;
+    const int pos = 64 * gi + lane;
+    const int j = pos / CPR;
+    ld_off[i] = (uint32_t)j * qstride + (((pos % CPR) ^ swz<CPR>(j)) * 16);
+    ld_do[i] = g >= TBLK;
+    ld_dst[i] = (uint32_t)((g >= TBLK ? TILE : 0) + 1024 * gi);
+  }
+  const int aux_b = aux_seq_base(p, b, sq.q_row0);
+  const uint32_t aux_dst = (uint32_t)(2 * TILE + wave_u * AUXW);
+  auto load_step = [&](int t) __attribute__((always_inline)) {
+    const int hi = t / nq;
+    const int qt = qt_first + t - hi * nq;
+    const int hq = kvh * p.group + hi;
+    const uint32_t base = (uint32_t)(qt * kKvM) * qstride + (uint32_t)hq * RB;
+    const uint32_t st = ring + (uint32_t)((t % kStages) * STAGE);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) lds_load16(ld_do[i] ? rdo : rq, base + ld_off[i], st + ld_dst[i]);
+    const uint32_t blk = (uint32_t)(aux_b + hq * p.aux_hstride + qt);
+    lds_load16(raux, blk * kAuxBlock + 16 * lane, st + aux_dst);
+  };
+  if (n_steps > 0) load_step(0);
+  if (n_steps > 1) load_step(1);
+
+  // per-lane LDS offsets: row-wise A reads of Q and dO, transposed reads of both
+  const uint32_t r_lane = l32 * RB + ((h32 ^ swz<CPR>(l32)) * 16);
+  const int g16 = (lane >> 4) & 1;
+  const int s16 = lane & 15;
+  const int t_row0 = 4 * h32 + (s16 >> 2);
+  const int t_part = 2 * g16 + ((s16 & 3) >> 1);
+  const uint32_t t_lane0 = t_row0 * RB + ((t_part ^ swz<CPR>(t_row0)) * 16) + 8 * (s16 & 1);
+  const uint32_t t_lane1 = (t_row0 + 8) * RB + ((t_part ^ swz<CPR>(t_row0 + 8)) * 16) + 8 * (s16 & 1);
+
+  f32x16 acc_k[NDB], acc_v[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    acc_k[db] = f32x16{};
+    acc_v[db] = f32x16{};
+  }
+  const float sl2 = p.scale_log2;
+
+  for (int t = 0; t < n_steps; ++t) {
+    if (t + 1 < n_steps)
+      wait_vmcnt<NLD>();
+    else
+      wait_vmcnt<0>();
+    phase_barrier();  // step t is in LDS for every wave; stage (t + 2) % 3 is free
+    if (t + 2 < n_steps) load_step(t + 2);
+    const int hi = t / nq;
+    const int q0 = (qt_first + t - hi * nq) * kKvM;
+    if (p.causal && q0 + kKvM - 1 + off < kw0) continue;  // no row of the tile sees the wave's keys
+    const uint32_t st = ring + (uint32_t)((t % kStages) * STAGE);
+
+    // S = Q K^T and dP = dO V^T: element r of block qb is row q0 + 32 qb + 4 h32 + 8 (r / 4) +
+    // r % 4, key `key`
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      s[qb] = f32x16{};
+      dp[qb] = f32x16{};
+      const uint32_t rr = st + r_lane + (uint32_t)(32 * qb * RB);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const i32x4 a = *(const lds_i32x4*)(uintptr_t)(rr ^ (32 * ks));
+        s[qb] = T::mma(a, kf[ks], s[qb]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const i32x4 a = *(const lds_i32x4*)(uintptr_t)((rr + TILE) ^ (32 * ks));
+        dp[qb] = T::mma(a, vf[ks], dp[qb]);
+      }
+    }
+    // P and dS with the rows' statistics (padding rows: lse2 = +inf, delta = 0, so P = 0)
+    const bool special = p.causal && q0 < kw0 + 31 - off;
+    const int lim = key - off - q0 - 4 * h32;  // keep element r iff 32 qb + 8 (r / 4) + r % 4 >= lim
+    const uint32_t sa = st + aux_dst;
+    uint32_t pp[16], pd[16];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t ra = sa + 4 * (32 * qb + 8 * g + 4 * h32);
+        const i32x4 l4 = *(const lds_i32x4*)(uintptr_t)ra;
+        const i32x4 d4 = *(const lds_i32x4*)(uintptr_t)(ra + 4 * kAuxRows);
+        float pr[4], ds[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e = 4 * g + u;
+          pr[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][e], sl2, -__builtin_bit_cast(float, (int)l4[u])));
+          if (special) pr[u] = 32 * qb + 8 * g + u >= lim ? pr[u] : 0.0f;
+          ds[u] = pr[u] * (dp[qb][e] - __builtin_bit_cast(float, (int)d4[u]));
+        }
+        pp[8 * qb + 2 * g] = T::pack(pr[0], pr[1]);
+        pp[8 * qb + 2 * g + 1] = T::pack(pr[2], pr[3]);
+        pd[8 * qb + 2 * g] = T::pack(ds[0], ds[1]);
+        pd[8 * qb + 2 * g + 1] = T::pack(ds[2], ds[3]);
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS, 16 rows per MFMA
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const i32x4 bp = {(int)pp[4 * c], (int)pp[4 * c + 1], (int)pp[4 * c + 2], (int)pp[4 * c + 3]};
+      const i32x4 bd = {(int)pd[4 * c], (int)pd[4 * c + 1], (int)pd[4 * c + 2], (int)pd[4 * c + 3]};
+      const uint32_t rows = (uint32_t)(16 * c * RB);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        acc_v[db] = T::mma(read_tr(st + TILE + t_lane0, st + TILE + t_lane1, db, rows), bp, acc_v[db]);
+        acc_k[db] = T::mma(read_tr(st + t_lane0, st + t_lane1, db, rows), bd, acc_k[db]);
+      }
+    }
+  }
+
+  // dK = scale * acc_k, dV = acc_v: lane holds key `key` (keys past the sequence are dropped
+  // by the descriptor)
+  const uint32_t at = (uint32_t)key * kstride;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    store_block<DT>(acc_k[db], p.scale, rdk, at + 64 * db, h32);
+    store_block<DT>(acc_v[db], 1.0f, rdv, at + 64 * db, h32);
+  }
+}
+
+template <int DT, int D>
+hipError_t launch(Params p, int n_aux_tiles, int n_q_tiles, int n_k_tiles, bool have_q, bool have_k,
+                  hipStream_t stream) {
+  if (have_q) {
+    p.n_tiles = n_aux_tiles;
+    hipLaunchKernelGGL((stats_kernel<DT, D>), dim3((unsigned)(p.B * n_aux_tiles), (unsigned)p.H), dim3(256), 0,
+                       stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t pairs = (int64_t)p.B * p.H;
+    p.n_tiles = n_q_tiles;
+    p.xcd_per = pairs % 8 == 0 ? (int32_t)(pairs / 8) : 0;
+    hipLaunchKernelGGL((dq_kernel<DT, D>), dim3((unsigned)(pairs * n_q_tiles)), dim3(kQThreads), 0, stream, p);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (have_k) {
+    const int64_t pairs = (int64_t)p.B * p.H_kv;
+    p.n_tiles = n_k_tiles;
+    p.xcd_per = pairs % 8 == 0 ? (int32_t)(pairs / 8) : 0;
+    hipLaunchKernelGGL((dkdv_kernel<DT, D>), dim3((unsigned)(pairs * n_k_tiles)), dim3(kKvThreads), 0, stream, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+// Shape checks and workspace size.  Fills the layout fields of p.
+fmha_status plan(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D, const fmha_varlen* varlen,
+                 Params* p, size_t* ws_bytes) {
+  const bool packed = varlen != nullptr;
+  if (B < 0 || Sq < 0 || Sk < 0 || H < 0 || H_kv < 0) return FMHA_ERR_INVALID_SHAPE;
+  if (H > 0 && (H_kv < 1 || H % H_kv != 0)) return FMHA_ERR_INVALID_SHAPE;
+  if (D != 32 && D != 64 && D != 128) return FMHA_ERR_INVALID_SHAPE;
+  if (packed && (varlen->total_length_q < 0 || varlen->total_length_k < 0)) return FMHA_ERR_INVALID_SHAPE;
+  if (H > 65535) return FMHA_ERR_UNSUPPORTED;  // the statistics grid's y dimension
+  const int64_t rows_q = packed ? varlen->total_length_q : Sq;
+  const int64_t rows_k = packed ? varlen->total_length_k : Sk;
+  const int64_t lim = (int64_t)1 << 31;
+  // per-sequence byte offsets, up to one workgroup tile past the end, fit 31 bits
+  if ((rows_q + kQM) * H * D * 2 >= lim || (rows_k + kKvN) * H_kv * D * 2 >= lim) return FMHA_ERR_UNSUPPORTED;
+  const int64_t nqb = (Sq + kAuxRows - 1) / kAuxRows;
+  int64_t blocks;
+  if (packed) {
+    const int64_t hb = (int64_t)(varlen->total_length_q >> 6) + B + 1;
+    if (hb >= lim) return FMHA_ERR_UNSUPPORTED;
+    p->aux_hstride = (int32_t)hb;
+    p->aux_bstride = 0;
+    blocks = hb * H;
+  } else {
+    p->aux_hstride = (int32_t)nqb;
+    if (nqb * H >= lim) return FMHA_ERR_UNSUPPORTED;
+    p->aux_bstride = (int32_t)(nqb * H);
+    blocks = (int64_t)B * H * nqb;
+  }
+  // the statistics loads read one block past the last
+  if ((blocks + 1) * kAuxBlock >= lim) return FMHA_ERR_UNSUPPORTED;
+  *ws_bytes = (size_t)blocks * kAuxBlock;
+  p->B = B;
+  p->Sq = Sq;
+  p->Sk = Sk;
+  p->H = H;
+  p->H_kv = H_kv;
+  p->group = H > 0 ? H / H_kv : 1;
+  p->total_q = packed ? varlen->total_length_q : 0;
+  return FMHA_OK;
+}
+
+}  // namespace bwd
+}  // namespace fmha
+
+// --------------------------------------------------------------------------------------
+// C ABI
+// --------------------------------------------------------------------------------------
+extern "C" {
+
+size_t fmha_bwd_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
+                               const fmha_varlen* varlen) {
+  fmha::bwd::Params p;
+  size_t bytes = 0;
+  return fmha::bwd::plan(B, Sq, Sk, H, H_kv, D, varlen, &p, &bytes) == FMHA_OK ? bytes : 0;
+}
+
+fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv,
+                     int32_t D, float scale, fmha_mask mask, fmha_dtype dtype, const fmha_varlen* varlen,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  using namespace fmha::bwd;
+  const bool packed = varlen != nullptr;
+  if (packed && (!varlen->cu_seqlens_q != !varlen->cu_seqlens_k)) return FMHA_ERR_NULL_POINTER;
+  if (packed && !varlen->cu_seqlens_q) return FMHA_ERR_NULL_POINTER;
+  Params p;
+  size_t need = 0;
+  const fmha_status st = plan(B, Sq, Sk, H, H_kv, D, varlen, &p, &need);
+  if (st != FMHA_OK) return st;
+  if ((int)dtype < 0 || (int)dtype > 2) return FMHA_ERR_UNSUPPORTED;
+  if ((int)mask < 0 || (int)mask > 3) return FMHA_ERR_UNSUPPORTED;
+  if (dtype == FMHA_DTYPE_F8E4M3) return FMHA_ERR_UNSUPPORTED;  // 16-bit types only
+  const bool have_q = B > 0 && H > 0 && (packed ? varlen->total_length_q > 0 : Sq > 0);
+  const bool have_k = B > 0 && H > 0 && (packed ? varlen->total_length_k > 0 : Sk > 0);
+  if (have_q && (!q || !o || !dout || !lse || !dq)) return FMHA_ERR_NULL_POINTER;
+  if (have_k && (!k || !v || !dk || !dv)) return FMHA_ERR_NULL_POINTER;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv) & 15)
+    return FMHA_ERR_MISALIGNED;
+  if ((uintptr_t)lse & 3) return FMHA_ERR_MISALIGNED;
+  if (!(scale > 0.0f) || !isfinite(scale)) return FMHA_ERR_INVALID_ARGUMENT;
+  if (!have_q && !have_k) return FMHA_OK;
+  if (have_q || have_k) {
+    // the dK/dV kernel reads the statistics of every row it visits
+    if (have_q && !workspace) return FMHA_ERR_NULL_POINTER;
+    if ((uintptr_t)workspace & 15) return FMHA_ERR_MISALIGNED;
+    if (have_q && workspace_bytes < need) return FMHA_ERR_INVALID_ARGUMENT;
+  }
+  const int64_t n_aux = (Sq + kAuxRows - 1) / kAuxRows;
+  const int64_t n_q = (Sq + kQM - 1) / kQM;
+  const int64_t n_k = (Sk + kKvN - 1) / kKvN;
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)B * n_aux >= lim || (int64_t)B * H * n_q >= lim || (int64_t)B * H_kv * n_k >= lim)
+    return FMHA_ERR_UNSUPPORTED;
+
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.aux = (float*)workspace;
+  p.aux_bytes = (uint32_t)need;
+  p.cu_q = packed ? varlen->cu_seqlens_q : nullptr;
+  p.cu_k = packed ? varlen->cu_seqlens_k : nullptr;
+  p.causal = mask == FMHA_MASK_CAUSAL_QBEGIN || mask == FMHA_MASK_CAUSAL_QEND;
+  p.qend = mask == FMHA_MASK_CAUSAL_QEND;
+  p.scale = scale;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.xcd_per = 0;
+  p.n_tiles = 0;
+
+  hipError_t err = hipSuccess;
+  const int a = (int)n_aux, nq = (int)n_q, nk = (int)n_k;
+  if (dtype == FMHA_DTYPE_BF16) {
+    if (D == 32) err = launch<fmha::kBF16, 32>(p, a, nq, nk, have_q, have_k, stream);
+    if (D == 64) err = launch<fmha::kBF16, 64>(p, a, nq, nk, have_q, have_k, stream);
+    if (D == 128) err = launch<fmha::kBF16, 128>(p, a, nq, nk, have_q, have_k, stream);
+  } else {
+    if (D == 32) err = launch<fmha::kF16, 32>(p, a, nq, nk, have_q, have_k, stream);
+    if (D == 64) err = launch<fmha::kF16, 64>(p, a, nq, nk, have_q, have_k, stream);
+    if (D == 128) err = launch<fmha::kF16, 128>(p, a, nq, nk, have_q, have_k, stream);
+  }
+  return err == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
+}
+
+}  // extern "C"

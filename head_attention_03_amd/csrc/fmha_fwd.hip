@@ -832,7 +832,7 @@ const char* fmha_status_string(fmha_status s) {
   return "unknown status";
 }
 
-int32_t fmha_version(void) { return 100; }
+int32_t fmha_version(void) { return 200; }
 
 fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Sq,
                      int32_t Sk, int32_t H, int32_t H_kv, int32_t D, float scale, fmha_mask mask, fmha_dtype dtype,

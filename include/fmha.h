@@ -1,5 +1,6 @@
 /*
- * fmha.h -- fused multi-head attention forward pass on AMD Instinct MI355X (gfx950).
+ * fmha.h -- fused multi-head attention on AMD Instinct MI355X (gfx950): forward pass
+ * (fmha_fwd, fmha_fwd_splitkv) and backward pass (fmha_bwd).
  *
  * C ABI of libfmha.so.  One call computes, for every sequence b, query head h and
  * query row i,
@@ -155,6 +156,55 @@ fmha_status fmha_fwd_splitkv(const void* q, const void* k, const void* v, void* 
  * shape, or a shape too large for the kernel's 32-bit offsets. */
 size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
                                        const fmha_varlen* varlen);
+
+/*
+ * fmha_bwd -- enqueue the backward pass of fmha_fwd (o_scale 1): the gradients dq, dk, dv of
+ * the forward's output for an upstream gradient dout,
+ *
+ *     P = exp(scale * Q K^T + mask - LSE)            (recomputed from the forward's LSE)
+ *     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta),  delta_i = sum_d O_id dO_id,
+ *     dQ = scale * dS K,  dK = scale * dS^T Q,
+ *
+ * per (sequence, head), after the backward of the CUTLASS Blackwell FMHA example (trdm.cn
+ * walk-through "CUTLASS Blackwell FMHA 示例完全解析", section "FMHA for Blackwell: Backward":
+ * a row sum of O * dO, the main dQ/dK/dV pass, dQ converted to the output type; masks as that
+ * section's backward mask, i.e. the forward masks).  Three kernels run on `stream`: the row
+ * statistics, dQ, and dK/dV.  No atomics: results are bitwise repeatable.  With GQA/MQA
+ * (H_kv < H), dk and dv of a K/V head are the sums over its group of query heads (the
+ * CUTLASS backward does not support GQA; this is the gradient of the shared head).
+ *
+ *   q, k, v, o   the forward's inputs and output (o written by fmha_fwd with o_scale 1)
+ *   dout         dO, same shape and type as o
+ *   lse          the forward's fp32 LSE (natural log), layout as in fmha_fwd; required
+ *   dq           same shape as q, written
+ *   dk, dv       same shapes as k and v, written (keys that no query sees get 0)
+ *   B, Sq, Sk, H, H_kv, D, scale, mask, varlen   as in fmha_fwd
+ *   dtype        FMHA_DTYPE_F16 or FMHA_DTYPE_BF16 (fp8: FMHA_ERR_UNSUPPORTED); every tensor
+ *                above except lse has this type
+ *   workspace    device memory owned by the caller, 16-byte aligned, at least
+ *                fmha_bwd_workspace_size(...) bytes for the same shape; contents on entry do
+ *                not matter (calls that overlap in time must not share it).  It holds 8 bytes of
+ *                row statistics per query row and head, in blocks of 64 rows.
+ *   workspace_bytes  its size
+ * The gradients are computed in fp32 with the probabilities and dS rounded to dtype for the
+ * matrix cores, and written rounded to nearest even.
+ * Errors as fmha_fwd (o, dout, lse and dq are required when there are query rows; k, v, dk and
+ * dv when there are keys; all but lse 16-byte aligned), and: workspace NULL ->
+ * FMHA_ERR_NULL_POINTER, not 16-byte aligned -> FMHA_ERR_MISALIGNED, smaller than needed ->
+ * FMHA_ERR_INVALID_ARGUMENT (checked when there are query rows), H > 65535 ->
+ * FMHA_ERR_UNSUPPORTED.  With query rows but no keys dq is zeroed; with keys but no query rows
+ * dk and dv are zeroed.  Rows and keys outside the sequences are never touched.
+ */
+fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv,
+                     int32_t D, float scale, fmha_mask mask, fmha_dtype dtype, const fmha_varlen* varlen,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes fmha_bwd needs for this shape (host arithmetic only; the packed form reads
+ * only varlen->total_length_q).  Returns 0 for an invalid shape, or one too large for the
+ * kernels' 32-bit offsets. */
+size_t fmha_bwd_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
+                               const fmha_varlen* varlen);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fmha_status_string(fmha_status status);

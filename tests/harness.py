@@ -155,3 +155,96 @@ def compare(name: str, got_bits: np.ndarray, dtype: str, expected: np.ndarray, g
     if rel_bound is not None and got.size:
         assert rel <= rel_bound, msg + f" (relative Frobenius bound {rel_bound:.3e})"
     return err
+
+
+# ----------------------------------------------------------------------------------------------
+# backward (fmha_bwd)
+# ----------------------------------------------------------------------------------------------
+# Gradient tolerance, relative to the largest |gradient| of the tensor and counted beyond each
+# element's own rounding to the output format.  The kernels round P and dS to the 16-bit type for
+# the matrix cores and form delta from the 16-bit O; an fp64 emulation of exactly those roundings
+# at these shapes stays within 3.1e-3 max|ref| (bf16) and 5e-4 (fp16), and fp32 accumulation adds
+# far less, so 1e-2 leaves a factor of three.  Where the exact gradient cancels to 0 (a row with
+# one visible key has dP - delta = 0), the scale is taken as 2^-8, the 16-bit rounding of the O(1)
+# terms that cancel (delta is formed from the rounded O).
+BWD_TOL = 1e-2
+BWD_SCALE_FLOOR = 2.0 ** -8
+# Sentinel written around packed gradients: the kernels must not touch rows outside the sequences.
+GRAD_SENTINEL = {"f16": 0x7BAD, "bf16": 0x4B1D}
+
+
+def oracle_forward_inputs(inp):
+    """O (rounded to the input type) and fp32 LSE from the oracle, as the backward's inputs."""
+    if isinstance(inp, VarlenInputs):
+        o, lse = oracle_varlen(inp)
+    else:
+        o, lse = oracle_dense(inp)
+    o_t = torch.from_numpy(o.astype(np.float32)).to(TORCH_DTYPES[inp.dtype])
+    return o_t, lse.astype(np.float32)
+
+
+def _bwd_workspace(need: int):
+    return _workspace(need)
+
+
+def run_bwd_dense(inp: DenseInputs, do: torch.Tensor, o: torch.Tensor, lse: np.ndarray, stream=None):
+    """dQ, dK, dV (CPU tensors) from fmha_bwd; o and lse are the forward's outputs (CPU)."""
+    dev = torch.device("cuda:0")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    o_d, do_d = o.to(dev), do.to(dev)
+    lse_d = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = fmha.fmha_bwd_workspace_size(inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D, None)
+    ws = _bwd_workspace(need)
+    st = fmha.fmha_bwd(q, k, v, o_d, do_d, lse_d, dq, dk, dv, inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D,
+                       inp.kernel_scale, inp.mask, inp.dtype, None, ws, need,
+                       stream if stream is not None else torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return st, dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def run_bwd_varlen(inp: VarlenInputs, do_buf: torch.Tensor, o: torch.Tensor, lse: np.ndarray):
+    """Packed backward.  do_buf holds pad_q leading rows like q_buf; o and lse cover the packed rows.
+
+    Returns the status and the whole dQ, dK, dV buffers (padding included, sentinel-initialised).
+    """
+    dev = torch.device("cuda:0")
+    q_buf, k_buf, v_buf = inp.q_buf.to(dev), inp.k_buf.to(dev), inp.v_buf.to(dev)
+    o_buf = torch.zeros_like(inp.q_buf)
+    o_buf[inp.pad_q:] = o
+    o_buf, do_d = o_buf.to(dev), do_buf.to(dev)
+    lse_d = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32).reshape(inp.H, -1)).to(dev)
+    bits = GRAD_SENTINEL[inp.dtype]
+    dq = torch.full(q_buf.shape, bits, dtype=torch.int16).view(TORCH_DTYPES[inp.dtype]).to(dev)
+    dk = torch.full(k_buf.shape, bits, dtype=torch.int16).view(TORCH_DTYPES[inp.dtype]).to(dev)
+    dv = torch.full(v_buf.shape, bits, dtype=torch.int16).view(TORCH_DTYPES[inp.dtype]).to(dev)
+    cu_q = torch.from_numpy(inp.cu_q).to(dev)
+    cu_k = torch.from_numpy(inp.cu_k).to(dev)
+    vl = fmha.make_varlen(cu_q, cu_k, inp.total_q, inp.total_k)
+    need = fmha.fmha_bwd_workspace_size(inp.B, inp.max_q, inp.max_k, inp.H, inp.H_kv, inp.D, vl)
+    ws = _bwd_workspace(need)
+    pq, pk = inp.pad_q, inp.pad_k
+    st = fmha.fmha_bwd(q_buf[pq:], k_buf[pk:], v_buf[pk:], o_buf[pq:], do_d[pq:], lse_d, dq[pq:], dk[pk:], dv[pk:],
+                       inp.B, inp.max_q, inp.max_k, inp.H, inp.H_kv, inp.D, inp.kernel_scale, inp.mask, inp.dtype, vl,
+                       ws, need, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return st, dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def compare_grad(name: str, got: torch.Tensor, dtype: str, expected: np.ndarray, tol: float = BWD_TOL) -> float:
+    """Element-by-element check of a gradient against the oracle's fp64 value; returns the error."""
+    g = oracle.decode(to_bits(got), dtype)
+    assert g.shape == expected.shape, (g.shape, expected.shape)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite gradients"
+    if not g.size:
+        return 0.0
+    best = oracle.decode(_round_to(expected, dtype), dtype)
+    beyond = float((np.abs(g - expected) - np.abs(best - expected)).max())
+    mx = float(np.abs(expected).max())
+    bound = tol * max(mx, BWD_SCALE_FLOOR)
+    rel = float(np.linalg.norm(g - expected) / max(np.linalg.norm(expected), 1e-30))
+    msg = (f"{name}: max|ref| {mx:.3e}, max|err| beyond the format rounding {beyond:.3e} (bound {bound:.3e}), "
+           f"rel fro {rel:.3e}")
+    log(msg)
+    assert beyond <= bound, msg
+    return beyond

@@ -123,3 +123,47 @@ def test_splitkv_workspace_size_packed_uses_total_rows():
     need = fmha.fmha_fwd_splitkv_workspace_size(3, 4, 3000, 8, 2, 64, vl)
     assert need > 0 and need % (7 * 8 * 65 * 4) == 0
     assert fmha.fmha_fwd_splitkv_workspace_size(3, 4, 3000, 6, 4, 64) == 0  # H % H_kv != 0
+
+
+# ----------------------------------------------------------------------------------------------
+# fmha_bwd: host validation and workspace size
+# ----------------------------------------------------------------------------------------------
+def call_bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=1, Sq=16, Sk=16, H=2, H_kv=1, D=64, scale=0.125,
+             mask="causal_qbegin", dtype="bf16", varlen=None, workspace=P, workspace_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return fmha.fmha_bwd(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(dout=None), 1), (dict(lse=None), 1), (dict(dq=None), 1),
+    (dict(k=None), 1), (dict(v=None), 1), (dict(dk=None), 1), (dict(dv=None), 1), (dict(workspace=None), 1),
+    (dict(varlen=fmha.make_varlen(P, None, 16, 16)), 1), (dict(varlen=fmha.make_varlen(None, None, 16, 16)), 1),
+    (dict(B=-1), 2), (dict(Sk=-1), 2), (dict(H=3, H_kv=2), 2), (dict(H_kv=0), 2), (dict(D=48), 2),
+    (dict(varlen=fmha.make_varlen(P, P, 16, -1)), 2),
+    (dict(dtype="f8e4m3"), 3), (dict(dtype=3), 3), (dict(mask=4), 3), (dict(mask=-1), 3),
+    (dict(H=70000, H_kv=70000, Sq=1, Sk=1), 3), (dict(Sq=1 << 22, H=64, H_kv=64, D=128), 3),
+    (dict(q=P + 2), 4), (dict(dq=P + 8), 4), (dict(dk=P + 4), 4), (dict(dout=P + 2), 4), (dict(lse=P + 2), 4),
+    (dict(workspace=P + 8), 4),
+    (dict(scale=0.0), 5), (dict(scale=float("inf")), 5), (dict(scale=float("nan")), 5), (dict(workspace_bytes=0), 5),
+    # no query rows: the q-side pointers and the workspace are not needed; no keys: the k side
+    (dict(B=0, q=None, k=None, workspace=None), 0),
+])
+def test_bwd_rejects_bad_arguments(kw, status):
+    assert call_bwd(**kw) == status
+
+
+def test_bwd_workspace_size():
+    # dense: 512 bytes per 64-row block of every (sequence, head)
+    assert fmha.fmha_bwd_workspace_size(4, 2048, 2048, 16, 16, 128, None) == 4 * 16 * 32 * 512
+    assert fmha.fmha_bwd_workspace_size(2, 65, 10, 3, 1, 64, None) == 2 * 3 * 2 * 512
+    assert fmha.fmha_bwd_workspace_size(1, 0, 10, 3, 1, 64, None) == 0
+    # packed: per head, floor(total_q / 64) + B + 1 blocks (sequences start on their own block)
+    vl = fmha.make_varlen(P, P, 1000, 50)
+    assert fmha.fmha_bwd_workspace_size(5, 400, 30, 4, 2, 128, vl) == 4 * (1000 // 64 + 5 + 1) * 512
+    # invalid shapes
+    assert fmha.fmha_bwd_workspace_size(1, 16, 16, 3, 2, 64, None) == 0
+    assert fmha.fmha_bwd_workspace_size(1, 16, 16, 2, 2, 48, None) == 0
+    # one byte short of the size is rejected
+    need = fmha.fmha_bwd_workspace_size(1, 16, 16, 2, 1, 64, None)
+    assert call_bwd(workspace_bytes=need - 1) == 5

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the attention forward pass.
+"""Seeded synthetic inputs for the attention forward and backward passes.
 
 This module only draws and encodes inputs (random normals, lengths, fp8 per-tensor
 quantisation, padding and sentinels). It holds none of the attention arithmetic,
@@ -10,6 +10,7 @@ from .synth import (  # noqa: F401
     VarlenInputs,
     config_seed,
     draw_normal,
+    make_grad,
     make_dense,
     make_varlen,
     make_config,

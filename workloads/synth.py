@@ -216,6 +216,12 @@ def make_dense(seed: int, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int, d
                        scale=float(scale), o_scale=float(o_scale), seed=seed, q_scale=sq, k_scale=sk, v_scale=sv)
 
 
+def make_grad(seed: int, shape: Sequence[int], dtype: str) -> torch.Tensor:
+    """Upstream gradient dO for the backward pass: N(0, 1) float32 from its own stream, cast to dtype."""
+    t, _ = _to_storage(draw_normal(np.random.default_rng(seed), shape), dtype)
+    return t
+
+
 def make_varlen(seed: int, seqlens_q: Sequence[int], seqlens_k: Sequence[int], H: int, H_kv: int, D: int,
                 dtype: str, mask: str = "none", scale: Optional[float] = None, o_scale: float = 1.0,
                 poison_pads: bool = False, rng: Optional[np.random.Generator] = None) -> VarlenInputs:
@@ -260,7 +266,8 @@ def make_varlen(seed: int, seqlens_q: Sequence[int], seqlens_k: Sequence[int], H
 
 
 # The measured workloads.  Config 4 is run twice on the same inputs (residual, then causal-qend);
-# config 6 is the split-KV (decode) entry point's workload.
+# config 6 is the split-KV (decode) entry point's workload; config 7 is the backward pass (fmha_bwd)
+# of config 2's shape.
 CONFIGS = {
     1: dict(name="tiny dense fp16 D64 no mask", kind="dense", B=1, H=2, H_kv=2, Sq=128, Sk=128, D=64,
             dtype="f16", mask="none", lse=False, o_scale=1.0),
@@ -277,6 +284,9 @@ CONFIGS = {
     # 8192-key cache, GQA 32/8 (one query row per head: no mask and causal-qend coincide).
     6: dict(name="decode GQA bf16 D128, 1 token vs 8192 keys (split-KV)", kind="dense", entry="splitkv", B=16,
             H=32, H_kv=8, Sq=1, Sk=8192, D=128, dtype="bf16", mask="none", lse=True, o_scale=1.0),
+    # Backward of the prefill workload: dQ, dK, dV for a N(0, 1) upstream gradient (fmha_bwd).
+    7: dict(name="backward of prefill causal-qbegin bf16 D128", kind="dense", entry="bwd", B=4, H=16, H_kv=16,
+            Sq=2048, Sk=2048, D=128, dtype="bf16", mask="causal_qbegin", lse=True, o_scale=1.0),
 }
 
 
