@@ -59,6 +59,10 @@ constexpr int kQThreads = 64 * kQWaves;
 constexpr int kQM = 32 * kQWaves;       // query rows per workgroup
 constexpr int kQN = 64;                 // keys per streamed tile
 
+constexpr int kSchedMfma = 0x008;  // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedDsRead = 0x100;
+constexpr int kPrefetch = 6;       // LDS reads kept in flight ahead of the MFMAs
+
 struct Params {
   const void* q;
   const void* k;
@@ -156,6 +160,30 @@ __device__ inline void store_block(const f32x16& a, float f, __amdgpu_buffer_rsr
                                                T::pack(a[4 * g1 + 2] * f, a[4 * g1 + 3] * f), false, false);
     const i32x4 w = {(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]};
     __builtin_amdgcn_raw_buffer_store_b128(w, r, at + (uint32_t)(16 * gp + 8 * h32) * 2, 0, 0);
+  }
+}
+
+// NC chains of v_mfma_f32_32x32x16 over the head dimension, interleaved: c[j] += sum_ks
+// A_j[ks] B_j[ks], A_j[ks] the 16-byte row-wise LDS read at base[j] ^ (32 ks) (chunk 2 ks + h32 of
+// the lane's row) and B_j = bj[ks] (j = 0, 2 take b0; 1, 3 take b1).  The reads run kPrefetch
+// ahead of their MFMAs (pinned with scheduling groups: left alone, the compiler waits for each
+// read right before its MFMA, and the matrix core idles for the LDS latency).
+template <int DT, int KS, int NC>
+__device__ inline void row_chains(f32x16 (&c)[NC], const uint32_t (&base)[NC], const i32x4 (&b0)[KS],
+                                  const i32x4 (&b1)[KS]) {
+  typedef Elem<DT> T;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const i32x4 a = *(const lds_i32x4*)(uintptr_t)(base[j] ^ (32 * ks));
+      c[j] = T::mma(a, (j & 1) ? b1[ks] : b0[ks], c[j]);
+    }
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
+#pragma unroll
+  for (int i = 0; i < NC * KS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
   }
 }
 
@@ -331,23 +359,13 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_kernel(const Params p) {
 
     // S^T = K Q^T and dP^T = V dO^T: element r of block kb2 is key kb + 32 kb2 + 4 h32 +
     // 8 (r / 4) + r % 4, row qi
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      s[kb2] = f32x16{};
-      dp[kb2] = f32x16{};
-      const uint32_t kr = st + k_lane + (uint32_t)(32 * kb2 * RB);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const i32x4 a = *(const lds_i32x4*)(uintptr_t)(kr ^ (32 * ks));
-        s[kb2] = T::mma(a, qf[ks], s[kb2]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const i32x4 a = *(const lds_i32x4*)(uintptr_t)((kr + TILE) ^ (32 * ks));
-        dp[kb2] = T::mma(a, dof[ks], dp[kb2]);
-      }
+    f32x16 c4[4] = {};  // S^T block 0, dP^T block 0, S^T block 1, dP^T block 1
+    {
+      const uint32_t k0 = st + k_lane, k1 = k0 + (uint32_t)(32 * RB);
+      const uint32_t base[4] = {k0, k0 + TILE, k1, k1 + TILE};
+      row_chains<DT, KS, 4>(c4, base, qf, dof);
     }
+    const f32x16 s[2] = {c4[0], c4[2]}, dp[2] = {c4[1], c4[3]};
     // P = exp2(scale log2(e) s - lse2) (0 where masked), dS = P (dP - delta), packed
     const bool special = kb + kQN - 1 > wave_lim;
     const int lim = lim_q - kb - 4 * h32;
@@ -364,13 +382,19 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_kernel(const Params p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) pk[8 * kb2 + i] = T::pack(d[2 * i], d[2 * i + 1]);
     }
-    // dQ^T += K^T dS^T, 16 keys per MFMA
+    // dQ^T += K^T dS^T, 16 keys per MFMA (two transposed reads each, kept ahead of the MFMAs)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const i32x4 bp = {(int)pk[4 * c], (int)pk[4 * c + 1], (int)pk[4 * c + 2], (int)pk[4 * c + 3]};
       const uint32_t rows = (uint32_t)(16 * c * RB);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[db] = T::mma(read_tr(st + t_lane0, st + t_lane1, db, rows), bp, acc[db]);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * NDB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
   }
 
@@ -510,30 +534,22 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
 
     // S = Q K^T and dP = dO V^T: element r of block qb is row q0 + 32 qb + 4 h32 + 8 (r / 4) +
     // r % 4, key `key`
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = f32x16{};
-      dp[qb] = f32x16{};
-      const uint32_t rr = st + r_lane + (uint32_t)(32 * qb * RB);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const i32x4 a = *(const lds_i32x4*)(uintptr_t)(rr ^ (32 * ks));
-        s[qb] = T::mma(a, kf[ks], s[qb]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const i32x4 a = *(const lds_i32x4*)(uintptr_t)((rr + TILE) ^ (32 * ks));
-        dp[qb] = T::mma(a, vf[ks], dp[qb]);
-      }
-    }
-    // P and dS with the rows' statistics (padding rows: lse2 = +inf, delta = 0, so P = 0)
+    // Per 32-row half qb of the tile: S and dP, then P and dS with the rows' statistics
+    // (padding rows: lse2 = +inf, delta = 0, so P = 0), then dV^T += dO^T P and dK^T += Q^T dS
+    // over the half's 32 rows.  Element r of a half's blocks is row q0 + 32 qb + 4 h32 +
+    // 8 (r / 4) + r % 4, key `key`.
     const bool special = p.causal && q0 < kw0 + 31 - off;
     const int lim = key - off - q0 - 4 * h32;  // keep element r iff 32 qb + 8 (r / 4) + r % 4 >= lim
     const uint32_t sa = st + aux_dst;
-    uint32_t pp[16], pd[16];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+      f32x16 c2[2] = {};  // S, dP
+      {
+        const uint32_t r0 = st + r_lane + (uint32_t)(32 * qb * RB);
+        const uint32_t base[2] = {r0, r0 + TILE};
+        row_chains<DT, KS, 2>(c2, base, kf, vf);
+      }
+      uint32_t pp[8], pd[8];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const uint32_t ra = sa + 4 * (32 * qb + 8 * g + 4 * h32);
@@ -543,26 +559,31 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int e = 4 * g + u;
-          pr[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][e], sl2, -__builtin_bit_cast(float, (int)l4[u])));
+          pr[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(c2[0][e], sl2, -__builtin_bit_cast(float, (int)l4[u])));
           if (special) pr[u] = 32 * qb + 8 * g + u >= lim ? pr[u] : 0.0f;
-          ds[u] = pr[u] * (dp[qb][e] - __builtin_bit_cast(float, (int)d4[u]));
+          ds[u] = pr[u] * (c2[1][e] - __builtin_bit_cast(float, (int)d4[u]));
         }
-        pp[8 * qb + 2 * g] = T::pack(pr[0], pr[1]);
-        pp[8 * qb + 2 * g + 1] = T::pack(pr[2], pr[3]);
-        pd[8 * qb + 2 * g] = T::pack(ds[0], ds[1]);
-        pd[8 * qb + 2 * g + 1] = T::pack(ds[2], ds[3]);
+        pp[2 * g] = T::pack(pr[0], pr[1]);
+        pp[2 * g + 1] = T::pack(pr[2], pr[3]);
+        pd[2 * g] = T::pack(ds[0], ds[1]);
+        pd[2 * g + 1] = T::pack(ds[2], ds[3]);
       }
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS, 16 rows per MFMA
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const i32x4 bp = {(int)pp[4 * c], (int)pp[4 * c + 1], (int)pp[4 * c + 2], (int)pp[4 * c + 3]};
-      const i32x4 bd = {(int)pd[4 * c], (int)pd[4 * c + 1], (int)pd[4 * c + 2], (int)pd[4 * c + 3]};
-      const uint32_t rows = (uint32_t)(16 * c * RB);
+      for (int ch = 0; ch < 2; ++ch) {  // 16-row chunk 2 qb + ch
+        const i32x4 bp = {(int)pp[4 * ch], (int)pp[4 * ch + 1], (int)pp[4 * ch + 2], (int)pp[4 * ch + 3]};
+        const i32x4 bd = {(int)pd[4 * ch], (int)pd[4 * ch + 1], (int)pd[4 * ch + 2], (int)pd[4 * ch + 3]};
+        const uint32_t rows = (uint32_t)(16 * (2 * qb + ch) * RB);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        acc_v[db] = T::mma(read_tr(st + TILE + t_lane0, st + TILE + t_lane1, db, rows), bp, acc_v[db]);
-        acc_k[db] = T::mma(read_tr(st + t_lane0, st + t_lane1, db, rows), bd, acc_k[db]);
+        for (int db = 0; db < NDB; ++db) {
+          acc_v[db] = T::mma(read_tr(st + TILE + t_lane0, st + TILE + t_lane1, db, rows), bp, acc_v[db]);
+          acc_k[db] = T::mma(read_tr(st + t_lane0, st + t_lane1, db, rows), bd, acc_k[db]);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * NDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
     }
   }
