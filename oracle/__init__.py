@@ -34,6 +34,12 @@ sum_j P dP, GQA == MHA on repeated heads summed, packed == per-sequence); plante
 (dropped or sign-flipped softmax term, untransposed operands, missing or doubled scale, dP
 from K, GQA overwrite or wrong head, varlen key offset) fail the pins.
 
+Paged-cache pins (tests/test_oracle_paged.py): brute force with per-key page arithmetic and
+the plain softmax quotient; the dense forward oracle on a cache laid out in order; invariance
+under relabelling the physical pages; NaN in memory no sequence owns changes nothing; the empty
+sequence; planted mistakes (page index off by one, whole last page kept, table order ignored,
+wrong GQA head) fail the pins.
+
 No function is "parity unpinned" except the two choices the pages leave open:
 rows with no visible key (O = 0, LSE = -inf) and fp8 saturation at +-448, which
 are pinned only by those stated choices.
@@ -53,3 +59,4 @@ from .backward import (  # noqa: F401
     attention_head_backward,
     sum_o_do,
 )
+from .paged import attention_paged, gather_pages  # noqa: F401
