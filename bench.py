@@ -15,6 +15,9 @@ fp64 CPU oracle timed on a bounded sample of the same workload.
 step, both of its kernels): bound by HBM, so its line reports GB/s of algorithmic bytes
 (|Q| + |K| + |V| + |O| + |LSE|) against MI355X's 8 TB/s.
 
+--config 8 is config 6 over a paged cache (fmha_fwd_splitkv_paged, 128-key pages dealt out in
+random order), reported the same way.
+
 --config 7 is the backward pass (one fmha_bwd call per step: its statistics, dQ and dK/dV
 kernels) of the prefill shape, with O and LSE from fmha_fwd computed once before timing.  Its
 FLOPs follow the 5-matmul count (S, dP, dV, dQ, dK: 2.5 times the forward's 4*B*H*Sq*Sk*D,
@@ -44,6 +47,7 @@ PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f8e4m3": 5033.2}
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 CSRC = os.path.join(ROOT, "head_attention_03_amd", "csrc")
 KERNEL_SOURCES = {"fwd": ("fmha_fwd.hip", "fmha_device.h"), "splitkv": ("fmha_splitkv.hip", "fmha_device.h"),
+                  "splitkv_paged": ("fmha_splitkv.hip", "fmha_device.h"),
                   "bwd": ("fmha_bwd.hip", "fmha_device.h")}
 BWD_FLOP_FACTOR = 2.5  # backward matmuls (S, dP, dV, dQ, dK) per forward matmul pair
 PROFILES = os.path.join(ROOT, "profiles")
@@ -62,6 +66,9 @@ def workload_slug(c: dict) -> str:
     heads = f"h{c['H']}" if c["H"] == c["H_kv"] else f"h{c['H']}kv{c['H_kv']}"
     if c.get("entry") == "bwd":
         return f"bwd_{c['dtype']}_d{c['D']}_{c['mask']}_b{c['B']}_{heads}_s{c['Sq']}"
+    if c.get("entry") == "splitkv_paged":
+        return (f"splitkv_paged_{c['dtype']}_d{c['D']}_{c['mask']}_b{c['B']}_{heads}_q{c['Sq']}_k{c['Sk']}"
+                f"_p{c['page_size']}")
     if c.get("entry") == "splitkv":
         return f"splitkv_{c['dtype']}_d{c['D']}_{c['mask']}_b{c['B']}_{heads}_q{c['Sq']}_k{c['Sk']}"
     if c["kind"] == "dense":
@@ -100,8 +107,23 @@ def cpu_baseline(config_id: int, budget_s: float):
         threads = os.cpu_count() or 1
     inp = make_config(config_id)
     q = oracle.decode(to_bits(inp.q), inp.dtype) * inp.q_scale
-    k = oracle.decode(to_bits(inp.k), inp.dtype) * inp.k_scale
-    v = oracle.decode(to_bits(inp.v), inp.dtype) * inp.v_scale
+    if CONFIGS[config_id]["kind"] == "paged":  # whole sequences through the paged oracle, gather included
+        kc, vc = oracle.decode(to_bits(inp.k_cache), inp.dtype), oracle.decode(to_bits(inp.v_cache), inp.dtype)
+        done, t0 = 0, time.perf_counter()
+        for b in range(inp.B):
+            oracle.attention_paged(q[b:b + 1], kc, vc, inp.block_table[b:b + 1], inp.seqlens_k[b:b + 1], inp.scale,
+                                   inp.mask)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        gbs = algorithmic_bytes(inp, bool(CONFIGS[config_id]["lse"])) * done / inp.B / dt / 1e9
+        return {"value": round(gbs, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"{done} of {inp.B} sequences of the same workload (all heads, page gather included), "
+                          f"fp64 numpy, {dt:.1f} s on {platform.processor() or platform.machine()}"}
+    else:
+        k = oracle.decode(to_bits(inp.k), inp.dtype) * inp.k_scale
+        v = oracle.decode(to_bits(inp.v), inp.dtype) * inp.v_scale
     group = inp.H // inp.H_kv
     units = [(b, h) for b in range(inp.B) for h in range(inp.H)]
     bwd = CONFIGS[config_id].get("entry") == "bwd"
@@ -121,7 +143,7 @@ def cpu_baseline(config_id: int, budget_s: float):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    if CONFIGS[config_id].get("entry") == "splitkv":  # the same unit as the GPU line: GB/s of the workload's bytes
+    if CONFIGS[config_id].get("entry") in ("splitkv", "splitkv_paged"):  # GB/s of the workload's bytes, as the GPU line
         gbs = algorithmic_bytes(inp, bool(CONFIGS[config_id]["lse"])) * done / len(units) / dt / 1e9
         return {"value": round(gbs, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
                 "sample": f"{done} of {len(units)} (sequence, head) units of the same workload, fp64 numpy, "
@@ -155,13 +177,21 @@ def main():
     c = CONFIGS[cid]
     dev = torch.device("cuda:0")
     inp = make_config(cid)
-    masks = [inp.mask] if c["kind"] == "dense" else list(c["masks"])
+    masks = [inp.mask] if c["kind"] in ("dense", "paged") else list(c["masks"])
     want_lse = bool(c["lse"])
 
     # device buffers: `rotate` copies of the inputs, one output (and LSE) per copy
     sets = []
     for r in range(max(1, args.rotate)):
-        if c["kind"] == "dense":
+        if c["kind"] == "paged":
+            q = inp.q.to(dev)
+            bt = torch.from_numpy(inp.block_table).to(dev)
+            sl = torch.from_numpy(inp.seqlens_k).to(dev)
+            sets.append(dict(q=q, k=inp.k_cache.to(dev), v=inp.v_cache.to(dev), o=torch.empty_like(q),
+                             lse=torch.empty((inp.B, inp.H, inp.Sq), dtype=torch.float32, device=dev),
+                             varlen=None, tables=(bt, sl),
+                             paged=fmha.make_paged_kv(bt, sl, bt.shape[1], inp.page_size, inp.num_pages)))
+        elif c["kind"] == "dense":
             q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
             o = torch.empty_like(q)
             lse = torch.empty((inp.B, inp.H, inp.Sq), dtype=torch.float32, device=dev) if want_lse else None
@@ -174,7 +204,10 @@ def main():
             lse = torch.empty((inp.H, inp.total_q), dtype=torch.float32, device=dev) if want_lse else None
             sets.append(dict(q=q, k=k, v=v, o=o, lse=lse, cu=(cu_q, cu_k),
                              varlen=fmha.make_varlen(cu_q, cu_k, inp.total_q, inp.total_k)))
-    if c["kind"] == "dense":
+    if c["kind"] == "paged":
+        B, Sq, Sk = inp.B, inp.Sq, inp.Sk
+        flops_step = 4.0 * B * inp.H * Sq * Sk * inp.D
+    elif c["kind"] == "dense":
         B, Sq, Sk = inp.B, inp.Sq, inp.Sk
         flops_step = inp.flops()
     else:
@@ -185,7 +218,8 @@ def main():
             flops_step += inp.flops_convention()
 
     stream = torch.cuda.Stream(device=dev)  # default priority
-    splitkv = c.get("entry") == "splitkv"
+    paged = c.get("entry") == "splitkv_paged"
+    splitkv = c.get("entry") in ("splitkv", "splitkv_paged")
     bwd = c.get("entry") == "bwd"
     if bwd:
         # the backward's inputs: dO (seeded), and O and LSE of the forward, computed once here
@@ -211,6 +245,10 @@ def main():
             if bwd:
                 st = fmha.fmha_bwd(s["q"], s["k"], s["v"], s["o"], s["do"], s["lse"], s["dq"], s["dk"], s["dv"], B, Sq,
                                    Sk, inp.H, inp.H_kv, inp.D, inp.kernel_scale, m, inp.dtype, None, bw, bws, stream)
+            elif paged:
+                st = fmha.fmha_fwd_splitkv_paged(s["q"], s["k"], s["v"], s["o"], s["lse"], B, Sq, Sk, inp.H, inp.H_kv,
+                                                 inp.D, inp.kernel_scale, m, inp.dtype, inp.kernel_o_scale, s["paged"],
+                                                 ws, ws_bytes, stream)
             elif splitkv:
                 st = fmha.fmha_fwd_splitkv(s["q"], s["k"], s["v"], s["o"], s["lse"], B, Sq, Sk, inp.H, inp.H_kv,
                                            inp.D, inp.kernel_scale, m, inp.dtype, inp.kernel_o_scale, s["varlen"],
@@ -250,6 +288,8 @@ def main():
     if splitkv:  # HBM-bound: GB/s of algorithmic bytes
         bytes_step = algorithmic_bytes(inp, want_lse)
         metric, unit, bound = "FMHA split-KV decode GB/s of algorithmic HBM bytes and % of MI355X HBM peak", "GB/s", "hbm"
+        if paged:
+            metric = "FMHA paged-KV split-KV decode GB/s of algorithmic HBM bytes and % of MI355X HBM peak"
         value = bytes_step * args.steps / elapsed / 1e9
         achieved = bytes_step / avg_launch_s / 1e9
         peak = PEAK_HBM_GBS
@@ -257,7 +297,10 @@ def main():
            "D": inp.D, "dtype": inp.dtype, "mask": "+".join(masks), "lse": want_lse, "seed": inp.seed,
            "rotate_buffers": len(sets), "flop_per_step": flops_step}
     if splitkv:
-        cfg.update(entry="fmha_fwd_splitkv", tflops=round(tflops, 3), workspace_bytes=ws_bytes)
+        cfg.update(entry="fmha_fwd_splitkv_paged" if paged else "fmha_fwd_splitkv", tflops=round(tflops, 3),
+                   workspace_bytes=ws_bytes)
+    if paged:
+        cfg.update(page_size=inp.page_size, num_pages=inp.num_pages)
     if bwd:
         cfg.update(entry="fmha_bwd", workspace_bytes=bws, flop_convention="2.5 x forward (S, dP, dV, dQ, dK)")
     out = {

@@ -14,10 +14,13 @@ from ._lib import (  # noqa: F401
     fmha_bwd_workspace_size,
     fmha_fwd,
     fmha_fwd_splitkv,
+    fmha_fwd_splitkv_paged,
+    fmha_paged_kv,
     fmha_fwd_splitkv_workspace_size,
     fmha_status_string,
     fmha_varlen,
     fmha_version,
     load,
+    make_paged_kv,
     make_varlen,
 )

@@ -19,8 +19,8 @@ MASKS = {"none": 0, "residual": 1, "causal_qbegin": 2, "causal_qend": 3}
 STATUS = {0: "FMHA_OK", 1: "FMHA_ERR_NULL_POINTER", 2: "FMHA_ERR_INVALID_SHAPE", 3: "FMHA_ERR_UNSUPPORTED",
           4: "FMHA_ERR_MISALIGNED", 5: "FMHA_ERR_INVALID_ARGUMENT", 6: "FMHA_ERR_HIP"}
 # every symbol include/fmha.h declares
-EXPORTS = ("fmha_fwd", "fmha_fwd_splitkv", "fmha_fwd_splitkv_workspace_size", "fmha_bwd", "fmha_bwd_workspace_size",
-           "fmha_status_string", "fmha_version")
+EXPORTS = ("fmha_fwd", "fmha_fwd_splitkv", "fmha_fwd_splitkv_workspace_size", "fmha_fwd_splitkv_paged", "fmha_bwd",
+           "fmha_bwd_workspace_size", "fmha_status_string", "fmha_version")
 
 
 class FmhaError(RuntimeError):
@@ -32,6 +32,11 @@ class FmhaError(RuntimeError):
 class fmha_varlen(ctypes.Structure):
     _fields_ = [("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
                 ("total_length_q", ctypes.c_int32), ("total_length_k", ctypes.c_int32)]
+
+
+class fmha_paged_kv(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("seqlens_k", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -54,6 +59,10 @@ def load() -> ctypes.CDLL:
         ctypes.c_size_t, ctypes.c_void_p]
     lib.fmha_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fmha_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int32] * 6 + [ctypes.POINTER(fmha_varlen)]
+    lib.fmha_fwd_splitkv_paged.restype = ctypes.c_int
+    lib.fmha_fwd_splitkv_paged.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int32] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.POINTER(fmha_paged_kv), ctypes.c_void_p,
+        ctypes.c_size_t, ctypes.c_void_p]
     lib.fmha_bwd.restype = ctypes.c_int
     lib.fmha_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int32] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.POINTER(fmha_varlen), ctypes.c_void_p, ctypes.c_size_t,
@@ -116,6 +125,23 @@ def fmha_fwd_splitkv_workspace_size(B: int, Sq: int, Sk: int, H: int, H_kv: int,
                                     varlen: Optional[fmha_varlen] = None) -> int:
     vl = ctypes.byref(varlen) if varlen is not None else None
     return int(load().fmha_fwd_splitkv_workspace_size(int(B), int(Sq), int(Sk), int(H), int(H_kv), int(D), vl))
+
+
+def make_paged_kv(block_table, seqlens_k, max_pages_per_seq: int, page_size: int, num_pages: int) -> fmha_paged_kv:
+    return fmha_paged_kv(_ptr(block_table), _ptr(seqlens_k), int(max_pages_per_seq), int(page_size), int(num_pages))
+
+
+def fmha_fwd_splitkv_paged(q, k_cache, v_cache, o, lse, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int,
+                           scale: float, mask, dtype, o_scale: float = 1.0, paged: Optional[fmha_paged_kv] = None,
+                           workspace=None, workspace_bytes: int = 0, stream=None) -> int:
+    """Call the paged-cache split-KV C entry point; returns the fmha_status code."""
+    lib = load()
+    mask = MASKS[mask] if isinstance(mask, str) else int(mask)
+    dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    pk = ctypes.byref(paged) if paged is not None else None
+    return int(lib.fmha_fwd_splitkv_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), int(B), int(Sq),
+                                          int(Sk), int(H), int(H_kv), int(D), float(scale), mask, dtype,
+                                          float(o_scale), pk, _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def fmha_bwd(q, k, v, o, dout, lse, dq, dk, dv, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int, scale: float,

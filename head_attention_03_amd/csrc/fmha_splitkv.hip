@@ -57,8 +57,11 @@ struct Params {
   float* lse_part;  // workspace: [n_splits][rows], natural log (-inf: the split saw no key)
   const int32_t* cu_q;  // null for dense batches
   const int32_t* cu_k;
+  const int32_t* block_table;  // paged cache: [B][bt_stride] physical page of each logical page; null: contiguous
+  const int32_t* seqlens_k;    // paged cache: keys of each sequence
+  int32_t bt_stride, page_shift, num_pages;
   int32_t Sq, H, H_kv, group;  // Sq: query rows per sequence (packed: maximum)
-  int32_t Sk;                  // dense: keys per sequence
+  int32_t Sk;                  // dense: keys per sequence; paged: the most keys of any sequence
   int32_t M;                   // packed rows per K/V head: group * Sq
   int32_t mblks;               // ceil(M / kRows)
   int32_t n_splits, chunk;     // splits per (sequence, K/V head) and keys per split
@@ -122,6 +125,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
     Sq_b = p.Sq;
     k_row0 = b * p.Sk;
     Sk_b = p.Sk;
+  }
+  const bool paged = p.block_table != nullptr;
+  if (paged) {  // keys live in pages; no sequence has more than Sk (which the tables cover)
+    k_row0 = 0;
+    Sk_b = min(max(p.seqlens_k[b], 0), p.Sk);
   }
   const int off = p.qend ? Sk_b - Sq_b : 0;
 
@@ -190,13 +198,31 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
     const int j = pos / CPR;
     ld_off[i] = (uint32_t)j * kstride + (((pos % CPR) ^ swz<CPR>(j)) * 16);
   }
+  // Paged cache: a tile (32 keys, page sizes are powers of two >= 32) lies inside one page; its
+  // descriptors start at the page's row 0 of this K/V head and end after the page's last row
+  // inside the sequence, so rows past the end read 0 as in the contiguous layout.  A table
+  // entry outside [0, num_pages) gets an empty descriptor: its keys read as 0.
   auto load_tile = [&](int n) __attribute__((always_inline)) {
-    const uint32_t key0 = (uint32_t)(k0 + (wave_u + n * kWaves) * kTN) * kstride;
+    const int kt = k0 + (wave_u + n * kWaves) * kTN;  // first key of the tile
     const uint32_t st = ring + (uint32_t)((n % kStages) * STAGE);
+    i32x4 tk = rk, tv = rv;
+    uint32_t key0 = (uint32_t)kt * kstride;
+    if (paged) {
+      const int ps = 1 << p.page_shift;
+      const int lp = kt >> p.page_shift;
+      const int phys = p.block_table[(size_t)b * p.bt_stride + lp];
+      const bool ok = (unsigned)phys < (unsigned)p.num_pages;
+      const int valid = min(ps, Sk_b - (lp << p.page_shift));  // >= 1: the tile starts inside the sequence
+      const size_t pb = ok ? ((size_t)phys * ps * p.H_kv + kvh) * RB : 0;
+      const uint32_t bytes = ok ? (uint32_t)(valid - 1) * kstride + RB : 0;
+      tk = make_rsrc_words((const char*)p.k + pb, bytes);
+      tv = make_rsrc_words((const char*)p.v + pb, bytes);
+      key0 = (uint32_t)(kt & (ps - 1)) * kstride;
+    }
 #pragma unroll
-    for (int i = 0; i < TBLK; ++i) lds_load16(rk, key0 + ld_off[i], st + 1024 * i);
+    for (int i = 0; i < TBLK; ++i) lds_load16(tk, key0 + ld_off[i], st + 1024 * i);
 #pragma unroll
-    for (int i = 0; i < TBLK; ++i) lds_load16(rv, key0 + ld_off[i], st + TILE + 1024 * i);
+    for (int i = 0; i < TBLK; ++i) lds_load16(tv, key0 + ld_off[i], st + TILE + 1024 * i);
   };
 #pragma unroll
   for (int n = 0; n < kStages - 1; ++n)
@@ -421,7 +447,8 @@ namespace {
 // The shape checks fmha_fwd makes, and the split plan.  Returns FMHA_OK with the plan filled.
 fmha_status splitkv_plan(const void* q, const void* k, const void* v, const void* o, const float* lse, int32_t B,
                          int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D, fmha_mask mask, fmha_dtype dtype,
-                         const fmha_varlen* varlen, fmha::skv::Params* p, int64_t* grid, size_t* ws_bytes) {
+                         const fmha_varlen* varlen, fmha::skv::Params* p, int64_t* grid, size_t* ws_bytes,
+                         bool paged = false) {
   using namespace fmha::skv;
   const bool packed = varlen != nullptr;
   if (B < 0 || Sq < 0 || Sk < 0 || H < 0 || H_kv < 0) return FMHA_ERR_INVALID_SHAPE;
@@ -436,8 +463,9 @@ fmha_status splitkv_plan(const void* q, const void* k, const void* v, const void
   const int64_t rows_q = packed ? varlen->total_length_q : Sq;
   const int64_t rows_k = packed ? varlen->total_length_k : Sk;
   const int64_t lim = (int64_t)1 << 31;
-  // per-sequence byte offsets (tiles run up to one wave-tile round past a split) fit 31 bits
-  if (rows_q * H * D * 2 >= lim || (rows_k + kWaves * kTN * kStages) * H_kv * D * 2 >= lim)
+  // per-sequence byte offsets (tiles run up to one wave-tile round past a split) fit 31 bits;
+  // a paged cache addresses each page on its own
+  if (rows_q * H * D * 2 >= lim || (!paged && (rows_k + kWaves * kTN * kStages) * H_kv * D * 2 >= lim))
     return FMHA_ERR_UNSUPPORTED;
   const int64_t q_rows = packed ? (int64_t)varlen->total_length_q : (int64_t)B * Sq;
   const int64_t group = H > 0 ? H / H_kv : 1;
@@ -507,6 +535,9 @@ fmha_status fmha_fwd_splitkv(const void* q, const void* k, const void* v, void* 
   p.lse_part = p.o_part + (size_t)p.n_splits * p.rows * D;
   p.cu_q = packed ? varlen->cu_seqlens_q : nullptr;
   p.cu_k = packed ? varlen->cu_seqlens_k : nullptr;
+  p.block_table = nullptr;
+  p.seqlens_k = nullptr;
+  p.bt_stride = p.page_shift = p.num_pages = 0;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   MergeParams mp;
   mp.o_part = p.o_part;
@@ -518,6 +549,70 @@ fmha_status fmha_fwd_splitkv(const void* q, const void* k, const void* v, void* 
   mp.H = H;
   mp.Sq = Sq;
   mp.total_q = packed ? varlen->total_length_q : 0;
+  mp.o_scale = o_scale;
+
+  hipError_t err = hipSuccess;
+  if (dtype == FMHA_DTYPE_BF16) {
+    if (D == 32) err = fmha::skv::launch<fmha::kBF16, 32>(p, mp, (int)grid, stream);
+    if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64>(p, mp, (int)grid, stream);
+    if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128>(p, mp, (int)grid, stream);
+  } else {
+    if (D == 32) err = fmha::skv::launch<fmha::kF16, 32>(p, mp, (int)grid, stream);
+    if (D == 64) err = fmha::skv::launch<fmha::kF16, 64>(p, mp, (int)grid, stream);
+    if (D == 128) err = fmha::skv::launch<fmha::kF16, 128>(p, mp, (int)grid, stream);
+  }
+  return err == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
+}
+
+fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                   int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D, float scale,
+                                   fmha_mask mask, fmha_dtype dtype, float o_scale, const fmha_paged_kv* paged,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  using namespace fmha::skv;
+  if (!paged) return FMHA_ERR_NULL_POINTER;
+  const bool no_keys = Sk == 0;
+  if (!q || !o || (!no_keys && (!k_cache || !v_cache || !paged->block_table || !paged->seqlens_k)))
+    return FMHA_ERR_NULL_POINTER;
+  Params p;
+  int64_t grid = 0;
+  size_t need = 0;
+  const fmha_status st = splitkv_plan(q, k_cache, v_cache, o, lse, B, Sq, Sk, H, H_kv, D, mask, dtype, nullptr, &p,
+                                      &grid, &need, true);
+  if (st != FMHA_OK) return st;
+  const int32_t ps = paged->page_size;
+  if (ps < kTN || ps > (1 << 16) || (ps & (ps - 1))) return FMHA_ERR_INVALID_SHAPE;
+  if (paged->max_pages_per_seq < 0 || paged->num_pages < 0) return FMHA_ERR_INVALID_SHAPE;
+  if (!no_keys && (paged->num_pages < 1 || (int64_t)paged->max_pages_per_seq * ps < Sk)) return FMHA_ERR_INVALID_SHAPE;
+  if ((int64_t)ps * H_kv * D * 2 >= ((int64_t)1 << 31)) return FMHA_ERR_UNSUPPORTED;
+  if (!(scale > 0.0f) || !isfinite(scale) || !isfinite(o_scale)) return FMHA_ERR_INVALID_ARGUMENT;
+  if (B == 0 || H == 0 || Sq == 0) return FMHA_OK;
+  if (!workspace) return FMHA_ERR_NULL_POINTER;
+  if ((uintptr_t)workspace & 15) return FMHA_ERR_MISALIGNED;
+  if (workspace_bytes < need) return FMHA_ERR_INVALID_ARGUMENT;
+
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.o_part = (float*)workspace;
+  p.lse_part = p.o_part + (size_t)p.n_splits * p.rows * D;
+  p.cu_q = nullptr;
+  p.cu_k = nullptr;
+  p.block_table = no_keys ? nullptr : paged->block_table;
+  p.seqlens_k = paged->seqlens_k;
+  p.bt_stride = paged->max_pages_per_seq;
+  p.page_shift = __builtin_ctz((unsigned)ps);
+  p.num_pages = paged->num_pages;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  MergeParams mp;
+  mp.o_part = p.o_part;
+  mp.lse_part = p.lse_part;
+  mp.o = o;
+  mp.lse = lse;
+  mp.rows = p.rows;
+  mp.n_splits = p.n_splits;
+  mp.H = H;
+  mp.Sq = Sq;
+  mp.total_q = 0;
   mp.o_scale = o_scale;
 
   hipError_t err = hipSuccess;

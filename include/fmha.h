@@ -206,6 +206,43 @@ fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o,
 size_t fmha_bwd_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
                                const fmha_varlen* varlen);
 
+/* Paged K/V cache: fixed-size pages shared by all sequences, addressed through a block table.
+ * This is the KV-cache-block layout that the sm120 article's TODO section names as the core of
+ * paged attention, with the per-sequence index remapping of the CUTLASS generation kernel and
+ * the power-of-two pages of its MLA kernel (trdm.cn walk-through "CUTLASS Blackwell FMHA 示例完全
+ * 解析", sections on the generation kernel and on MLA).
+ *   k_cache, v_cache  [num_pages, page_size, H_kv, D], contiguous, 16-byte aligned
+ *   block_table       device int32 [B, max_pages_per_seq]: key j of sequence b is row
+ *                     j % page_size of page block_table[b * max_pages_per_seq + j / page_size].
+ *                     Entries outside [0, num_pages) read as zero keys and values (no fault).
+ *   seqlens_k         device int32 [B]: keys of sequence b, at most the Sk of the call
+ *                     (larger values are clamped to Sk, negative ones to 0)
+ *   page_size         a power of two from 32 to 65536
+ * Rows of a page past its sequence's end are never read. */
+typedef struct {
+  const int32_t* block_table;
+  const int32_t* seqlens_k;
+  int32_t max_pages_per_seq;
+  int32_t page_size;
+  int32_t num_pages;
+} fmha_paged_kv;
+
+/*
+ * fmha_fwd_splitkv_paged -- fmha_fwd_splitkv with K and V in a paged cache (see fmha_paged_kv):
+ * the same split-KV kernels, reading each 32-key tile from the page that holds it.  q, o and lse
+ * are dense ([B, Sq, H, D], [B, H, Sq]); Sk is the most keys of any sequence (it sizes the
+ * splits, and max_pages_per_seq * page_size must reach it).  The causal-qend offset of sequence b
+ * is seqlens_k[b] - Sq.  workspace: fmha_fwd_splitkv_workspace_size(B, Sq, Sk, H, H_kv, D, NULL)
+ * bytes.  dtype: FMHA_DTYPE_F16 or FMHA_DTYPE_BF16.
+ * Errors as fmha_fwd_splitkv, and: paged NULL, or (when Sk > 0) k_cache, v_cache, block_table or
+ * seqlens_k NULL -> FMHA_ERR_NULL_POINTER; page_size not a power of two in [32, 65536],
+ * max_pages_per_seq * page_size < Sk, or num_pages < 1 -> FMHA_ERR_INVALID_SHAPE.
+ */
+fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                   int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D, float scale,
+                                   fmha_mask mask, fmha_dtype dtype, float o_scale, const fmha_paged_kv* paged,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fmha_status_string(fmha_status status);
 

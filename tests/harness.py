@@ -248,3 +248,34 @@ def compare_grad(name: str, got: torch.Tensor, dtype: str, expected: np.ndarray,
     log(msg)
     assert beyond <= bound, msg
     return beyond
+
+
+# ----------------------------------------------------------------------------------------------
+# paged cache (fmha_fwd_splitkv_paged)
+# ----------------------------------------------------------------------------------------------
+def run_paged(inp, want_lse: bool = True, block_table=None):
+    """O bits and LSE of fmha_fwd_splitkv_paged (NaN-filled workspace)."""
+    dev = torch.device("cuda:0")
+    q, kc, vc = inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((inp.B, inp.H, inp.Sq), dtype=torch.float32, device=dev) if want_lse else None
+    bt = torch.from_numpy(np.ascontiguousarray(inp.block_table if block_table is None else block_table)).to(dev)
+    sl = torch.from_numpy(inp.seqlens_k).to(dev)
+    pk = fmha.make_paged_kv(bt, sl, bt.shape[1], inp.page_size, inp.num_pages)
+    need = fmha.fmha_fwd_splitkv_workspace_size(inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D, None)
+    ws = _workspace(need)
+    st = fmha.fmha_fwd_splitkv_paged(q, kc, vc, o, lse, inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D,
+                                     inp.kernel_scale, inp.mask, inp.dtype, inp.kernel_o_scale, pk, ws, need,
+                                     torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return GpuResult(o_bits=to_bits(o.cpu()), lse=lse.cpu().numpy() if want_lse else None, status=st)
+
+
+def oracle_paged(inp, block_table=None, k_cache=None):
+    kc = oracle.decode(to_bits(inp.k_cache if k_cache is None else k_cache), inp.dtype)
+    vc = oracle.decode(to_bits(inp.v_cache), inp.dtype)
+    if k_cache is not None and kc.shape[0] > vc.shape[0]:
+        vc = np.concatenate([vc, np.zeros((kc.shape[0] - vc.shape[0],) + vc.shape[1:])])
+    q = oracle.decode(to_bits(inp.q), inp.dtype)
+    bt = inp.block_table if block_table is None else block_table
+    return oracle.attention_paged(q, kc, vc, bt, inp.seqlens_k, inp.scale, inp.mask, o_scale=inp.o_scale)

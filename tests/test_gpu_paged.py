@@ -1,0 +1,92 @@
+"""Parity of the paged-cache split-KV entry point (fmha_fwd_splitkv_paged) with the fp64 oracle.
+
+Decode shapes over a cache of fixed-size pages dealt out to the sequences in random order,
+with the pages no sequence owns and the rows past each sequence's end filled with NaN: none
+may reach the output.  The same kernels as fmha_fwd_splitkv, so the results must also equal,
+bit for bit, the contiguous entry point run on the gathered keys.
+"""
+import numpy as np
+import pytest
+import torch
+
+from harness import _workspace, compare, log, oracle_paged, run_paged
+from workloads import make_paged, to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import head_attention_03_amd as fmha
+    fmha.load()  # fails loudly when libfmha.so is missing
+
+
+PAGED = [
+    # (B, Sq, seqlens_k, H, H_kv, D, dtype, mask, page_size)
+    (4, 1, [4097, 1, 300, 0], 32, 8, 128, "bf16", "none", 128),        # ragged caches, an empty one
+    (3, 4, [1000, 64, 2500], 16, 2, 64, "f16", "causal_qend", 32),     # smallest pages, 4 new tokens
+    (2, 1, [8192, 7000], 8, 1, 128, "bf16", "none", 256),              # MQA, long caches
+    (2, 16, [3000, 33], 8, 2, 32, "bf16", "causal_qend", 64),          # 64 packed rows, D = 32
+    (1, 7, [2500], 4, 1, 32, "f16", "causal_qbegin", 512),             # rows see only the first keys
+    (5, 2, [129, 128, 127, 1, 640], 8, 8, 64, "bf16", "residual", 128), # page edges
+]
+
+
+@pytest.mark.parametrize("case", PAGED, ids=lambda c: f"B{c[0]}-q{c[1]}-H{c[3]}/{c[4]}-D{c[5]}-{c[6]}-{c[7]}-p{c[8]}")
+def test_paged_decode(case):
+    B, Sq, lk, H, H_kv, D, dtype, mask, ps = case
+    inp = make_paged(5100 + sum(lk) + ps, B, Sq, lk, H, H_kv, D, dtype, ps, mask=mask)
+    log(f"[case] paged {case} seed={inp.seed} pages={inp.num_pages}")
+    res = run_paged(inp)
+    assert res.status == 0
+    o, lse = oracle_paged(inp)
+    compare(f"paged {case}", res.o_bits, dtype, o, res.lse, lse)
+
+
+def test_paged_equals_contiguous_bitwise():
+    # the same split plan and tile order as fmha_fwd_splitkv on the gathered (packed) keys
+    import head_attention_03_amd as fmha
+    from oracle import gather_pages
+    B, Sq, lk, H, H_kv, D, ps = 3, 2, [3000, 700, 4096], 16, 4, 128, 128
+    inp = make_paged(5200, B, Sq, lk, H, H_kv, D, "bf16", ps, mask="causal_qend")
+    res = run_paged(inp)
+    assert res.status == 0
+    dev = torch.device("cuda:0")
+    k = torch.cat([torch.from_numpy(gather_pages(inp.k_cache.view(torch.int16).numpy(), inp.block_table[b], lk[b], ps))
+                   for b in range(B)]).view(torch.bfloat16)
+    v = torch.cat([torch.from_numpy(gather_pages(inp.v_cache.view(torch.int16).numpy(), inp.block_table[b], lk[b], ps))
+                   for b in range(B)]).view(torch.bfloat16)
+    q = inp.q.reshape(B * Sq, H, D).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, B * Sq), dtype=torch.float32, device=dev)
+    cu_q = torch.tensor([0] + list(np.cumsum([Sq] * B)), dtype=torch.int32, device=dev)
+    cu_k = torch.tensor([0] + list(np.cumsum(lk)), dtype=torch.int32, device=dev)
+    vl = fmha.make_varlen(cu_q, cu_k, B * Sq, int(sum(lk)))
+    need = fmha.fmha_fwd_splitkv_workspace_size(B, Sq, max(lk), H, H_kv, D, vl)
+    ws = _workspace(need)
+    st = fmha.fmha_fwd_splitkv(q, k.to(dev), v.to(dev), o, lse, B, Sq, max(lk), H, H_kv, D, inp.kernel_scale,
+                               "causal_qend", "bf16", 1.0, vl, ws, need, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert st == 0
+    assert np.array_equal(to_bits(o.cpu()).reshape(res.o_bits.shape), res.o_bits)
+    lse_packed = lse.cpu().numpy().reshape(H, B, Sq).transpose(1, 0, 2)
+    assert np.array_equal(lse_packed, res.lse)
+
+
+def test_paged_table_entry_out_of_range_reads_zero_keys():
+    # an entry past the cache reads as a page of zero keys and values (no fault)
+    B, Sq, lk, H, H_kv, D, ps = 2, 1, [300, 200], 8, 2, 64, 64
+    inp = make_paged(5300, B, Sq, lk, H, H_kv, D, "f16", ps, mask="none", poison=False)
+    bt = inp.block_table.copy()
+    bt[0, 2] = inp.num_pages + 7
+    res = run_paged(inp, block_table=bt)
+    assert res.status == 0
+    kz = torch.cat([inp.k_cache, torch.zeros((1,) + tuple(inp.k_cache.shape[1:]), dtype=inp.k_cache.dtype)])
+    vz = torch.cat([inp.v_cache, torch.zeros((1,) + tuple(inp.v_cache.shape[1:]), dtype=inp.v_cache.dtype)])
+    bt_o = bt.copy()
+    bt_o[0, 2] = inp.num_pages
+    inp2 = make_paged(5300, B, Sq, lk, H, H_kv, D, "f16", ps, mask="none", poison=False)
+    inp2.k_cache, inp2.v_cache = kz, vz
+    o, lse = oracle_paged(inp2, block_table=bt_o)
+    compare("paged out-of-range entry", res.o_bits, "f16", o, res.lse, lse)

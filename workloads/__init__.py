@@ -11,6 +11,8 @@ from .synth import (  # noqa: F401
     config_seed,
     draw_normal,
     make_grad,
+    make_paged,
+    PagedInputs,
     make_dense,
     make_varlen,
     make_config,

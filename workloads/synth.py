@@ -222,6 +222,87 @@ def make_grad(seed: int, shape: Sequence[int], dtype: str) -> torch.Tensor:
     return t
 
 
+@dataclasses.dataclass
+class PagedInputs:
+    q: torch.Tensor        # [B, Sq, H, D]
+    k_cache: torch.Tensor  # [num_pages, page_size, H_kv, D]
+    v_cache: torch.Tensor
+    block_table: np.ndarray  # int32 [B, max_pages_per_seq]; unused entries -1
+    seqlens_k: np.ndarray    # int32 [B]
+    page_size: int
+    B: int
+    Sq: int
+    H: int
+    H_kv: int
+    D: int
+    dtype: str
+    mask: str
+    scale: float
+    o_scale: float
+    seed: int
+    q_scale: float = 1.0
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def Sk(self) -> int:
+        """The most keys of any sequence."""
+        return int(self.seqlens_k.max()) if len(self.seqlens_k) else 0
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    def flops(self) -> float:
+        """4*B*H*Sq*Sk*D with Sk the longest cache (the decode workloads give every sequence that length)."""
+        return 4.0 * self.B * self.H * self.Sq * self.Sk * self.D
+
+    @property
+    def kernel_scale(self) -> float:
+        return self.scale * self.q_scale * self.k_scale
+
+    @property
+    def kernel_o_scale(self) -> float:
+        return self.o_scale * self.v_scale
+
+
+def make_paged(seed: int, B: int, Sq: int, seqlens_k: Sequence[int], H: int, H_kv: int, D: int, dtype: str,
+               page_size: int, mask: str = "none", extra_pages: int = 3, poison: bool = True,
+               scale: Optional[float] = None, o_scale: float = 1.0) -> PagedInputs:
+    """Dense Q and a paged K/V cache.  Draws Q, then the whole K cache, then the V cache (N(0, 1)), then
+    a random permutation that deals the physical pages out to the sequences' logical pages in order.
+    ``extra_pages`` pages belong to no sequence; with ``poison`` they, and the rows of each last page
+    past its sequence's end, hold NaN."""
+    rng = np.random.default_rng(seed)
+    lk = np.asarray(seqlens_k, dtype=np.int32)
+    assert lk.shape == (B,)
+    pages_b = [-(-int(s) // page_size) for s in lk]
+    num_pages = sum(pages_b) + int(extra_pages)
+    max_pages = max(pages_b + [1])
+    q, _ = _to_storage(draw_normal(rng, (B, Sq, H, D)), dtype)
+    kc, _ = _to_storage(draw_normal(rng, (num_pages, page_size, H_kv, D)), dtype)
+    vc, _ = _to_storage(draw_normal(rng, (num_pages, page_size, H_kv, D)), dtype)
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = np.full((B, max_pages), -1, dtype=np.int32)
+    used = np.zeros((num_pages, page_size), dtype=bool)
+    n = 0
+    for b in range(B):
+        for i in range(pages_b[b]):
+            pg = int(perm[n])
+            n += 1
+            table[b, i] = pg
+            rows = min(page_size, int(lk[b]) - i * page_size)
+            used[pg, :rows] = True
+    if poison:
+        kc[torch.from_numpy(~used)] = float("nan")
+        vc[torch.from_numpy(~used)] = float("nan")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return PagedInputs(q=q, k_cache=kc, v_cache=vc, block_table=table, seqlens_k=lk, page_size=int(page_size), B=B,
+                       Sq=Sq, H=H, H_kv=H_kv, D=D, dtype=dtype, mask=mask, scale=float(scale),
+                       o_scale=float(o_scale), seed=seed)
+
+
 def make_varlen(seed: int, seqlens_q: Sequence[int], seqlens_k: Sequence[int], H: int, H_kv: int, D: int,
                 dtype: str, mask: str = "none", scale: Optional[float] = None, o_scale: float = 1.0,
                 poison_pads: bool = False, rng: Optional[np.random.Generator] = None) -> VarlenInputs:
@@ -267,7 +348,7 @@ def make_varlen(seed: int, seqlens_q: Sequence[int], seqlens_k: Sequence[int], H
 
 # The measured workloads.  Config 4 is run twice on the same inputs (residual, then causal-qend);
 # config 6 is the split-KV (decode) entry point's workload; config 7 is the backward pass (fmha_bwd)
-# of config 2's shape.
+# of config 2's shape; config 8 is config 6 over a paged cache (fmha_fwd_splitkv_paged).
 CONFIGS = {
     1: dict(name="tiny dense fp16 D64 no mask", kind="dense", B=1, H=2, H_kv=2, Sq=128, Sk=128, D=64,
             dtype="f16", mask="none", lse=False, o_scale=1.0),
@@ -287,12 +368,19 @@ CONFIGS = {
     # Backward of the prefill workload: dQ, dK, dV for a N(0, 1) upstream gradient (fmha_bwd).
     7: dict(name="backward of prefill causal-qbegin bf16 D128", kind="dense", entry="bwd", B=4, H=16, H_kv=16,
             Sq=2048, Sk=2048, D=128, dtype="bf16", mask="causal_qbegin", lse=True, o_scale=1.0),
+    # Decode over a paged cache: config 6's shape with 128-key pages dealt out in random order.
+    8: dict(name="paged decode GQA bf16 D128, 1 token vs 8192 keys, 128-key pages", kind="paged",
+            entry="splitkv_paged", B=16, H=32, H_kv=8, Sq=1, Sk=8192, D=128, page_size=128, dtype="bf16",
+            mask="none", lse=True, o_scale=1.0),
 }
 
 
 def make_config(config_id: int, seed: Optional[int] = None, mask: Optional[str] = None, poison_pads: bool = False):
     c = CONFIGS[config_id]
     seed = config_seed(config_id) if seed is None else seed
+    if c["kind"] == "paged":
+        return make_paged(seed, c["B"], c["Sq"], [c["Sk"]] * c["B"], c["H"], c["H_kv"], c["D"], c["dtype"],
+                          c["page_size"], mask=mask or c["mask"], extra_pages=0, poison=False, o_scale=c["o_scale"])
     if c["kind"] == "dense":
         return make_dense(seed, c["B"], c["Sq"], c["Sk"], c["H"], c["H_kv"], c["D"], c["dtype"],
                           mask=mask or c["mask"], o_scale=c["o_scale"])
