@@ -16,7 +16,8 @@ step, both of its kernels): bound by HBM, so its line reports GB/s of algorithmi
 (|Q| + |K| + |V| + |O| + |LSE|) against MI355X's 8 TB/s.
 
 --config 8 is config 6 over a paged cache (fmha_fwd_splitkv_paged, 128-key pages dealt out in
-random order), reported the same way.
+random order), reported the same way; --config 9 is config 8 over an e4m3 cache (half the K/V
+bytes; bf16 queries and output).
 
 --config 7 is the backward pass (one fmha_bwd call per step: its statistics, dQ and dK/dV
 kernels) of the prefill shape, with O and LSE from fmha_fwd computed once before timing.  Its
@@ -67,7 +68,8 @@ def workload_slug(c: dict) -> str:
     if c.get("entry") == "bwd":
         return f"bwd_{c['dtype']}_d{c['D']}_{c['mask']}_b{c['B']}_{heads}_s{c['Sq']}"
     if c.get("entry") == "splitkv_paged":
-        return (f"splitkv_paged_{c['dtype']}_d{c['D']}_{c['mask']}_b{c['B']}_{heads}_q{c['Sq']}_k{c['Sk']}"
+        kv = f"_kv{c['kv_dtype']}" if c.get("kv_dtype") else ""
+        return (f"splitkv_paged_{c['dtype']}{kv}_d{c['D']}_{c['mask']}_b{c['B']}_{heads}_q{c['Sq']}_k{c['Sk']}"
                 f"_p{c['page_size']}")
     if c.get("entry") == "splitkv":
         return f"splitkv_{c['dtype']}_d{c['D']}_{c['mask']}_b{c['B']}_{heads}_q{c['Sq']}_k{c['Sk']}"
@@ -92,8 +94,9 @@ def measured_traffic(c: dict):
 def algorithmic_bytes(inp, want_lse: bool) -> float:
     """|Q| + |K| + |V| + |O| (+ |LSE|) of a dense workload: what the path must move at least."""
     e = 1 if inp.dtype == "f8e4m3" else 2
+    ek = 1 if (getattr(inp, "kv_dtype", "") or inp.dtype) == "f8e4m3" else 2
     qo = 2.0 * inp.B * inp.Sq * inp.H * inp.D * e
-    kv = 2.0 * inp.B * inp.Sk * inp.H_kv * inp.D * e
+    kv = 2.0 * inp.B * inp.Sk * inp.H_kv * inp.D * ek
     return qo + kv + (4.0 * inp.B * inp.H * inp.Sq if want_lse else 0.0)
 
 
@@ -108,7 +111,9 @@ def cpu_baseline(config_id: int, budget_s: float):
     inp = make_config(config_id)
     q = oracle.decode(to_bits(inp.q), inp.dtype) * inp.q_scale
     if CONFIGS[config_id]["kind"] == "paged":  # whole sequences through the paged oracle, gather included
-        kc, vc = oracle.decode(to_bits(inp.k_cache), inp.dtype), oracle.decode(to_bits(inp.v_cache), inp.dtype)
+        kvt = inp.kv_dtype or inp.dtype
+        kc = oracle.decode(to_bits(inp.k_cache), kvt) * inp.k_scale
+        vc = oracle.decode(to_bits(inp.v_cache), kvt) * inp.v_scale
         done, t0 = 0, time.perf_counter()
         for b in range(inp.B):
             oracle.attention_paged(q[b:b + 1], kc, vc, inp.block_table[b:b + 1], inp.seqlens_k[b:b + 1], inp.scale,
@@ -190,7 +195,8 @@ def main():
             sets.append(dict(q=q, k=inp.k_cache.to(dev), v=inp.v_cache.to(dev), o=torch.empty_like(q),
                              lse=torch.empty((inp.B, inp.H, inp.Sq), dtype=torch.float32, device=dev),
                              varlen=None, tables=(bt, sl),
-                             paged=fmha.make_paged_kv(bt, sl, bt.shape[1], inp.page_size, inp.num_pages)))
+                             paged=fmha.make_paged_kv(bt, sl, bt.shape[1], inp.page_size, inp.num_pages,
+                                                      inp.kv_dtype or inp.dtype)))
         elif c["kind"] == "dense":
             q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
             o = torch.empty_like(q)
@@ -300,7 +306,7 @@ def main():
         cfg.update(entry="fmha_fwd_splitkv_paged" if paged else "fmha_fwd_splitkv", tflops=round(tflops, 3),
                    workspace_bytes=ws_bytes)
     if paged:
-        cfg.update(page_size=inp.page_size, num_pages=inp.num_pages)
+        cfg.update(page_size=inp.page_size, num_pages=inp.num_pages, kv_dtype=inp.kv_dtype or inp.dtype)
     if bwd:
         cfg.update(entry="fmha_bwd", workspace_bytes=bws, flop_convention="2.5 x forward (S, dP, dV, dQ, dK)")
     out = {

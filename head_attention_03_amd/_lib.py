@@ -36,7 +36,7 @@ class fmha_varlen(ctypes.Structure):
 
 class fmha_paged_kv(ctypes.Structure):
     _fields_ = [("block_table", ctypes.c_void_p), ("seqlens_k", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int32),
-                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("kv_dtype", ctypes.c_int)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -127,8 +127,11 @@ def fmha_fwd_splitkv_workspace_size(B: int, Sq: int, Sk: int, H: int, H_kv: int,
     return int(load().fmha_fwd_splitkv_workspace_size(int(B), int(Sq), int(Sk), int(H), int(H_kv), int(D), vl))
 
 
-def make_paged_kv(block_table, seqlens_k, max_pages_per_seq: int, page_size: int, num_pages: int) -> fmha_paged_kv:
-    return fmha_paged_kv(_ptr(block_table), _ptr(seqlens_k), int(max_pages_per_seq), int(page_size), int(num_pages))
+def make_paged_kv(block_table, seqlens_k, max_pages_per_seq: int, page_size: int, num_pages: int,
+                  kv_dtype) -> fmha_paged_kv:
+    """``kv_dtype``: the cache's element type (name or enum value): the call's dtype, or "f8e4m3"."""
+    kv = DTYPES[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
+    return fmha_paged_kv(_ptr(block_table), _ptr(seqlens_k), int(max_pages_per_seq), int(page_size), int(num_pages), kv)
 
 
 def fmha_fwd_splitkv_paged(q, k_cache, v_cache, o, lse, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int,

@@ -25,6 +25,13 @@
 //   of one (sequence, K/V head).  S^T = K Q^T and O^T += V^T P^T run on the same
 //   v_mfma_f32_32x32x16 operand layouts as fmha_fwd (K and V rows XOR-swizzled in LDS, V^T
 //   from ds_read_b64_tr_b16); rows past the group are zero and their output is dropped.
+// * Paged caches (fmha_fwd_splitkv_paged): each 32-key tile lies in one page; the wave looks the
+//   page up in the block table and bounds its descriptors to the page's rows in the sequence.
+// * e4m3 caches under 16-bit queries: tiles land in LDS as bytes (fmha_fwd's fp8 row swizzle) and
+//   widen exactly to the 16-bit MFMA type as the operands are read (v_cvt_scalef32_pk_*_fp8 with
+//   scale 1; V^T through ds_read_b64_tr_b8, with P regrouped to its 8-consecutive-key order).
+//   The 8 KiB tiles make a 40 KiB workgroup, so four share a compute unit and the split target
+//   doubles: 1.55x faster than keeping two per unit, which left the SIMDs waiting.
 // * Masks, varlen and GQA follow fmha_fwd: per-row last visible key, buffer descriptors
 //   bounded to the sequence (rows past either end read 0), and the causal alignment offset
 //   Sk_b - Sq_b for causal-qend.
@@ -44,10 +51,25 @@ namespace skv {
 constexpr int kWaves = 1;       // waves per workgroup, each streaming its own K/V tiles
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTN = 32;         // keys per tile: one 32-key block of the MFMA
-constexpr int kStages = 4;      // tiles in a wave's LDS ring (three in flight)
+constexpr int kStages = 4;      // tiles in a wave's LDS ring (three in flight) for 16-bit K/V
+constexpr int kStages8 = 4;     // the same for e4m3 K/V (8 KiB tiles: a 40 KiB workgroup, four per CU)
+
+// s_waitcnt for "at most `ahead` tiles of NLD loads each still in flight" (ahead capped at T)
+template <int NLD, int T>
+__device__ inline void wait_tiles(int ahead) {
+  if constexpr (T == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= T)
+      wait_vmcnt<T * NLD>();
+    else
+      wait_tiles<NLD, T - 1>(ahead);
+  }
+}
 constexpr int kRows = 32;       // packed query rows per workgroup (the MFMA N dimension)
 constexpr int kMinChunk = 256;  // fewest keys per split
 constexpr int kTargetWgs = 512; // split until about this many workgroups (two per compute unit)
+constexpr int kTargetWgs8 = 1024;  // the same for e4m3 K/V (four per compute unit)
 
 struct Params {
   const void* q;
@@ -80,25 +102,47 @@ struct MergeParams {
 };
 
 // split kernel: grid = B * H_kv * mblks * n_splits workgroups of kThreads
-template <int DT, int D>
+// KV8: K and V are e4m3 (a quantised cache); they are widened to the 16-bit type of Q exactly
+// (every e4m3 value is a bf16 and an fp16 value) as the MFMA operands are read from LDS.
+template <int DT, int D, bool KV8>
 __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
-  constexpr int E = 2;
-  constexpr int RB = D * E;          // bytes per K/V/Q row
-  constexpr int CPR = RB / 16;       // 16-byte chunks per row
-  constexpr int TILE = kTN * RB;     // bytes per K or V tile
+  constexpr int E = 2;               // bytes per Q element
+  constexpr int EK = KV8 ? 1 : 2;    // bytes per K/V element
+  constexpr int RB = D * E;          // bytes per Q row
+  constexpr int RBK = D * EK;        // bytes per K/V row
+  constexpr int CPR = RB / 16;       // 16-byte chunks per Q row
+  constexpr int CPRK = RBK / 16;     // 16-byte chunks per K/V row
+  constexpr int TILE = kTN * RBK;    // bytes per K or V tile
   constexpr int TBLK = TILE / 1024;  // 1 KiB LDS-direct loads per K or V tile
   constexpr int NLD = 2 * TBLK;      // loads per tile
   constexpr int STAGE = 2 * TILE;    // K tile, then V tile
+  constexpr int STG = KV8 ? kStages8 : kStages;  // ring depth
   constexpr int QB = kRows * RB;     // a wave's copy of the query rows
   constexpr int QBLK = QB / 1024;
   constexpr int KS = D / 16;         // MFMA k-steps over the head dimension
   constexpr int NDB = D / 32;        // 32-wide blocks of the head dimension in O
   static_assert(TILE % 1024 == 0 && QB % 1024 == 0, "whole 1 KiB loads");
-  static_assert(3 * NLD < 64, "vmcnt range");
+  static_assert(!KV8 || D >= 64, "e4m3 K/V rows of at least 64 bytes");
+  static_assert((STG - 1) * NLD < 64, "vmcnt range");
   typedef Elem<DT> T;
+  // eight e4m3 values (bytes 0..7 of w) as eight 16-bit values of the MFMA type, in order
+  auto widen8 = [](i32x2 w) __attribute__((always_inline)) {
+    i32x4 a;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if constexpr (DT == kBF16) {
+        a[2 * h] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.0f, false));
+        a[2 * h + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.0f, true));
+      } else {
+        a[2 * h] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[h], 1.0f, false));
+        a[2 * h + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[h], 1.0f, true));
+      }
+    }
+    return a;
+  };
 
-  // LDS: per wave a ring of kStages {K, V} stages, then per wave a copy of the Q rows
-  __shared__ __attribute__((aligned(1024))) char lds[kWaves * (kStages * STAGE + QB)];
+  // LDS: per wave a ring of STG {K, V} stages, then per wave a copy of the Q rows
+  __shared__ __attribute__((aligned(1024))) char lds[kWaves * (STG * STAGE + QB)];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
 
   const int lane = threadIdx.x & 63;
@@ -156,17 +200,17 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
 
   // ---- descriptors: bounded to the rows of this sequence ------------------------------
   const uint32_t qstride = (uint32_t)p.H * D * E;
-  const uint32_t kstride = (uint32_t)p.H_kv * D * E;
+  const uint32_t kstride = (uint32_t)p.H_kv * RBK;
   const size_t q_base = (size_t)q_row0 * p.H * D * E;
-  const size_t k_base = ((size_t)k_row0 * p.H_kv + kvh) * D * E;
+  const size_t k_base = ((size_t)k_row0 * p.H_kv + kvh) * RBK;
   const uint32_t q_bytes = Sq_b > 0 ? (uint32_t)Sq_b * qstride : 0;
-  const uint32_t k_bytes = Sk_b > 0 ? (uint32_t)(Sk_b - 1) * kstride + RB : 0;
+  const uint32_t k_bytes = Sk_b > 0 ? (uint32_t)(Sk_b - 1) * kstride + RBK : 0;
   const i32x4 rq = make_rsrc_words((const char*)p.q + q_base, q_bytes);
   const i32x4 rk = make_rsrc_words((const char*)p.k + k_base, k_bytes);
   const i32x4 rv = make_rsrc_words((const char*)p.v + k_base, k_bytes);
 
-  const uint32_t ring = lds0 + (uint32_t)(wave_u * kStages * STAGE);
-  const uint32_t q_lds = lds0 + (uint32_t)(kWaves * kStages * STAGE + wave_u * QB);
+  const uint32_t ring = lds0 + (uint32_t)(wave_u * STG * STAGE);
+  const uint32_t q_lds = lds0 + (uint32_t)(kWaves * STG * STAGE + wave_u * QB);
 
   // ---- Q rows into this wave's LDS copy (swizzled like a K tile), then the B operand ----
 #pragma unroll
@@ -181,22 +225,27 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
     lds_load16(rq, src, q_lds + 1024 * i);
   }
 
-  // per-lane LDS offsets: K row l32, chunk h32 of each k-step; V^T transpose read (as fmha_fwd)
-  const int k_lane = l32 * RB + ((h32 ^ swz<CPR>(l32)) * 16);
+  // per-lane LDS offsets: Q (and 16-bit K) row l32, chunk h32 of each k-step; V^T transpose
+  // read (as fmha_fwd).  e4m3 K/V tiles use fmha_fwd's fp8 row swizzle: K row l32, 8 bytes at
+  // chunk ks, half h32; V^T from ds_read_b64_tr_b8, which gives each lane column l32 of the
+  // 8 consecutive rows 8 h32 + 0..7 of a 16-row chunk.
+  auto swk = [](int j) __attribute__((always_inline)) { return KV8 ? swz8<CPRK>(j) : swz<CPRK>(j); };
+  const int q_lane = l32 * RB + ((h32 ^ swz<CPR>(l32)) * 16);
+  const int k_lane = KV8 ? l32 * RBK + (swk(l32) * 16) + 8 * h32 : q_lane;
   const int g16 = (lane >> 4) & 1;
   const int s16 = lane & 15;
-  const int v_row0 = 4 * h32 + (s16 >> 2);
-  const int v_part = 2 * g16 + ((s16 & 3) >> 1);
-  const int v_lane0 = TILE + v_row0 * RB + ((v_part ^ swz<CPR>(v_row0)) * 16) + 8 * (s16 & 1);
-  const int v_lane1 = TILE + (v_row0 + 8) * RB + ((v_part ^ swz<CPR>(v_row0 + 8)) * 16) + 8 * (s16 & 1);
+  const int v_row0 = KV8 ? 8 * h32 + (s16 >> 1) : 4 * h32 + (s16 >> 2);
+  const int v_part = KV8 ? g16 : 2 * g16 + ((s16 & 3) >> 1);
+  const int v_lane0 = TILE + v_row0 * RBK + ((v_part ^ swk(v_row0)) * 16) + 8 * (s16 & 1);
+  const int v_lane1 = TILE + (v_row0 + 8) * RBK + ((v_part ^ swk(v_row0 + 8)) * 16) + 8 * (s16 & 1);
 
-  // loads of this wave's tile n (keys k0 + (wave + n kWaves) kTN ..) into stage n % kStages
+  // loads of this wave's tile n (keys k0 + (wave + n kWaves) kTN ..) into stage n % STG
   uint32_t ld_off[TBLK];
 #pragma unroll
   for (int i = 0; i < TBLK; ++i) {
     const int pos = 64 * i + lane;
-    const int j = pos / CPR;
-    ld_off[i] = (uint32_t)j * kstride + (((pos % CPR) ^ swz<CPR>(j)) * 16);
+    const int j = pos / CPRK;
+    ld_off[i] = (uint32_t)j * kstride + (((pos % CPRK) ^ swk(j)) * 16);
   }
   // Paged cache: a tile (32 keys, page sizes are powers of two >= 32) lies inside one page; its
   // descriptors start at the page's row 0 of this K/V head and end after the page's last row
@@ -204,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
   // entry outside [0, num_pages) gets an empty descriptor: its keys read as 0.
   auto load_tile = [&](int n) __attribute__((always_inline)) {
     const int kt = k0 + (wave_u + n * kWaves) * kTN;  // first key of the tile
-    const uint32_t st = ring + (uint32_t)((n % kStages) * STAGE);
+    const uint32_t st = ring + (uint32_t)((n % STG) * STAGE);
     i32x4 tk = rk, tv = rv;
     uint32_t key0 = (uint32_t)kt * kstride;
     if (paged) {
@@ -213,8 +262,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
       const int phys = p.block_table[(size_t)b * p.bt_stride + lp];
       const bool ok = (unsigned)phys < (unsigned)p.num_pages;
       const int valid = min(ps, Sk_b - (lp << p.page_shift));  // >= 1: the tile starts inside the sequence
-      const size_t pb = ok ? ((size_t)phys * ps * p.H_kv + kvh) * RB : 0;
-      const uint32_t bytes = ok ? (uint32_t)(valid - 1) * kstride + RB : 0;
+      const size_t pb = ok ? ((size_t)phys * ps * p.H_kv + kvh) * RBK : 0;
+      const uint32_t bytes = ok ? (uint32_t)(valid - 1) * kstride + RBK : 0;
       tk = make_rsrc_words((const char*)p.k + pb, bytes);
       tv = make_rsrc_words((const char*)p.v + pb, bytes);
       key0 = (uint32_t)(kt & (ps - 1)) * kstride;
@@ -225,21 +274,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
     for (int i = 0; i < TBLK; ++i) lds_load16(tv, key0 + ld_off[i], st + TILE + 1024 * i);
   };
 #pragma unroll
-  for (int n = 0; n < kStages - 1; ++n)
+  for (int n = 0; n < STG - 1; ++n)
     if (n < n_w) load_tile(n);
 
   // Q landed (it is older than every tile load): read the B operand, dims 16 ks + 8 h32 ..
-  if (n_w >= 3)
-    wait_vmcnt<3 * NLD>();
-  else if (n_w == 2)
-    wait_vmcnt<2 * NLD>();
-  else if (n_w == 1)
-    wait_vmcnt<NLD>();
-  else
-    wait_vmcnt<0>();
+  wait_tiles<NLD, STG - 1>(n_w);
   i32x4 qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const lds_i32x4*)(uintptr_t)((q_lds + k_lane) ^ (32 * ks));
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const lds_i32x4*)(uintptr_t)((q_lds + q_lane) ^ (32 * ks));
 
   f32x16 acc_o[NDB];
 #pragma unroll
@@ -250,20 +292,19 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
 
   for (int n = 0; n < n_w; ++n) {
     // tile n must have landed; the tiles requested after it may still be in flight
-    if (n + 2 < n_w)
-      wait_vmcnt<2 * NLD>();
-    else if (n + 1 < n_w)
-      wait_vmcnt<NLD>();
-    else
-      wait_vmcnt<0>();
-    const uint32_t st = ring + (uint32_t)((n % kStages) * STAGE);
+    wait_tiles<NLD, STG - 2>(n_w - 1 - n);
+    const uint32_t st = ring + (uint32_t)((n % STG) * STAGE);
     const int kb = k0 + (wave_u + n * kWaves) * kTN;  // first key of the tile
 
     // S^T = K Q^T: score r of this lane is key kb + 4 h32 + 8 (r / 4) + r % 4, row l32
     f32x16 s = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const i32x4 a = *(const lds_i32x4*)(uintptr_t)((st + k_lane) ^ (32 * ks));
+      i32x4 a;
+      if constexpr (KV8)
+        a = widen8(*(const lds_i32x2*)(uintptr_t)((st + k_lane) ^ (16 * ks)));
+      else
+        a = *(const lds_i32x4*)(uintptr_t)((st + k_lane) ^ (32 * ks));
       s = T::mma(a, qf[ks], s);
     }
     if (kb + kTN > mask_from) {
@@ -299,12 +340,31 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
       l2 += T::lo(pk[2 * qd + 1]) + T::hi(pk[2 * qd + 1]);
     }
     l_run += l2;
+    if constexpr (KV8) {
+      // regroup to the order of the transposed e4m3 V read, 8 consecutive keys per lane and
+      // 16-key chunk: lane h32 = 0 trades its keys 8..11 for keys 4..7 of lane l + 32
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int a = 4 * (i >> 1) + (i & 1);
+        auto r = __builtin_amdgcn_permlane32_swap(pk[a], pk[a + 2], false, false);
+        pk[a] = r[0];
+        pk[a + 2] = r[1];
+      }
+    }
 
     // O^T += V^T P^T: 16-key chunk c, d-block db
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const i32x4 bp = {(int)pk[4 * c], (int)pk[4 * c + 1], (int)pk[4 * c + 2], (int)pk[4 * c + 3]};
-      const uint32_t rows = (uint32_t)(16 * c * RB);
+      const uint32_t rows = (uint32_t)(16 * c * RBK);
+      if constexpr (KV8) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)(((st + v_lane0) ^ (32 * db)) + rows));
+          acc_o[db] = T::mma(widen8(t), bp, acc_o[db]);
+        }
+        continue;
+      }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const i16x4 v0 =
@@ -318,9 +378,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
         acc_o[db] = T::mma(a, bp, acc_o[db]);
       }
     }
-    // stage (n - 1) % kStages was read in the previous iteration: refill it with tile n + 3
+    // stage (n - 1) % STG was read in the previous iteration: refill it with tile n + STG - 1
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (n + kStages - 1 < n_w) load_tile(n + kStages - 1);
+    if (n + STG - 1 < n_w) load_tile(n + STG - 1);
   }
 
   // ---- merge the waves' states in LDS (the rings are free now), then write the partial --
@@ -413,10 +473,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   }
 }
 
-// Splits per (sequence, K/V head) and keys per split: split until about kTargetWgs
-// workgroups, but never below kMinChunk keys per split; chunks are whole wave-tile rounds.
-inline void plan(int64_t units, int64_t Sk, int32_t* n_splits, int32_t* chunk) {
-  int64_t n = units > 0 ? (kTargetWgs + units - 1) / units : 1;
+// Splits per (sequence, K/V head) and keys per split: split until about `target` workgroups,
+// but never below kMinChunk keys per split; chunks are whole wave-tile rounds.
+inline void plan(int64_t units, int64_t Sk, int64_t target, int32_t* n_splits, int32_t* chunk) {
+  int64_t n = units > 0 ? (target + units - 1) / units : 1;
   const int64_t n_max = Sk > kMinChunk ? (Sk + kMinChunk - 1) / kMinChunk : 1;
   n = n < 1 ? 1 : n > n_max ? n_max : n;
   constexpr int64_t round = kWaves * kTN;
@@ -426,9 +486,9 @@ inline void plan(int64_t units, int64_t Sk, int32_t* n_splits, int32_t* chunk) {
   *n_splits = (int32_t)(Sk > 0 ? (Sk + c - 1) / c : 1);
 }
 
-template <int DT, int D>
+template <int DT, int D, bool KV8 = false>
 hipError_t launch(const Params& p, const MergeParams& mp, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((split_kernel<DT, D>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((split_kernel<DT, D, KV8>), dim3(grid), dim3(kThreads), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t threads = (int64_t)mp.rows * (D / 4);
@@ -448,7 +508,7 @@ namespace {
 fmha_status splitkv_plan(const void* q, const void* k, const void* v, const void* o, const float* lse, int32_t B,
                          int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D, fmha_mask mask, fmha_dtype dtype,
                          const fmha_varlen* varlen, fmha::skv::Params* p, int64_t* grid, size_t* ws_bytes,
-                         bool paged = false) {
+                         bool paged = false, bool kv8 = false) {
   using namespace fmha::skv;
   const bool packed = varlen != nullptr;
   if (B < 0 || Sq < 0 || Sk < 0 || H < 0 || H_kv < 0) return FMHA_ERR_INVALID_SHAPE;
@@ -471,13 +531,15 @@ fmha_status splitkv_plan(const void* q, const void* k, const void* v, const void
   const int64_t group = H > 0 ? H / H_kv : 1;
   const int64_t M = group * Sq;
   const int64_t mblks = (M + kRows - 1) / kRows;
-  int32_t n_splits = 1, chunk = kWaves * kTN;
-  plan((int64_t)B * H_kv * mblks, Sk, &n_splits, &chunk);
+  // The workspace is sized for the larger split target, so one size serves both cache types.
+  int32_t n_splits = 1, chunk = kWaves * kTN, ws_splits = 1, ws_chunk = kWaves * kTN;
+  plan((int64_t)B * H_kv * mblks, Sk, kv8 ? kTargetWgs8 : kTargetWgs, &n_splits, &chunk);
+  plan((int64_t)B * H_kv * mblks, Sk, kTargetWgs8, &ws_splits, &ws_chunk);
   const int64_t rows = q_rows * H;
-  if (rows >= lim || (int64_t)n_splits * rows * D >= lim * 2) return FMHA_ERR_UNSUPPORTED;
+  if (rows >= lim || (int64_t)ws_splits * rows * D >= lim * 2) return FMHA_ERR_UNSUPPORTED;
   *grid = (int64_t)B * H_kv * mblks * n_splits;
   if (*grid >= lim) return FMHA_ERR_UNSUPPORTED;
-  *ws_bytes = (size_t)n_splits * (size_t)rows * (size_t)(D + 1) * sizeof(float);
+  *ws_bytes = (size_t)ws_splits * (size_t)rows * (size_t)(D + 1) * sizeof(float);
   p->Sq = Sq;
   p->Sk = Sk;
   p->H = H;
@@ -576,11 +638,14 @@ fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const voi
   Params p;
   int64_t grid = 0;
   size_t need = 0;
+  const bool kv8 = paged->kv_dtype == FMHA_DTYPE_F8E4M3;
   const fmha_status st = splitkv_plan(q, k_cache, v_cache, o, lse, B, Sq, Sk, H, H_kv, D, mask, dtype, nullptr, &p,
-                                      &grid, &need, true);
+                                      &grid, &need, true, kv8);
   if (st != FMHA_OK) return st;
   const int32_t ps = paged->page_size;
   if (ps < kTN || ps > (1 << 16) || (ps & (ps - 1))) return FMHA_ERR_INVALID_SHAPE;
+  if (!kv8 && paged->kv_dtype != dtype) return FMHA_ERR_UNSUPPORTED;
+  if (kv8 && D == 32) return FMHA_ERR_UNSUPPORTED;  // e4m3 rows of 32 bytes: not built
   if (paged->max_pages_per_seq < 0 || paged->num_pages < 0) return FMHA_ERR_INVALID_SHAPE;
   if (!no_keys && (paged->num_pages < 1 || (int64_t)paged->max_pages_per_seq * ps < Sk)) return FMHA_ERR_INVALID_SHAPE;
   if ((int64_t)ps * H_kv * D * 2 >= ((int64_t)1 << 31)) return FMHA_ERR_UNSUPPORTED;
@@ -616,7 +681,15 @@ fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const voi
   mp.o_scale = o_scale;
 
   hipError_t err = hipSuccess;
-  if (dtype == FMHA_DTYPE_BF16) {
+  if (kv8) {
+    if (dtype == FMHA_DTYPE_BF16) {
+      if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64, true>(p, mp, (int)grid, stream);
+      if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128, true>(p, mp, (int)grid, stream);
+    } else {
+      if (D == 64) err = fmha::skv::launch<fmha::kF16, 64, true>(p, mp, (int)grid, stream);
+      if (D == 128) err = fmha::skv::launch<fmha::kF16, 128, true>(p, mp, (int)grid, stream);
+    }
+  } else if (dtype == FMHA_DTYPE_BF16) {
     if (D == 32) err = fmha::skv::launch<fmha::kBF16, 32>(p, mp, (int)grid, stream);
     if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64>(p, mp, (int)grid, stream);
     if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128>(p, mp, (int)grid, stream);

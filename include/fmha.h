@@ -218,6 +218,11 @@ size_t fmha_bwd_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int
  *   seqlens_k         device int32 [B]: keys of sequence b, at most the Sk of the call
  *                     (larger values are clamped to Sk, negative ones to 0)
  *   page_size         a power of two from 32 to 65536
+ *   kv_dtype          element type of the cache: the call's dtype, or FMHA_DTYPE_F8E4M3 for an
+ *                     e4m3 cache under fp16/bf16 queries (the fp8/INT8 KV quantisation the sm120
+ *                     article's TODO section lists).  e4m3 values widen exactly to fp16/bf16 for
+ *                     the matrix cores; the caller folds the cache's per-tensor dequantisation
+ *                     scales into scale (K) and o_scale (V), as for fp8 in fmha_fwd.  D 64 or 128.
  * Rows of a page past its sequence's end are never read. */
 typedef struct {
   const int32_t* block_table;
@@ -225,6 +230,7 @@ typedef struct {
   int32_t max_pages_per_seq;
   int32_t page_size;
   int32_t num_pages;
+  fmha_dtype kv_dtype;
 } fmha_paged_kv;
 
 /*
@@ -233,10 +239,11 @@ typedef struct {
  * are dense ([B, Sq, H, D], [B, H, Sq]); Sk is the most keys of any sequence (it sizes the
  * splits, and max_pages_per_seq * page_size must reach it).  The causal-qend offset of sequence b
  * is seqlens_k[b] - Sq.  workspace: fmha_fwd_splitkv_workspace_size(B, Sq, Sk, H, H_kv, D, NULL)
- * bytes.  dtype: FMHA_DTYPE_F16 or FMHA_DTYPE_BF16.
+ * bytes.  dtype (q and o): FMHA_DTYPE_F16 or FMHA_DTYPE_BF16.
  * Errors as fmha_fwd_splitkv, and: paged NULL, or (when Sk > 0) k_cache, v_cache, block_table or
  * seqlens_k NULL -> FMHA_ERR_NULL_POINTER; page_size not a power of two in [32, 65536],
- * max_pages_per_seq * page_size < Sk, or num_pages < 1 -> FMHA_ERR_INVALID_SHAPE.
+ * max_pages_per_seq * page_size < Sk, or num_pages < 1 -> FMHA_ERR_INVALID_SHAPE; kv_dtype neither
+ * dtype nor FMHA_DTYPE_F8E4M3, or an e4m3 cache with D == 32 -> FMHA_ERR_UNSUPPORTED.
  */
 fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                                    int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D, float scale,

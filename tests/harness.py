@@ -261,7 +261,7 @@ def run_paged(inp, want_lse: bool = True, block_table=None):
     lse = torch.empty((inp.B, inp.H, inp.Sq), dtype=torch.float32, device=dev) if want_lse else None
     bt = torch.from_numpy(np.ascontiguousarray(inp.block_table if block_table is None else block_table)).to(dev)
     sl = torch.from_numpy(inp.seqlens_k).to(dev)
-    pk = fmha.make_paged_kv(bt, sl, bt.shape[1], inp.page_size, inp.num_pages)
+    pk = fmha.make_paged_kv(bt, sl, bt.shape[1], inp.page_size, inp.num_pages, inp.kv_dtype or inp.dtype)
     need = fmha.fmha_fwd_splitkv_workspace_size(inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D, None)
     ws = _workspace(need)
     st = fmha.fmha_fwd_splitkv_paged(q, kc, vc, o, lse, inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D,
@@ -272,8 +272,9 @@ def run_paged(inp, want_lse: bool = True, block_table=None):
 
 
 def oracle_paged(inp, block_table=None, k_cache=None):
-    kc = oracle.decode(to_bits(inp.k_cache if k_cache is None else k_cache), inp.dtype)
-    vc = oracle.decode(to_bits(inp.v_cache), inp.dtype)
+    kvt = inp.kv_dtype or inp.dtype
+    kc = oracle.decode(to_bits(inp.k_cache if k_cache is None else k_cache), kvt) * inp.k_scale
+    vc = oracle.decode(to_bits(inp.v_cache), kvt) * inp.v_scale
     if k_cache is not None and kc.shape[0] > vc.shape[0]:
         vc = np.concatenate([vc, np.zeros((kc.shape[0] - vc.shape[0],) + vc.shape[1:])])
     q = oracle.decode(to_bits(inp.q), inp.dtype)

@@ -173,7 +173,7 @@ def test_bwd_workspace_size():
 # fmha_fwd_splitkv_paged: host validation
 # ----------------------------------------------------------------------------------------------
 def call_paged(**kw):
-    pk = kw.pop("paged", fmha.make_paged_kv(P, P, 4, 128, 8))
+    pk = kw.pop("paged", fmha.make_paged_kv(P, P, 4, 128, 8, "bf16"))
     a = dict(q=P, k_cache=P, v_cache=P, o=P, lse=None, B=1, Sq=1, Sk=500, H=8, H_kv=2, D=128, scale=0.1,
              mask="none", dtype="bf16", o_scale=1.0, paged=pk, workspace=P, workspace_bytes=1 << 24, stream=None)
     a.update(kw)
@@ -182,14 +182,16 @@ def call_paged(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(paged=None), 1), (dict(k_cache=None), 1), (dict(q=None), 1), (dict(workspace=None), 1),
-    (dict(paged=fmha.make_paged_kv(None, P, 4, 128, 8)), 1), (dict(paged=fmha.make_paged_kv(P, None, 4, 128, 8)), 1),
-    (dict(paged=fmha.make_paged_kv(P, P, 4, 96, 8)), 2), (dict(paged=fmha.make_paged_kv(P, P, 4, 16, 8)), 2),
-    (dict(paged=fmha.make_paged_kv(P, P, 3, 128, 8)), 2), (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 0)), 2),
-    (dict(paged=fmha.make_paged_kv(P, P, 4, 1 << 17, 8)), 2),
+    (dict(paged=fmha.make_paged_kv(None, P, 4, 128, 8, "bf16")), 1), (dict(paged=fmha.make_paged_kv(P, None, 4, 128, 8, "bf16")), 1),
+    (dict(paged=fmha.make_paged_kv(P, P, 4, 96, 8, "bf16")), 2), (dict(paged=fmha.make_paged_kv(P, P, 4, 16, 8, "bf16")), 2),
+    (dict(paged=fmha.make_paged_kv(P, P, 3, 128, 8, "bf16")), 2), (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 0, "bf16")), 2),
+    (dict(paged=fmha.make_paged_kv(P, P, 4, 1 << 17, 8, "bf16")), 2),
+    (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 8, "f16")), 3), (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 8, 7)), 3),
+    (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 8, "f8e4m3"), D=32), 3),
     (dict(dtype="f8e4m3"), 3), (dict(H=3), 2), (dict(D=48), 2),
     (dict(k_cache=P + 8), 4), (dict(workspace=P + 8), 4),
     (dict(scale=0.0), 5), (dict(workspace_bytes=16), 5),
-    (dict(B=0), 0), (dict(Sk=0, k_cache=None, v_cache=None, paged=fmha.make_paged_kv(None, None, 0, 128, 0), B=0), 0),
+    (dict(B=0), 0), (dict(Sk=0, k_cache=None, v_cache=None, paged=fmha.make_paged_kv(None, None, 0, 128, 0, "bf16"), B=0), 0),
 ])
 def test_paged_rejects_bad_arguments(kw, status):
     assert call_paged(**kw) == status

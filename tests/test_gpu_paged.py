@@ -90,3 +90,26 @@ def test_paged_table_entry_out_of_range_reads_zero_keys():
     inp2.k_cache, inp2.v_cache = kz, vz
     o, lse = oracle_paged(inp2, block_table=bt_o)
     compare("paged out-of-range entry", res.o_bits, "f16", o, res.lse, lse)
+
+
+PAGED_FP8 = [
+    # (B, Sq, seqlens_k, H, H_kv, D, dtype, mask, page_size): e4m3 cache, 16-bit queries and output
+    (4, 1, [4097, 1, 300, 0], 32, 8, 128, "bf16", "none", 128),
+    (3, 4, [1000, 64, 2500], 16, 2, 64, "f16", "causal_qend", 32),
+    (2, 16, [3000, 33], 8, 2, 128, "bf16", "causal_qend", 64),
+    (2, 2, [700, 1300], 4, 1, 64, "bf16", "causal_qbegin", 256),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_FP8,
+                         ids=lambda c: f"fp8kv-B{c[0]}-q{c[1]}-H{c[3]}/{c[4]}-D{c[5]}-{c[6]}-{c[7]}-p{c[8]}")
+def test_paged_decode_e4m3_cache(case):
+    # The cache's e4m3 values widen exactly to the 16-bit type, so the oracle on the dequantised
+    # cache and the 16-bit tolerance apply (the probabilities stay 16-bit)
+    B, Sq, lk, H, H_kv, D, dtype, mask, ps = case
+    inp = make_paged(5400 + sum(lk) + ps, B, Sq, lk, H, H_kv, D, dtype, ps, mask=mask, kv_dtype="f8e4m3")
+    log(f"[case] paged e4m3 cache {case} seed={inp.seed} k_scale={inp.k_scale:.4g} v_scale={inp.v_scale:.4g}")
+    res = run_paged(inp)
+    assert res.status == 0
+    o, lse = oracle_paged(inp)
+    compare(f"paged e4m3 cache {case}", res.o_bits, dtype, o, res.lse, lse)

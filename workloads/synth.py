@@ -243,6 +243,7 @@ class PagedInputs:
     q_scale: float = 1.0
     k_scale: float = 1.0
     v_scale: float = 1.0
+    kv_dtype: str = ""  # element type of the cache ("" = dtype)
 
     @property
     def Sk(self) -> int:
@@ -268,20 +269,22 @@ class PagedInputs:
 
 def make_paged(seed: int, B: int, Sq: int, seqlens_k: Sequence[int], H: int, H_kv: int, D: int, dtype: str,
                page_size: int, mask: str = "none", extra_pages: int = 3, poison: bool = True,
-               scale: Optional[float] = None, o_scale: float = 1.0) -> PagedInputs:
+               scale: Optional[float] = None, o_scale: float = 1.0, kv_dtype: Optional[str] = None) -> PagedInputs:
     """Dense Q and a paged K/V cache.  Draws Q, then the whole K cache, then the V cache (N(0, 1)), then
     a random permutation that deals the physical pages out to the sequences' logical pages in order.
     ``extra_pages`` pages belong to no sequence; with ``poison`` they, and the rows of each last page
-    past its sequence's end, hold NaN."""
+    past its sequence's end, hold NaN.  ``kv_dtype="f8e4m3"`` quantises each cache per tensor (the
+    scale from the rows the sequences own)."""
     rng = np.random.default_rng(seed)
     lk = np.asarray(seqlens_k, dtype=np.int32)
     assert lk.shape == (B,)
     pages_b = [-(-int(s) // page_size) for s in lk]
     num_pages = sum(pages_b) + int(extra_pages)
     max_pages = max(pages_b + [1])
+    kv_dtype = kv_dtype or dtype
     q, _ = _to_storage(draw_normal(rng, (B, Sq, H, D)), dtype)
-    kc, _ = _to_storage(draw_normal(rng, (num_pages, page_size, H_kv, D)), dtype)
-    vc, _ = _to_storage(draw_normal(rng, (num_pages, page_size, H_kv, D)), dtype)
+    k32 = draw_normal(rng, (num_pages, page_size, H_kv, D))
+    v32 = draw_normal(rng, (num_pages, page_size, H_kv, D))
     perm = rng.permutation(num_pages).astype(np.int32)
     table = np.full((B, max_pages), -1, dtype=np.int32)
     used = np.zeros((num_pages, page_size), dtype=bool)
@@ -293,14 +296,28 @@ def make_paged(seed: int, B: int, Sq: int, seqlens_k: Sequence[int], H: int, H_k
             table[b, i] = pg
             rows = min(page_size, int(lk[b]) - i * page_size)
             used[pg, :rows] = True
+    sk = sv = 1.0
+    if kv_dtype == "f8e4m3":
+        _, sk = quantize_e4m3(torch.from_numpy(k32[used]))
+        _, sv = quantize_e4m3(torch.from_numpy(v32[used]))
+        kc = (torch.from_numpy(k32) / sk).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+        vc = (torch.from_numpy(v32) / sv).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    else:
+        kc, _ = _to_storage(k32, kv_dtype)
+        vc, _ = _to_storage(v32, kv_dtype)
     if poison:
-        kc[torch.from_numpy(~used)] = float("nan")
-        vc[torch.from_numpy(~used)] = float("nan")
+        unused = torch.from_numpy(~used)
+        if kv_dtype == "f8e4m3":  # 0x7F: e4m3fn NaN
+            kc.view(torch.uint8)[unused] = 0x7F
+            vc.view(torch.uint8)[unused] = 0x7F
+        else:
+            kc[unused] = float("nan")
+            vc[unused] = float("nan")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     return PagedInputs(q=q, k_cache=kc, v_cache=vc, block_table=table, seqlens_k=lk, page_size=int(page_size), B=B,
                        Sq=Sq, H=H, H_kv=H_kv, D=D, dtype=dtype, mask=mask, scale=float(scale),
-                       o_scale=float(o_scale), seed=seed)
+                       o_scale=float(o_scale), seed=seed, k_scale=float(sk), v_scale=float(sv), kv_dtype=kv_dtype)
 
 
 def make_varlen(seed: int, seqlens_q: Sequence[int], seqlens_k: Sequence[int], H: int, H_kv: int, D: int,
@@ -348,7 +365,8 @@ def make_varlen(seed: int, seqlens_q: Sequence[int], seqlens_k: Sequence[int], H
 
 # The measured workloads.  Config 4 is run twice on the same inputs (residual, then causal-qend);
 # config 6 is the split-KV (decode) entry point's workload; config 7 is the backward pass (fmha_bwd)
-# of config 2's shape; config 8 is config 6 over a paged cache (fmha_fwd_splitkv_paged).
+# of config 2's shape; config 8 is config 6 over a paged cache (fmha_fwd_splitkv_paged), config 9
+# the same over an e4m3 cache.
 CONFIGS = {
     1: dict(name="tiny dense fp16 D64 no mask", kind="dense", B=1, H=2, H_kv=2, Sq=128, Sk=128, D=64,
             dtype="f16", mask="none", lse=False, o_scale=1.0),
@@ -372,6 +390,10 @@ CONFIGS = {
     8: dict(name="paged decode GQA bf16 D128, 1 token vs 8192 keys, 128-key pages", kind="paged",
             entry="splitkv_paged", B=16, H=32, H_kv=8, Sq=1, Sk=8192, D=128, page_size=128, dtype="bf16",
             mask="none", lse=True, o_scale=1.0),
+    # The same over an e4m3 cache (per-tensor scales), bf16 queries and output.
+    9: dict(name="paged decode GQA bf16 D128 over an e4m3 cache, 1 token vs 8192 keys, 128-key pages",
+            kind="paged", entry="splitkv_paged", B=16, H=32, H_kv=8, Sq=1, Sk=8192, D=128, page_size=128,
+            dtype="bf16", kv_dtype="f8e4m3", mask="none", lse=True, o_scale=1.0),
 }
 
 
@@ -380,7 +402,8 @@ def make_config(config_id: int, seed: Optional[int] = None, mask: Optional[str] 
     seed = config_seed(config_id) if seed is None else seed
     if c["kind"] == "paged":
         return make_paged(seed, c["B"], c["Sq"], [c["Sk"]] * c["B"], c["H"], c["H_kv"], c["D"], c["dtype"],
-                          c["page_size"], mask=mask or c["mask"], extra_pages=0, poison=False, o_scale=c["o_scale"])
+                          c["page_size"], mask=mask or c["mask"], extra_pages=0, poison=False, o_scale=c["o_scale"],
+                          kv_dtype=c.get("kv_dtype"))
     if c["kind"] == "dense":
         return make_dense(seed, c["B"], c["Sq"], c["Sk"], c["H"], c["H_kv"], c["D"], c["dtype"],
                           mask=mask or c["mask"], o_scale=c["o_scale"])
