@@ -90,12 +90,17 @@ __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// 16-byte chunk swizzle of a K/V tile row j in LDS (CPR chunks per row).  Rows 0..15 map
-// to distinct chunks, so the 32-row b128 reads of K spread over all banks; four
-// consecutive rows move whole chunk pairs, so the 4-row transpose reads of V do too.
+// 16-byte chunk swizzle of a K/V/Q tile row j in LDS (CPR chunks per row), for the 64
+// four-byte banks of the gfx950 LDS, which serve a b128 read 16 lanes at a time and a b64 read
+// 32 lanes at a time.  Row j's chunks are XORed with a value of bits 0..3 of j only (so rows
+// 16 apart share it): the 16 rows of a b128 group land on 16 distinct bank groups for the
+// row-wise operand reads, and the 4 rows x 4 chunks of a 32-lane ds_read_b64_tr_b16 group
+// cover all 64 banks for the transposed reads.
 template <int CPR>
 __device__ inline int swz(int j) {
-  return (2 * (j & 3) + ((j >> 2) & 1) + 8 * ((j >> 3) & 1)) & (CPR - 1);
+  if constexpr (CPR >= 16) return (((j & 3) << 2) | ((j >> 2) & 3)) & (CPR - 1);
+  if constexpr (CPR == 8) return (((j >> 1) & 1) << 2) | ((j >> 2) & 3);
+  return (j >> 2) & 3;
 }
 
 template <int DT>

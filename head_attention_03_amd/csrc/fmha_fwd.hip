@@ -484,6 +484,11 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // (plain steps): every row of every wave sees the whole tile.
   auto softmax_phase = [&](int t, auto& hook, auto maskable_tag) __attribute__((always_inline)) {
     constexpr bool MASKABLE = decltype(maskable_tag)::value;
+    // The scores are pinned again here, after the phase barrier, so that the row max (which
+    // waits for the last S^T MFMA) cannot be hoisted into the matrix phase: there it held the
+    // wave back from the barrier while its last MFMAs drained, and the other group's matrix
+    // work started only after that.  Issued MFMAs complete across a barrier by themselves.
+    asm volatile("" : "+v"(s[0]), "+v"(s[1]));
     if (MASKABLE && t >= w_full) {  // some key of the tile is hidden from some row of the wave
       // score (jb, r) belongs to key t kBN + 4 h32 + 32 jb + 8 (r / 4) + r % 4
       const int lim = vis_last - t * kBN;
