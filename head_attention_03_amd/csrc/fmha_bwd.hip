@@ -13,12 +13,14 @@
 // masked positions carrying P = 0 (the backward mask of the walk-through's fusion-point
 // section: the forward masks with the causal offset 0 or Sk - Sq).
 //
-// CDNA4 design (three kernels, no atomics, deterministic):
-// * stats_kernel: delta_i and LSE_i * log2(e) (+inf for a row with no key) into a workspace of
-//   64-row blocks [lse2[64], delta[64]]; the rows past a sequence's end in its last block get
-//   +inf and 0, so the kernels below read whole blocks and padding rows yield P = 0.
+// CDNA4 design (two kernels, no atomics, deterministic):
 // * dq_kernel: a workgroup owns 256 query rows of one (sequence, head), 32 per wave, with its Q
-//   and dO rows held as MFMA B operands in registers; 64-key K/V tiles stream through a 3-stage
+//   and dO rows held as MFMA B operands in registers.  It first forms the rows' statistics,
+//   delta_i and LSE_i * log2(e) (+inf for a row with no key), from its dO fragment and the same
+//   fragment of O (the walk-through's row sum of O * dO, so it needs no kernel of its own), and
+//   stores them in a workspace of 64-row blocks [lse2[64], delta[64]] for the dK/dV kernel; the
+//   rows past a sequence's end in its last block get +inf and 0, so that kernel reads whole
+//   blocks and padding rows yield P = 0.  64-key K/V tiles stream through a 3-stage
 //   LDS ring (LDS-direct loads, one barrier per tile).  S^T = K Q^T and dP^T = V dO^T run on
 //   v_mfma_f32_32x32x16 with K and V read row-wise from LDS; the accumulator layout of dS^T is
 //   the B operand of dQ^T += K^T dS^T, whose A operand is K read transposed with
@@ -81,7 +83,7 @@ struct Params {
   int32_t total_q;       // packed: LSE row length; dense: 0
   int32_t aux_bstride;   // dense: blocks per sequence (H * ceil(Sq / 64)); packed: 0
   int32_t aux_hstride;   // blocks between consecutive heads of one sequence
-  int32_t n_tiles;       // stats: 64-row blocks per sequence; dq: q tiles; dkdv: key tiles
+  int32_t n_tiles;       // dq: q tiles per sequence; dkdv: key tiles
   int32_t xcd_per;       // (sequence, head) pairs per XCD when their count is a multiple of 8
   int32_t causal, qend;
   float scale, scale_log2;
@@ -188,53 +190,6 @@ __device__ inline void row_chains(f32x16 (&c)[NC], const uint32_t (&base)[NC], c
 }
 
 // ------------------------------------------------------------------------------------------
-// stats kernel: one 64-row block of one (sequence, head) per workgroup of 256 threads
-// ------------------------------------------------------------------------------------------
-template <int DT, int D>
-__global__ __launch_bounds__(256) void stats_kernel(const Params p) {
-  constexpr int CPR = D / 8;      // 16-byte chunks per row
-  constexpr int RPP = 256 / CPR;  // rows per pass
-  typedef Elem<DT> T;
-  const int h = blockIdx.y;
-  const int b = blockIdx.x / p.n_tiles;
-  const int qt = blockIdx.x - b * p.n_tiles;
-  const Seq sq = seq_bounds(p, b);
-  if (qt * kAuxRows >= sq.Sq_b) return;
-  float* blk = p.aux + (size_t)(aux_seq_base(p, b, sq.q_row0) + h * p.aux_hstride + qt) * (kAuxBlock / 4);
-  const int c = threadIdx.x % CPR;
-  const int rr = threadIdx.x / CPR;
-#pragma unroll
-  for (int pass = 0; pass < kAuxRows / RPP; ++pass) {
-    const int row = pass * RPP + rr;
-    const int qi = qt * kAuxRows + row;
-    float s = 0.0f;
-    if (qi < sq.Sq_b) {
-      const size_t e = ((size_t)(sq.q_row0 + qi) * p.H + h) * D + 8 * c;
-      const i32x4 o = *(const i32x4*)((const char*)p.o + 2 * e);
-      const i32x4 g = *(const i32x4*)((const char*)p.dout + 2 * e);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        s = __builtin_fmaf(T::lo((uint32_t)o[u]), T::lo((uint32_t)g[u]), s);
-        s = __builtin_fmaf(T::hi((uint32_t)o[u]), T::hi((uint32_t)g[u]), s);
-      }
-    }
-#pragma unroll
-    for (int m = CPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-    if (c == 0) {
-      float l2 = __builtin_inff(), dl = 0.0f;
-      if (qi < sq.Sq_b) {
-        const float L = p.lse[p.cu_q ? (size_t)h * p.total_q + sq.q_row0 + qi
-                                     : ((size_t)b * p.H + h) * p.Sq + qi];
-        l2 = L == -__builtin_inff() ? __builtin_inff() : L * 1.4426950408889634f;
-        dl = s;
-      }
-      blk[row] = l2;
-      blk[kAuxRows + row] = dl;
-    }
-  }
-}
-
-// ------------------------------------------------------------------------------------------
 // dQ kernel: grid = B * H * n_tiles workgroups of kQThreads
 // ------------------------------------------------------------------------------------------
 template <int DT, int D>
@@ -302,11 +257,34 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_kernel(const Params p) {
     qf[ks] = load_b128(rq, frag + 32 * ks);
     dof[ks] = load_b128(rdo, frag + 32 * ks);
   }
+  // The row's statistics: delta = sum over the head dimension of O * dO (this lane holds half
+  // the dims of its row, lane l ^ 32 the other half) and the LSE in log2 units.  Every lane of
+  // the lower half stores its row into the workspace block of the dK/dV kernel when the block
+  // holds a row of the sequence, as +inf and 0 past the sequence's end.
   float lse2 = __builtin_inff(), delta = 0.0f;
-  if (qi < sq.Sq_b) {
-    const float* blk = p.aux + (size_t)(aux_seq_base(p, b, sq.q_row0) + h * p.aux_hstride + (qi >> 6)) * (kAuxBlock / 4);
-    lse2 = blk[qi & 63];
-    delta = blk[kAuxRows + (qi & 63)];
+  {
+    const auto ro = make_rsrc((const char*)p.o + q_base, q_bytes);
+    float s = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const i32x4 of = load_b128(ro, frag + 32 * ks);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s = __builtin_fmaf(T::lo((uint32_t)of[u]), T::lo((uint32_t)dof[ks][u]), s);
+        s = __builtin_fmaf(T::hi((uint32_t)of[u]), T::hi((uint32_t)dof[ks][u]), s);
+      }
+    }
+    s = wave_row_sum(s);
+    if (qi < sq.Sq_b) {
+      const float L = p.lse[p.cu_q ? (size_t)h * p.total_q + sq.q_row0 + qi : ((size_t)b * p.H + h) * p.Sq + qi];
+      lse2 = L == -__builtin_inff() ? __builtin_inff() : L * 1.4426950408889634f;
+      delta = s;
+    }
+    if (h32 == 0 && (qi & ~(kAuxRows - 1)) < sq.Sq_b) {
+      float* blk = p.aux + (size_t)(aux_seq_base(p, b, sq.q_row0) + h * p.aux_hstride + qi / kAuxRows) * (kAuxBlock / 4);
+      blk[qi % kAuxRows] = lse2;
+      blk[kAuxRows + qi % kAuxRows] = delta;
+    }
   }
 
   // tile loads: load g of a step (0 .. 2 TBLK - 1; K first, then V) is wave g % kQWaves's
@@ -599,19 +577,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
 }
 
 template <int DT, int D>
-hipError_t launch(Params p, int n_aux_tiles, int n_q_tiles, int n_k_tiles, bool have_q, bool have_k,
-                  hipStream_t stream) {
-  if (have_q) {
-    p.n_tiles = n_aux_tiles;
-    hipLaunchKernelGGL((stats_kernel<DT, D>), dim3((unsigned)(p.B * n_aux_tiles), (unsigned)p.H), dim3(256), 0,
-                       stream, p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+hipError_t launch(Params p, int n_q_tiles, int n_k_tiles, bool have_q, bool have_k, hipStream_t stream) {
+  if (have_q) {  // dQ and the row statistics; the dK/dV kernel after it reads the statistics
     const int64_t pairs = (int64_t)p.B * p.H;
     p.n_tiles = n_q_tiles;
     p.xcd_per = pairs % 8 == 0 ? (int32_t)(pairs / 8) : 0;
     hipLaunchKernelGGL((dq_kernel<DT, D>), dim3((unsigned)(pairs * n_q_tiles)), dim3(kQThreads), 0, stream, p);
-    err = hipGetLastError();
+    const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (have_k) {
@@ -632,7 +604,6 @@ fmha_status plan(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int
   if (H > 0 && (H_kv < 1 || H % H_kv != 0)) return FMHA_ERR_INVALID_SHAPE;
   if (D != 32 && D != 64 && D != 128) return FMHA_ERR_INVALID_SHAPE;
   if (packed && (varlen->total_length_q < 0 || varlen->total_length_k < 0)) return FMHA_ERR_INVALID_SHAPE;
-  if (H > 65535) return FMHA_ERR_UNSUPPORTED;  // the statistics grid's y dimension
   const int64_t rows_q = packed ? varlen->total_length_q : Sq;
   const int64_t rows_k = packed ? varlen->total_length_k : Sk;
   const int64_t lim = (int64_t)1 << 31;
@@ -711,11 +682,10 @@ fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o,
     if ((uintptr_t)workspace & 15) return FMHA_ERR_MISALIGNED;
     if (have_q && workspace_bytes < need) return FMHA_ERR_INVALID_ARGUMENT;
   }
-  const int64_t n_aux = (Sq + kAuxRows - 1) / kAuxRows;
   const int64_t n_q = (Sq + kQM - 1) / kQM;
   const int64_t n_k = (Sk + kKvN - 1) / kKvN;
   const int64_t lim = (int64_t)1 << 31;
-  if ((int64_t)B * n_aux >= lim || (int64_t)B * H * n_q >= lim || (int64_t)B * H_kv * n_k >= lim)
+  if ((int64_t)B * H * n_q >= lim || (int64_t)B * H_kv * n_k >= lim)
     return FMHA_ERR_UNSUPPORTED;
 
   p.q = q;
@@ -739,15 +709,15 @@ fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o,
   p.n_tiles = 0;
 
   hipError_t err = hipSuccess;
-  const int a = (int)n_aux, nq = (int)n_q, nk = (int)n_k;
+  const int nq = (int)n_q, nk = (int)n_k;
   if (dtype == FMHA_DTYPE_BF16) {
-    if (D == 32) err = launch<fmha::kBF16, 32>(p, a, nq, nk, have_q, have_k, stream);
-    if (D == 64) err = launch<fmha::kBF16, 64>(p, a, nq, nk, have_q, have_k, stream);
-    if (D == 128) err = launch<fmha::kBF16, 128>(p, a, nq, nk, have_q, have_k, stream);
+    if (D == 32) err = launch<fmha::kBF16, 32>(p, nq, nk, have_q, have_k, stream);
+    if (D == 64) err = launch<fmha::kBF16, 64>(p, nq, nk, have_q, have_k, stream);
+    if (D == 128) err = launch<fmha::kBF16, 128>(p, nq, nk, have_q, have_k, stream);
   } else {
-    if (D == 32) err = launch<fmha::kF16, 32>(p, a, nq, nk, have_q, have_k, stream);
-    if (D == 64) err = launch<fmha::kF16, 64>(p, a, nq, nk, have_q, have_k, stream);
-    if (D == 128) err = launch<fmha::kF16, 128>(p, a, nq, nk, have_q, have_k, stream);
+    if (D == 32) err = launch<fmha::kF16, 32>(p, nq, nk, have_q, have_k, stream);
+    if (D == 64) err = launch<fmha::kF16, 64>(p, nq, nk, have_q, have_k, stream);
+    if (D == 128) err = launch<fmha::kF16, 128>(p, nq, nk, have_q, have_k, stream);
   }
   return err == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
 }

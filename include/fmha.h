@@ -168,8 +168,8 @@ size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_
  * per (sequence, head), after the backward of the CUTLASS Blackwell FMHA example (trdm.cn
  * walk-through "CUTLASS Blackwell FMHA 示例完全解析", section "FMHA for Blackwell: Backward":
  * a row sum of O * dO, the main dQ/dK/dV pass, dQ converted to the output type; masks as that
- * section's backward mask, i.e. the forward masks).  Three kernels run on `stream`: the row
- * statistics, dQ, and dK/dV.  No atomics: results are bitwise repeatable.  With GQA/MQA
+ * section's backward mask, i.e. the forward masks).  Two kernels run on `stream`: dQ (which
+ * also forms the row statistics), then dK/dV.  No atomics: results are bitwise repeatable.  With GQA/MQA
  * (H_kv < H), dk and dv of a K/V head are the sums over its group of query heads (the
  * CUTLASS backward does not support GQA; this is the gradient of the shared head).
  *
@@ -191,8 +191,7 @@ size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_
  * Errors as fmha_fwd (o, dout, lse and dq are required when there are query rows; k, v, dk and
  * dv when there are keys; all but lse 16-byte aligned), and: workspace NULL ->
  * FMHA_ERR_NULL_POINTER, not 16-byte aligned -> FMHA_ERR_MISALIGNED, smaller than needed ->
- * FMHA_ERR_INVALID_ARGUMENT (checked when there are query rows), H > 65535 ->
- * FMHA_ERR_UNSUPPORTED.  With query rows but no keys dq is zeroed; with keys but no query rows
+ * FMHA_ERR_INVALID_ARGUMENT (checked when there are query rows).  With query rows but no keys dq is zeroed; with keys but no query rows
  * dk and dv are zeroed.  Rows and keys outside the sequences are never touched.
  */
 fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
