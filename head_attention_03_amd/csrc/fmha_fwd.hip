@@ -492,31 +492,34 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
         }
       }
     } else {
+    // fp8: the S^T MFMAs first, then the PV MFMAs, so the tile's row max (in the softmax code,
+    // free to move here) runs on the vector ALU while the PV products execute: in fp8 the
+    // softmax phase, not the matrix phase, sets the step.
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      if (i < NQK) qk_mma(ka, kb, i);
-      if (i < NPV) pv_mma(va0, va1, i);
+    for (int i = 0; i < NQK; ++i) qk_mma(ka, kb, i);
 #pragma unroll
-      for (int j = 0; j < LPP; ++j)  // load j goes after step j * N / LPP
-        if ((j * N) / LPP == i) hook(j);
+    for (int i = 0; i < NPV; ++i) {
+      pv_mma(va0, va1, i);
+#pragma unroll
+      for (int j = 0; j < LPP; ++j)  // load j goes after PV step j * NPV / LPP
+        if ((j * NPV) / LPP == i) hook(j);
     }
     // The LDS reads run kPrefetch reads ahead of the MFMAs that consume them (pinned with
     // scheduling groups: the compiler alone keeps only one or two in flight, which leaves
     // the matrix core waiting on LDS latency).
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      if (i < NQK) {
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RQK, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      if (i == NDB - 1)  // this step also adds the row sums
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      else
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RQK, 0);
-      }
-      if (i < NPV) {
-        if (F8 && i == NDB - 1)  // this step also adds the row sums
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-        else
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPV, 0);
-      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPV, 0);
     }
     }
     // Pin the products here: the compiler may otherwise sink MFMAs past the phase barrier,
@@ -544,11 +547,12 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // (plain steps): every row of every wave sees the whole tile.
   auto softmax_phase = [&](int t, auto& hook, auto maskable_tag) __attribute__((always_inline)) {
     constexpr bool MASKABLE = decltype(maskable_tag)::value;
-    // The scores are pinned again here, after the phase barrier, so that the row max (which
-    // waits for the last S^T MFMA) cannot be hoisted into the matrix phase: there it held the
-    // wave back from the barrier while its last MFMAs drained, and the other group's matrix
-    // work started only after that.  Issued MFMAs complete across a barrier by themselves.
-    asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+    // 16-bit: the scores are pinned again here, after the phase barrier, so that the row max
+    // (which waits for the last S^T MFMA) cannot be hoisted into the matrix phase: there it
+    // held the wave back from the barrier while its last MFMAs drained, and the other group's
+    // matrix work started only after that.  Issued MFMAs complete across a barrier by
+    // themselves.  (fp8 issues its S^T MFMAs first and lets the max move up.)
+    if constexpr (!F8) asm volatile("" : "+v"(s[0]), "+v"(s[1]));
     if (MASKABLE && t >= w_full) {  // some key of the tile is hidden from some row of the wave
       // score (jb, r) belongs to key t kBN + 4 h32 + 32 jb + 8 (r / 4) + r % 4
       const int lim = vis_last - t * kBN;
