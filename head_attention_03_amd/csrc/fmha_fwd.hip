@@ -67,7 +67,7 @@ namespace fmha {
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
-constexpr int kBN = 64;           // keys per K/V tile
+constexpr int kBN = 64;           // keys per K/V tile (16-bit; fp8 tiles hold 2 kBN keys, the same bytes)
 // fp8 probabilities are shifted up by 2^kF8Shift before the e4m3 conversion (and the running
 // max is raised past 2^kF8Threshold), so they span [2^-9, 2^8] with e4m3 normals covering
 // down to 2^-6 below the running max of the row, instead of most of a long row's weights
@@ -115,7 +115,9 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   constexpr int E = F8 ? 1 : 2;    // bytes per element
   constexpr int RB = D * E;        // bytes per K/V row, in memory and in LDS (swizzled)
   constexpr int CPR = RB / 16;     // 16-byte chunks per row
-  constexpr int TILE = kBN * RB;   // LDS bytes per K or V tile
+  constexpr int BN = F8 ? 2 * kBN : kBN;  // keys per K/V tile
+  constexpr int NJB = BN / 32;     // 32-key blocks of a tile (S^T accumulators per wave)
+  constexpr int TILE = BN * RB;    // LDS bytes per K or V tile
   constexpr int KBLK = TILE / 1024;  // 1 KiB LDS-direct loads (64 lanes x 16 B) per K or V tile
   constexpr int NBLK = 2 * KBLK;
   constexpr int NSTAGE = 3;          // K/V tile pairs resident in LDS: in use, landed, landing
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // gets a tile of masked scores, hence O = 0 and LSE = -inf)
   auto item_tiles = [&](int k) __attribute__((always_inline)) {
     const int e = key_end(min(Sq_b, item_q0(k) + kBM) - 1);
-    return e > 0 ? (e + kBN - 1) / kBN : 1;
+    return e > 0 ? (e + BN - 1) / BN : 1;
   };
   int n_stream = 0;  // K/V tiles of the whole stream
   for (int k = 0; k < n_items; ++k) n_stream += item_tiles(k);
@@ -223,14 +225,14 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     w_full = 0x7fffffff;  // a wave with no row in the sequence: its output is dropped anyway
     if (qw0 < Sq_b) {
       const int first_sees = p.causal ? min(Sk_b, qw0 + off + 1) : Sk_b;
-      w_full = first_sees > 0 ? first_sees / kBN : 0;
+      w_full = first_sees > 0 ? first_sees / BN : 0;
     }
     vis_last = (p.causal ? min(Sk_b - 1, qi + off) : Sk_b - 1) - 4 * h32;
   };
   set_rows(0);
   auto item_full = [&](int k) __attribute__((always_inline)) {
     const int first_sees = p.causal ? min(Sk_b, item_q0(k) + off + 1) : Sk_b;
-    return first_sees > 0 ? first_sees / kBN : 0;
+    return first_sees > 0 ? first_sees / BN : 0;
   };
 
   // ---- Q: each wave's 32 rows of an item land in its own LDS block (LDS-direct loads,
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // (tile -1 before the first; past the last item the K tile index runs on past its end), as
   // byte offsets in the K/V rows, and the LDS address of stage c % 3 plus this wave's first
   // block.  Kept as running sums: the loop carries no multiplies or remainders for them.
-  const uint32_t tile_bytes = (uint32_t)kBN * kstride;
+  const uint32_t tile_bytes = (uint32_t)BN * kstride;
   constexpr uint32_t kStages = NSTAGE * STAGE;
   static_assert(7 * 1024 < STAGE, "a wave's block offset stays inside the first stage");
   int lt = 0, ln = item_tiles(0), litem = 0;
@@ -313,9 +315,9 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   f32x16 acc_o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
-  f32x16 s[2];                      // scores of the tile between its matrix and softmax phases
+  f32x16 s[NJB];                    // scores of the tile between its matrix and softmax phases
   constexpr int NPK = F8 ? 4 : 8;   // packed probability registers per 32-key block
-  uint32_t pk[2][NPK] = {};         // probabilities of the tile between its softmax and PV phases
+  uint32_t pk[NJB][NPK] = {};       // probabilities of the tile between its softmax and PV phases
   bool pk_masked = false;           // 16-bit: pk holds a masked tile, whose row sum the matrix cores add
   float m_run = -__builtin_inff();  // running max of scale*log2(e)*s for query l32
   // Row sums on the matrix cores: an all-ones A operand against the probability operand of
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // one QK^T MFMA of the tile: k-step ks of key block jb (ka, kb: k_lane, k_lane2 + the
   // stage's address)
   auto qk_mma = [&](uint32_t ka, uint32_t kb, int i) __attribute__((always_inline)) {
-    const int jb = i & 1, ks = i >> 1;
+    const int jb = i % NJB, ks = i / NJB;
     if constexpr (F8) {
       const i32x4 a0 = *(const lds_i32x4*)(uintptr_t)((ka ^ (64 * ks)) + 32 * jb * RB);
       const i32x4 a1 = *(const lds_i32x4*)(uintptr_t)((kb ^ (64 * ks)) + 32 * jb * RB);
@@ -379,20 +381,23 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       s[jb] = T::mma(a, qf[ks], s[jb]);
     }
   };
-  // one PV MFMA.  16-bit: d-block db, 16-key chunk (jb, c).  fp8: d-block i, all 64 keys; byte
-  // 8 c + r of either operand is key 16 c + 8 h32 + r (the probabilities are regrouped to
-  // this order at the end of the softmax, and the transposed V reads deliver it).
+  // one PV MFMA.  16-bit: d-block db, 16-key chunk (jb, c).  fp8: d-block i % NDB, 64-key half
+  // kh = i / NDB of the 128-key tile; byte 8 c + r of either operand is key 64 kh + 16 c + 8 h32
+  // + r (the probabilities are regrouped to this order at the end of the softmax, and the
+  // transposed V reads deliver it).
   auto pv_mma = [&](uint32_t va0, uint32_t va1, int i) __attribute__((always_inline)) {
     if constexpr (F8) {
+      const int db = i % NDB, kh = i / NDB;
       i32x2 t[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        t[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)((va0 ^ (32 * i)) + 16 * c * RB));
+        t[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_i32x2*)(uintptr_t)((va0 ^ (32 * db)) + (64 * kh + 16 * c) * RB));
       const i32x8 a = {t[0][0], t[0][1], t[1][0], t[1][1], t[2][0], t[2][1], t[3][0], t[3][1]};
-      const i32x8 b = {(int)pk[0][0], (int)pk[0][1], (int)pk[0][2], (int)pk[0][3],
-                       (int)pk[1][0], (int)pk[1][1], (int)pk[1][2], (int)pk[1][3]};
-      acc_o[i] = mma_f8(a, b, acc_o[i]);
-      if (i == NDB - 1) {  // row sums: e4m3 1.0 = 0x38
+      const i32x8 b = {(int)pk[2 * kh][0], (int)pk[2 * kh][1], (int)pk[2 * kh][2], (int)pk[2 * kh][3],
+                       (int)pk[2 * kh + 1][0], (int)pk[2 * kh + 1][1], (int)pk[2 * kh + 1][2], (int)pk[2 * kh + 1][3]};
+      acc_o[db] = mma_f8(a, b, acc_o[db]);
+      if (db == NDB - 1) {  // row sums of this half: e4m3 1.0 = 0x38
         const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                             0x38383838, 0x38383838, 0x38383838, 0x38383838};
         acc_l = mma_f8(ones, b, acc_l);
@@ -410,8 +415,8 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     const i32x4 bp = {(int)pk[jb][4 * c], (int)pk[jb][4 * c + 1], (int)pk[jb][4 * c + 2], (int)pk[jb][4 * c + 3]};
     acc_o[db] = T::mma(a, bp, acc_o[db]);
   };
-  constexpr int NQK = 2 * KS;                // MFMAs of S^T for one tile
-  constexpr int NPV = F8 ? NDB : 4 * NDB;    // MFMAs of O^T += V^T P^T for one tile
+  constexpr int NQK = NJB * KS;              // MFMAs of S^T for one tile
+  constexpr int NPV = F8 ? 2 * NDB : 4 * NDB;  // MFMAs of O^T += V^T P^T for one tile
   constexpr int RQK = F8 ? 2 : 1;            // LDS reads per S^T MFMA
   constexpr int RPV = F8 ? 4 : 2;            // LDS reads per O^T MFMA
 
@@ -433,8 +438,8 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       asm volatile("" : "+v"(ka), "+v"(kb), "+v"(va0));
     else
       asm volatile("" : "+v"(ka), "+v"(va0), "+v"(va1));
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) s[jb] = f32x16{};
     if constexpr (!F8) {
       // 16-bit: an explicit software pipeline.  Each b128 K read is issued kKLead S^T MFMAs
       // before its use (four 4-register buffers), each pair of V^T transpose reads kVLead PV
@@ -515,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     }
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
-      if (i == NDB - 1)  // this step also adds the row sums
+      if (i % NDB == NDB - 1)  // this step also adds the row sums of its 64 keys
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
       else
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
@@ -524,7 +529,8 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     }
     // Pin the products here: the compiler may otherwise sink MFMAs past the phase barrier,
     // into the softmax or the epilogue of an item that follows on this wave.
-    asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) asm volatile("" : "+v"(s[jb]));
 #pragma unroll
     for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(acc_o[db]));
     if constexpr (!F8 && MASKABLE) {
@@ -554,17 +560,17 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     // themselves.  (fp8 issues its S^T MFMAs first and lets the max move up.)
     if constexpr (!F8) asm volatile("" : "+v"(s[0]), "+v"(s[1]));
     if (MASKABLE && t >= w_full) {  // some key of the tile is hidden from some row of the wave
-      // score (jb, r) belongs to key t kBN + 4 h32 + 32 jb + 8 (r / 4) + r % 4
-      const int lim = vis_last - t * kBN;
+      // score (jb, r) belongs to key t BN + 4 h32 + 32 jb + 8 (r / 4) + r % 4
+      const int lim = vis_last - t * BN;
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
+      for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           s[jb][r] = 32 * jb + 8 * (r >> 2) + (r & 3) <= lim ? s[jb][r] : -__builtin_inff();
     }
     float mx = s[0][0];
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[jb][r]);
     mx = wave_row_max(mx);
@@ -587,7 +593,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     auto exps = [&](auto masked_tag) __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
+      for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {  // scores 4 qd .. 4 qd + 3: keys 8 qd + 4 h32 + 0..3
           float e[4];
@@ -604,8 +610,8 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
             l_run2 += e[1] + e[3];
           }
 #pragma unroll
-          for (int j = 0; j < LPP; ++j)  // load j goes after exponential quad j * 8 / LPP
-            if ((j * 8) / LPP == 4 * jb + qd) hook(j);
+          for (int j = 0; j < LPP; ++j)  // load j goes after exponential quad j * 4 NJB / LPP
+            if ((j * 4 * NJB) / LPP == 4 * jb + qd) hook(j);
         }
     };
     if constexpr (F8) {
@@ -624,7 +630,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       // Regroup to 8 consecutive keys per lane and 16-key chunk (the fp8 PV operand order):
       // lane h32 = 0 trades its keys 8..11 of each chunk for keys 4..7 of lane l + 32.
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
+      for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           auto r = __builtin_amdgcn_permlane32_swap(pk[jb][2 * m], pk[jb][2 * m + 1], false, false);
@@ -635,7 +641,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     // Pin the results here: the compiler may otherwise sink the tail of this arithmetic past
     // the phase barrier, into the matrix phase that follows on this wave.
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
       for (int q = 0; q < NPK; ++q) asm volatile("" : "+v"(pk[jb][q]));
     asm volatile("" : "+v"(m_run));
@@ -931,7 +937,7 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
   if (rows_q * H * D * esz >= lim || rows_k * H_kv * D * esz >= lim) return FMHA_ERR_UNSUPPORTED;
   // tiles requested one before and two past the keys, and the rows of a partial last q-tile
   // past the end of a sequence, must not wrap the 32-bit offset
-  if ((int64_t)3 * kBN * H_kv * D * esz >= lim || (int64_t)kBM * H * D * esz >= lim) return FMHA_ERR_UNSUPPORTED;
+  if ((int64_t)3 * (esz == 1 ? 2 * kBN : kBN) * H_kv * D * esz >= lim || (int64_t)kBM * H * D * esz >= lim) return FMHA_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || Sq == 0 || (packed && varlen->total_length_q == 0)) return FMHA_OK;
 
   Params p;
