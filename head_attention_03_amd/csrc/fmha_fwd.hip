@@ -12,9 +12,9 @@
 //
 // * One workgroup = 8 waves of 64 lanes; a q-tile is 256 query rows (32 per wave) of one
 //   (sequence, head).  The two halves of the workgroup ping-pong between the matrix cores
-//   and the vector ALU (the phase schedule above the kernel).  K/V tiles of 64 keys stream
-//   through three LDS stages, filled by buffer loads that write LDS directly (no VGPR
-//   staging).  The buffer descriptor bounds every load to the rows of the current
+//   and the vector ALU (the phase schedule above the kernel).  K/V tiles of 64 keys (fp8:
+//   128, the same bytes) stream through three LDS stages, filled by buffer loads that write
+//   LDS directly (no VGPR staging).  The buffer descriptor bounds every load to the rows of the current
 //   sequence: rows past the end read as 0, which is how ragged tails and packed sequences
 //   are handled without touching neighbouring memory.
 // * A workgroup runs up to 8 q-tiles of one (sequence, head) back to back as a single K/V
@@ -366,54 +366,35 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     for (int i = 0; i < NQF; ++i) asm volatile("" : "+v"(qf[i]));
   };
 
-  // one QK^T MFMA of the tile: k-step ks of key block jb (ka, kb: k_lane, k_lane2 + the
-  // stage's address)
+  // fp8: one QK^T MFMA of the tile, k-step ks of key block jb (ka, kb: k_lane, k_lane2 + the
+  // stage's address).  (The 16-bit matrix phase has its own operand pipeline below.)
   auto qk_mma = [&](uint32_t ka, uint32_t kb, int i) __attribute__((always_inline)) {
     const int jb = i % NJB, ks = i / NJB;
-    if constexpr (F8) {
-      const i32x4 a0 = *(const lds_i32x4*)(uintptr_t)((ka ^ (64 * ks)) + 32 * jb * RB);
-      const i32x4 a1 = *(const lds_i32x4*)(uintptr_t)((kb ^ (64 * ks)) + 32 * jb * RB);
-      const i32x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-      const i32x8 b = __builtin_shufflevector(qf[2 * ks], qf[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-      s[jb] = mma_f8(a, b, s[jb]);
-    } else {
-      const i32x4 a = *(const lds_i32x4*)(uintptr_t)((ka ^ (32 * ks)) + 32 * jb * RB);
-      s[jb] = T::mma(a, qf[ks], s[jb]);
-    }
+    const i32x4 a0 = *(const lds_i32x4*)(uintptr_t)((ka ^ (64 * ks)) + 32 * jb * RB);
+    const i32x4 a1 = *(const lds_i32x4*)(uintptr_t)((kb ^ (64 * ks)) + 32 * jb * RB);
+    const i32x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    const i32x8 b = __builtin_shufflevector(qf[2 * ks], qf[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    s[jb] = mma_f8(a, b, s[jb]);
   };
-  // one PV MFMA.  16-bit: d-block db, 16-key chunk (jb, c).  fp8: d-block i % NDB, 64-key half
-  // kh = i / NDB of the 128-key tile; byte 8 c + r of either operand is key 64 kh + 16 c + 8 h32
-  // + r (the probabilities are regrouped to this order at the end of the softmax, and the
-  // transposed V reads deliver it).
-  auto pv_mma = [&](uint32_t va0, uint32_t va1, int i) __attribute__((always_inline)) {
-    if constexpr (F8) {
-      const int db = i % NDB, kh = i / NDB;
-      i32x2 t[4];
+  // fp8: one PV MFMA, d-block i % NDB and 64-key half kh = i / NDB of the 128-key tile; byte
+  // 8 c + r of either operand is key 64 kh + 16 c + 8 h32 + r (the probabilities are regrouped
+  // to this order at the end of the softmax, and the transposed V reads deliver it).
+  auto pv_mma = [&](uint32_t va0, int i) __attribute__((always_inline)) {
+    const int db = i % NDB, kh = i / NDB;
+    i32x2 t[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        t[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (lds_i32x2*)(uintptr_t)((va0 ^ (32 * db)) + (64 * kh + 16 * c) * RB));
-      const i32x8 a = {t[0][0], t[0][1], t[1][0], t[1][1], t[2][0], t[2][1], t[3][0], t[3][1]};
-      const i32x8 b = {(int)pk[2 * kh][0], (int)pk[2 * kh][1], (int)pk[2 * kh][2], (int)pk[2 * kh][3],
-                       (int)pk[2 * kh + 1][0], (int)pk[2 * kh + 1][1], (int)pk[2 * kh + 1][2], (int)pk[2 * kh + 1][3]};
-      acc_o[db] = mma_f8(a, b, acc_o[db]);
-      if (db == NDB - 1) {  // row sums of this half: e4m3 1.0 = 0x38
-        const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                            0x38383838, 0x38383838, 0x38383838, 0x38383838};
-        acc_l = mma_f8(ones, b, acc_l);
-      }
-      return;
+    for (int c = 0; c < 4; ++c)
+      t[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (lds_i32x2*)(uintptr_t)((va0 ^ (32 * db)) + (64 * kh + 16 * c) * RB));
+    const i32x8 a = {t[0][0], t[0][1], t[1][0], t[1][1], t[2][0], t[2][1], t[3][0], t[3][1]};
+    const i32x8 b = {(int)pk[2 * kh][0], (int)pk[2 * kh][1], (int)pk[2 * kh][2], (int)pk[2 * kh][3],
+                     (int)pk[2 * kh + 1][0], (int)pk[2 * kh + 1][1], (int)pk[2 * kh + 1][2], (int)pk[2 * kh + 1][3]};
+    acc_o[db] = mma_f8(a, b, acc_o[db]);
+    if (db == NDB - 1) {  // row sums of this half: e4m3 1.0 = 0x38
+      const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                          0x38383838, 0x38383838, 0x38383838, 0x38383838};
+      acc_l = mma_f8(ones, b, acc_l);
     }
-    const int db = i % NDB, jc = i / NDB, jb = jc >> 1, c = jc & 1;
-    const uint32_t rows = (32 * jb + 16 * c) * RB;
-    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)((va0 ^ (64 * db)) + rows));
-    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)((va1 ^ (64 * db)) + rows));
-    const i32x4 a = {__builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 0, 1)),
-                     __builtin_bit_cast(int, __builtin_shufflevector(v0, v0, 2, 3)),
-                     __builtin_bit_cast(int, __builtin_shufflevector(v1, v1, 0, 1)),
-                     __builtin_bit_cast(int, __builtin_shufflevector(v1, v1, 2, 3))};
-    const i32x4 bp = {(int)pk[jb][4 * c], (int)pk[jb][4 * c + 1], (int)pk[jb][4 * c + 2], (int)pk[jb][4 * c + 3]};
-    acc_o[db] = T::mma(a, bp, acc_o[db]);
   };
   constexpr int NQK = NJB * KS;              // MFMAs of S^T for one tile
   constexpr int NPV = F8 ? 2 * NDB : 4 * NDB;  // MFMAs of O^T += V^T P^T for one tile
@@ -497,35 +478,35 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
         }
       }
     } else {
-    // fp8: the S^T MFMAs first, then the PV MFMAs, so the tile's row max (in the softmax code,
-    // free to move here) runs on the vector ALU while the PV products execute: in fp8 the
-    // softmax phase, not the matrix phase, sets the step.
+      // fp8: the S^T MFMAs first, then the PV MFMAs, so the tile's row max (in the softmax code,
+      // free to move here) runs on the vector ALU while the PV products execute: in fp8 the
+      // softmax phase, not the matrix phase, sets the step.
 #pragma unroll
-    for (int i = 0; i < NQK; ++i) qk_mma(ka, kb, i);
+      for (int i = 0; i < NQK; ++i) qk_mma(ka, kb, i);
 #pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      pv_mma(va0, va1, i);
+      for (int i = 0; i < NPV; ++i) {
+        pv_mma(va0, i);
 #pragma unroll
-      for (int j = 0; j < LPP; ++j)  // load j goes after PV step j * NPV / LPP
-        if ((j * NPV) / LPP == i) hook(j);
-    }
-    // The LDS reads run kPrefetch reads ahead of the MFMAs that consume them (pinned with
-    // scheduling groups: the compiler alone keeps only one or two in flight, which leaves
-    // the matrix core waiting on LDS latency).
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
+        for (int j = 0; j < LPP; ++j)  // load j goes after PV step j * NPV / LPP
+          if ((j * NPV) / LPP == i) hook(j);
+      }
+      // The LDS reads run kPrefetch reads ahead of the MFMAs that consume them (pinned with
+      // scheduling groups: the compiler alone keeps only one or two in flight, which leaves
+      // the matrix core waiting on LDS latency).
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
 #pragma unroll
-    for (int i = 0; i < NQK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RQK, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      if (i % NDB == NDB - 1)  // this step also adds the row sums of its 64 keys
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-      else
+      for (int i = 0; i < NQK; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPV, 0);
-    }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RQK, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        if (i % NDB == NDB - 1)  // this step also adds the row sums of its 64 keys
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPV, 0);
+      }
     }
     // Pin the products here: the compiler may otherwise sink MFMAs past the phase barrier,
     // into the softmax or the epilogue of an item that follows on this wave.
