@@ -48,6 +48,22 @@
 namespace fmha {
 namespace skv {
 
+// lds_load16 with the non-temporal hint, for the K/V tiles: every cached K/V byte is read by
+// one workgroup once, so nothing is gained by keeping it in the caches.  Measured on the decode
+// workload: 15% faster over a contiguous cache, 4% over a paged e4m3 cache, but 2% slower over
+// a paged 16-bit cache, which keeps the plain load (as does the forward kernel, whose
+// workgroups share K/V tiles through L2: 6% slower with the hint).
+__device__ inline void lds_load16_stream(i32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(lds_addr));
+}
+
 constexpr int kWaves = 1;       // waves per workgroup, each streaming its own K/V tiles
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTN = 32;         // keys per tile: one 32-key block of the MFMA
@@ -268,10 +284,17 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
       tv = make_rsrc_words((const char*)p.v + pb, bytes);
       key0 = (uint32_t)(kt & (ps - 1)) * kstride;
     }
+    if (KV8 || !paged) {
 #pragma unroll
-    for (int i = 0; i < TBLK; ++i) lds_load16(tk, key0 + ld_off[i], st + 1024 * i);
+      for (int i = 0; i < TBLK; ++i) lds_load16_stream(tk, key0 + ld_off[i], st + 1024 * i);
 #pragma unroll
-    for (int i = 0; i < TBLK; ++i) lds_load16(tv, key0 + ld_off[i], st + TILE + 1024 * i);
+      for (int i = 0; i < TBLK; ++i) lds_load16_stream(tv, key0 + ld_off[i], st + TILE + 1024 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TBLK; ++i) lds_load16(tk, key0 + ld_off[i], st + 1024 * i);
+#pragma unroll
+      for (int i = 0; i < TBLK; ++i) lds_load16(tv, key0 + ld_off[i], st + TILE + 1024 * i);
+    }
   };
 #pragma unroll
   for (int n = 0; n < STG - 1; ++n)
