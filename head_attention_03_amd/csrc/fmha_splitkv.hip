@@ -49,10 +49,10 @@ namespace fmha {
 namespace skv {
 
 // lds_load16 with the non-temporal hint, for the K/V tiles: every cached K/V byte is read by
-// one workgroup once, so nothing is gained by keeping it in the caches.  Measured on the decode
-// workload: 15% faster over a contiguous cache, 4% over a paged e4m3 cache, but 2% slower over
-// a paged 16-bit cache, which keeps the plain load (as does the forward kernel, whose
-// workgroups share K/V tiles through L2: 6% slower with the hint).
+// one workgroup once, so nothing is gained by keeping it in the caches (measured on the decode
+// workload: 18% faster over a contiguous cache; over a paged cache, together with the page
+// numbers read ahead, see the kernel).  The forward kernel, whose workgroups share K/V tiles
+// through L2, is 6% slower with the hint and keeps the plain load.
 __device__ inline void lds_load16_stream(i32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
   int saved;
   asm volatile(
@@ -120,7 +120,7 @@ struct MergeParams {
 // split kernel: grid = B * H_kv * mblks * n_splits workgroups of kThreads
 // KV8: K and V are e4m3 (a quantised cache); they are widened to the 16-bit type of Q exactly
 // (every e4m3 value is a bf16 and an fp16 value) as the MFMA operands are read from LDS.
-template <int DT, int D, bool KV8>
+template <int DT, int D, bool KV8, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
   constexpr int E = 2;               // bytes per Q element
   constexpr int EK = KV8 ? 1 : 2;    // bytes per K/V element
@@ -186,7 +186,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
     k_row0 = b * p.Sk;
     Sk_b = p.Sk;
   }
-  const bool paged = p.block_table != nullptr;
+  // (PAGED: the paged entry point, which always passes a block table.  The contiguous build
+  // keeps the run-time test, whose code measured 4% faster than the one without it.)
+  const bool paged = PAGED || p.block_table != nullptr;
   if (paged) {  // keys live in pages; no sequence has more than Sk (which the tables cover)
     k_row0 = 0;
     Sk_b = min(max(p.seqlens_k[b], 0), p.Sk);
@@ -227,6 +229,15 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
 
   const uint32_t ring = lds0 + (uint32_t)(wave_u * STG * STAGE);
   const uint32_t q_lds = lds0 + (uint32_t)(kWaves * STG * STAGE + wave_u * QB);
+
+  // Paged cache: when the split's keys lie in at most 64 pages, lane j holds the table entry of
+  // the split's j-th page, loaded once here, and each tile takes its page with a lane read
+  // instead of a scalar load it would wait for (waited for below, behind the Q rows).
+  const int lp_first = paged ? k0 >> p.page_shift : 0;
+  const bool pre = PAGED && n_tiles > 0 && ((k1 - 1) >> p.page_shift) - lp_first < 64;
+  int page_v = 0;
+  if (pre && lp_first + lane <= ((k1 - 1) >> p.page_shift))
+    page_v = p.block_table[(size_t)b * p.bt_stride + lp_first + lane];
 
   // ---- Q rows into this wave's LDS copy (swizzled like a K tile), then the B operand ----
 #pragma unroll
@@ -275,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
     if (paged) {
       const int ps = 1 << p.page_shift;
       const int lp = kt >> p.page_shift;
-      const int phys = p.block_table[(size_t)b * p.bt_stride + lp];
+      const int phys = pre ? __builtin_amdgcn_readlane(page_v, lp - lp_first) : p.block_table[(size_t)b * p.bt_stride + lp];
       const bool ok = (unsigned)phys < (unsigned)p.num_pages;
       const int valid = min(ps, Sk_b - (lp << p.page_shift));  // >= 1: the tile starts inside the sequence
       const size_t pb = ok ? ((size_t)phys * ps * p.H_kv + kvh) * RBK : 0;
@@ -284,12 +295,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
       tv = make_rsrc_words((const char*)p.v + pb, bytes);
       key0 = (uint32_t)(kt & (ps - 1)) * kstride;
     }
-    if (KV8 || !paged) {
+    if (PAGED || KV8 || !paged) {
 #pragma unroll
       for (int i = 0; i < TBLK; ++i) lds_load16_stream(tk, key0 + ld_off[i], st + 1024 * i);
 #pragma unroll
       for (int i = 0; i < TBLK; ++i) lds_load16_stream(tv, key0 + ld_off[i], st + TILE + 1024 * i);
-    } else {
+    } else {  // (not reached: kept for the code shape of the contiguous build, above)
 #pragma unroll
       for (int i = 0; i < TBLK; ++i) lds_load16(tk, key0 + ld_off[i], st + 1024 * i);
 #pragma unroll
@@ -509,9 +520,9 @@ inline void plan(int64_t units, int64_t Sk, int64_t target, int32_t* n_splits, i
   *n_splits = (int32_t)(Sk > 0 ? (Sk + c - 1) / c : 1);
 }
 
-template <int DT, int D, bool KV8 = false>
+template <int DT, int D, bool KV8 = false, bool PAGED = false>
 hipError_t launch(const Params& p, const MergeParams& mp, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((split_kernel<DT, D, KV8>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((split_kernel<DT, D, KV8, PAGED>), dim3(grid), dim3(kThreads), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t threads = (int64_t)mp.rows * (D / 4);
@@ -706,20 +717,20 @@ fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const voi
   hipError_t err = hipSuccess;
   if (kv8) {
     if (dtype == FMHA_DTYPE_BF16) {
-      if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64, true>(p, mp, (int)grid, stream);
-      if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128, true>(p, mp, (int)grid, stream);
+      if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64, true, true>(p, mp, (int)grid, stream);
+      if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128, true, true>(p, mp, (int)grid, stream);
     } else {
-      if (D == 64) err = fmha::skv::launch<fmha::kF16, 64, true>(p, mp, (int)grid, stream);
-      if (D == 128) err = fmha::skv::launch<fmha::kF16, 128, true>(p, mp, (int)grid, stream);
+      if (D == 64) err = fmha::skv::launch<fmha::kF16, 64, true, true>(p, mp, (int)grid, stream);
+      if (D == 128) err = fmha::skv::launch<fmha::kF16, 128, true, true>(p, mp, (int)grid, stream);
     }
   } else if (dtype == FMHA_DTYPE_BF16) {
-    if (D == 32) err = fmha::skv::launch<fmha::kBF16, 32>(p, mp, (int)grid, stream);
-    if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64>(p, mp, (int)grid, stream);
-    if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128>(p, mp, (int)grid, stream);
+    if (D == 32) err = fmha::skv::launch<fmha::kBF16, 32, false, true>(p, mp, (int)grid, stream);
+    if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64, false, true>(p, mp, (int)grid, stream);
+    if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128, false, true>(p, mp, (int)grid, stream);
   } else {
-    if (D == 32) err = fmha::skv::launch<fmha::kF16, 32>(p, mp, (int)grid, stream);
-    if (D == 64) err = fmha::skv::launch<fmha::kF16, 64>(p, mp, (int)grid, stream);
-    if (D == 128) err = fmha::skv::launch<fmha::kF16, 128>(p, mp, (int)grid, stream);
+    if (D == 32) err = fmha::skv::launch<fmha::kF16, 32, false, true>(p, mp, (int)grid, stream);
+    if (D == 64) err = fmha::skv::launch<fmha::kF16, 64, false, true>(p, mp, (int)grid, stream);
+    if (D == 128) err = fmha::skv::launch<fmha::kF16, 128, false, true>(p, mp, (int)grid, stream);
   }
   return err == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
 }
