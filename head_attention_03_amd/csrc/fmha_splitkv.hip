@@ -715,7 +715,19 @@ fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const voi
   mp.o_scale = o_scale;
 
   hipError_t err = hipSuccess;
-  if (kv8) {
+  if (no_keys) {
+    // An empty cache: the block table and the lengths may be NULL, and no key is read.  The
+    // contiguous kernels (no table) give every row O = 0 and LSE = -inf, whatever the cache type.
+    if (dtype == FMHA_DTYPE_BF16) {
+      if (D == 32) err = fmha::skv::launch<fmha::kBF16, 32>(p, mp, (int)grid, stream);
+      if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64>(p, mp, (int)grid, stream);
+      if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128>(p, mp, (int)grid, stream);
+    } else {
+      if (D == 32) err = fmha::skv::launch<fmha::kF16, 32>(p, mp, (int)grid, stream);
+      if (D == 64) err = fmha::skv::launch<fmha::kF16, 64>(p, mp, (int)grid, stream);
+      if (D == 128) err = fmha::skv::launch<fmha::kF16, 128>(p, mp, (int)grid, stream);
+    }
+  } else if (kv8) {
     if (dtype == FMHA_DTYPE_BF16) {
       if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64, true, true>(p, mp, (int)grid, stream);
       if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128, true, true>(p, mp, (int)grid, stream);

@@ -92,6 +92,29 @@ def test_paged_table_entry_out_of_range_reads_zero_keys():
     compare("paged out-of-range entry", res.o_bits, "f16", o, res.lse, lse)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f8e4m3"])
+def test_paged_empty_cache_needs_no_table(kv_dtype):
+    # Sk = 0: the caches, the block table and the lengths may all be NULL (nothing is read);
+    # every row gets O = 0 and LSE = -inf, as from fmha_fwd with no keys
+    import head_attention_03_amd as fmha
+    B, Sq, H, H_kv, D = 2, 3, 8, 2, 128
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(5500)
+    q = torch.randn((B, Sq, H, D), generator=g).to(torch.bfloat16).to(dev)
+    o = torch.full_like(q, 7.0)
+    lse = torch.zeros((B, H, Sq), dtype=torch.float32, device=dev)
+    log(f"[case] paged empty cache kv={kv_dtype}")
+    pk = fmha.make_paged_kv(None, None, 0, 128, 0, kv_dtype)
+    need = fmha.fmha_fwd_splitkv_workspace_size(B, Sq, 0, H, H_kv, D, None)
+    ws = _workspace(need)
+    st = fmha.fmha_fwd_splitkv_paged(q, None, None, o, lse, B, Sq, 0, H, H_kv, D, 0.0884, "none", "bf16", 1.0, pk,
+                                     ws, need, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.all(o.cpu().float() == 0.0)
+    assert torch.all(lse.cpu() == float("-inf"))
+
+
 PAGED_FP8 = [
     # (B, Sq, seqlens_k, H, H_kv, D, dtype, mask, page_size): e4m3 cache, 16-bit queries and output
     (4, 1, [4097, 1, 300, 0], 32, 8, 128, "bf16", "none", 128),
