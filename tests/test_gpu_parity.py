@@ -209,6 +209,22 @@ def test_varlen_shapes_fp8(case):
     _varlen_case(f"varlen fp8 {lq}/{lk}", make_varlen(2650, lq, lk, H, H_kv, D, "f8e4m3", mask=mask, o_scale=0.5))
 
 
+# fp8 tiles hold 128 keys: key lengths on either side of one and two tiles, with every mask that
+# ends a sequence inside a tile (the ragged tail, the causal diagonal aligned to the last key)
+FP8_TILE_EDGES = [
+    ([130, 128, 127, 256, 300, 1], [127, 128, 129, 255, 256, 257], 4, 2, 128, "residual"),
+    ([127, 128, 129, 255, 256, 257], [127, 128, 129, 255, 256, 257], 4, 4, 64, "causal_qend"),
+    ([64, 200, 129], [129, 255, 385], 2, 1, 128, "causal_qbegin"),
+]
+
+
+@pytest.mark.parametrize("case", FP8_TILE_EDGES, ids=lambda c: f"k{c[1]}-{c[5]}-D{c[4]}")
+def test_varlen_fp8_key_tile_edges(case):
+    lq, lk, H, H_kv, D, mask = case
+    _varlen_case(f"varlen fp8 tile edges {lq}/{lk}",
+                 make_varlen(2680 + len(lk), lq, lk, H, H_kv, D, "f8e4m3", mask=mask, o_scale=0.5))
+
+
 def test_varlen_poisoned_padding_never_read_fp8():
     inp = make_varlen(2750, [100, 37, 250], [90, 300, 5], 4, 2, 128, "f8e4m3", mask="causal_qend", poison_pads=True)
     _varlen_case("varlen fp8 NaN pads", inp)
