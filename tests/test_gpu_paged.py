@@ -30,6 +30,9 @@ PAGED = [
     (2, 16, [3000, 33], 8, 2, 32, "bf16", "causal_qend", 64),          # 64 packed rows, D = 32
     (1, 7, [2500], 4, 1, 32, "f16", "causal_qbegin", 512),             # rows see only the first keys
     (5, 2, [129, 128, 127, 1, 640], 8, 8, 64, "bf16", "residual", 128), # page edges
+    # one split per (sequence, head): the long caches span 66 pages per split and read the table
+    # tile by tile, the short ones take their page numbers read ahead (both in one launch)
+    (8, 1, [2112, 2080, 1500, 2112, 33, 2112, 1999, 64], 64, 64, 32, "bf16", "none", 32),
 ]
 
 
