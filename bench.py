@@ -19,8 +19,8 @@ step, both of its kernels): bound by HBM, so its line reports GB/s of algorithmi
 random order), reported the same way; --config 9 is config 8 over an e4m3 cache (half the K/V
 bytes; bf16 queries and output).
 
---config 7 is the backward pass (one fmha_bwd call per step: its statistics, dQ and dK/dV
-kernels) of the prefill shape, with O and LSE from fmha_fwd computed once before timing.  Its
+--config 7 is the backward pass (one fmha_bwd call per step: its two kernels, dQ with the row
+statistics, then dK/dV) of the prefill shape, with O and LSE from fmha_fwd computed once before timing.  Its
 FLOPs follow the 5-matmul count (S, dP, dV, dQ, dK: 2.5 times the forward's 4*B*H*Sq*Sk*D,
 halved for causal masks); the roofline is taken over the whole call.
 """

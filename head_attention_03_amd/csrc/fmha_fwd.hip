@@ -124,8 +124,10 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   constexpr int STAGE = 2 * TILE;    // LDS bytes per stage: K tile, then V tile
   constexpr int LPP = (NBLK + 15) / 16;  // loads one wave issues per phase
   static_assert(NBLK % 8 == 0, "every wave issues the same number of tile loads");
-  static_assert(!F8 || D >= 64, "fp8 needs D >= 64 (one 64-deep MFMA k-step)");
-  constexpr int KS = F8 ? D / 64 : D / 16;  // MFMA k-steps over the head dimension
+  // fp8 with D = 32: one 64-deep MFMA k-step whose upper 32 dims are zero (the lanes that
+  // supply them hold a zero Q operand and reread the K bytes of the lower half)
+  constexpr bool F8_HALF = F8 && D == 32;
+  constexpr int KS = F8 ? (D + 63) / 64 : D / 16;  // MFMA k-steps over the head dimension
   constexpr int NDB = D / 32;      // 32-wide blocks of the head dimension in O
   typedef Elem<DT == kF8 ? kBF16 : DT> T;  // (fp8 uses the helpers above instead)
   auto sw = [](int j) __attribute__((always_inline)) { return F8 ? swz8<CPR>(j) : swz<CPR>(j); };
@@ -338,8 +340,8 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // the d-block (V) index leaves clear, so every read address is one of these bases XOR a
   // compile-time constant, plus an immediate row offset.
   //   16-bit: K row l32, chunk 2 ks + h32; fp8: K row l32, chunks 4 ks + 2 h32 (+1).
-  const int k_lane = l32 * RB + (((F8 ? 2 * h32 : h32) ^ sw(l32)) * 16);
-  const int k_lane2 = l32 * RB + (((2 * h32 + 1) ^ sw(l32)) * 16);  // fp8 only
+  const int k_lane = l32 * RB + (((F8 ? (F8_HALF ? 0 : 2 * h32) : h32) ^ sw(l32)) * 16);
+  const int k_lane2 = l32 * RB + ((((F8_HALF ? 0 : 2 * h32) + 1) ^ sw(l32)) * 16);  // fp8 only
   const int g16 = (lane >> 4) & 1;
   const int s16 = lane & 15;
   // 16-bit V transpose read (ds_read_b64_tr_b16): row 4 h32 + s16 / 4 of a 16-row group (and
@@ -361,6 +363,10 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
         qf[i] = *(const lds_i32x4*)(uintptr_t)(((i & 1) ? q_lds + k_lane2 : q_lds + k_lane) ^ (64 * (i >> 1)));
       else
         qf[i] = *(const lds_i32x4*)(uintptr_t)((q_lds + k_lane) ^ (32 * i));
+    }
+    if constexpr (F8_HALF) {  // dims 32..63 of the k-step do not exist
+#pragma unroll
+      for (int i = 0; i < NQF; ++i) qf[i] = h32 ? i32x4{} : qf[i];
     }
 #pragma unroll
     for (int i = 0; i < NQF; ++i) asm volatile("" : "+v"(qf[i]));
@@ -908,7 +914,6 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FMHA_ERR_MISALIGNED;
   if ((uintptr_t)lse & 3) return FMHA_ERR_MISALIGNED;
   if (!(scale > 0.0f) || !isfinite(scale) || !isfinite(o_scale)) return FMHA_ERR_INVALID_ARGUMENT;
-  if (dtype == FMHA_DTYPE_F8E4M3 && D == 32) return FMHA_ERR_UNSUPPORTED;  // fp8 MFMA k-step is 64 deep
 
   const int64_t esz = dtype == FMHA_DTYPE_F8E4M3 ? 1 : 2;
   // every per-sequence byte offset must fit the 31-bit range of a buffer descriptor
@@ -957,6 +962,7 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
 
   hipError_t err = hipSuccess;
   if (dtype == FMHA_DTYPE_F8E4M3) {
+    if (D == 32) err = launch<kF8, 32>(p, (int)grid, stream);
     if (D == 64) err = launch<kF8, 64>(p, (int)grid, stream);
     if (D == 128) err = launch<kF8, 128>(p, (int)grid, stream);
   } else if (dtype == FMHA_DTYPE_BF16) {

@@ -598,8 +598,10 @@ size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_
   fmha::skv::Params p;
   int64_t grid = 0;
   size_t bytes = 0;
+  // The workspace holds per-split partial rows of Q's shape, whatever the K/V bytes: planned as
+  // for a paged cache, which skips the contiguous K/V offset bound (the entry points check it).
   const fmha_status st = splitkv_plan(nullptr, nullptr, nullptr, nullptr, nullptr, B, Sq, Sk, H, H_kv, D,
-                                      FMHA_MASK_NONE, FMHA_DTYPE_BF16, varlen, &p, &grid, &bytes);
+                                      FMHA_MASK_NONE, FMHA_DTYPE_BF16, varlen, &p, &grid, &bytes, true);
   return st == FMHA_OK ? bytes : 0;
 }
 

@@ -63,9 +63,10 @@ typedef enum {
   FMHA_ERR_NULL_POINTER = 1,     /* q, o, or (when there are keys) k or v is NULL, or only one
                                     cu_seqlens pointer is set */
   FMHA_ERR_INVALID_SHAPE = 2,    /* negative sizes, H % H_kv != 0, D not in {32, 64, 128}, totals < 0 */
-  FMHA_ERR_UNSUPPORTED = 3,      /* dtype/mask enum out of range, fp8 with D == 32, or a tensor too
-                                    large for 32-bit offsets (any tensor of 2^31 bytes or more,
-                                    192 K/V rows or 256 Q rows of 2^31 bytes or more) */
+  FMHA_ERR_UNSUPPORTED = 3,      /* dtype/mask enum out of range, or a tensor too large for 32-bit
+                                    offsets (any tensor of 2^31 bytes or more, or three K/V tiles --
+                                    192 16-bit or 384 e4m3 rows -- or 256 Q rows of 2^31 bytes or
+                                    more) */
   FMHA_ERR_MISALIGNED = 4,       /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   FMHA_ERR_INVALID_ARGUMENT = 5, /* scale not finite and > 0, or o_scale not finite */
   FMHA_ERR_HIP = 6               /* the kernel launch failed (hipGetLastError) */
@@ -101,7 +102,7 @@ typedef struct {
  *          natural-log log-sum-exp of scale * q.k over the visible keys (-inf if none)
  *   B      number of sequences (>= 0);  Sq, Sk: lengths (packed: the maximum lengths)
  *   H, H_kv  query heads and key/value heads, H % H_kv == 0 (H_kv == 1 is MQA)
- *   D      head dimension: 32, 64 or 128 (fp8: 64 or 128)
+ *   D      head dimension: 32, 64 or 128
  *   scale  softmax scale (finite, > 0), applied to q.k in fp32.  For fp8 inputs the
  *          caller folds the per-tensor dequantisation scales of q and k into it.
  *   mask   see fmha_mask
@@ -151,9 +152,12 @@ fmha_status fmha_fwd_splitkv(const void* q, const void* k, const void* v, void* 
                              const fmha_varlen* varlen, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
-/* Workspace bytes fmha_fwd_splitkv needs for this shape (host arithmetic only: no device
- * call; the packed form reads only varlen->total_length_q).  Returns 0 for an invalid
- * shape, or a shape too large for the kernel's 32-bit offsets. */
+/* Workspace bytes fmha_fwd_splitkv and fmha_fwd_splitkv_paged need for this shape (host
+ * arithmetic only: no device call; the packed form reads only varlen->total_length_q).  The
+ * size depends on the query rows, heads, D and the split plan, not on the bytes of K and V, so a
+ * contiguous K/V too large for the kernel's 32-bit offsets still gets a size (fmha_fwd_splitkv
+ * then returns FMHA_ERR_UNSUPPORTED).  Returns 0 for an invalid shape, or query rows or
+ * partials too large for 32-bit offsets. */
 size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
                                        const fmha_varlen* varlen);
 

@@ -119,9 +119,29 @@ def output_floor(expected: np.ndarray, dtype: str) -> float:
     return float(np.abs(oracle.decode(_round_to(expected, dtype), dtype) - expected).max()) if expected.size else 0.0
 
 
+def oracle_dense_heads(inp, heads, workers: int = 8):
+    """Whole heads [(b, h), ...] of a dense problem from the oracle, several at a time (numpy's
+    matmul and exp release the GIL; each head is the oracle's own per-head definition).
+    Returns O [n, Sq, D] (times o_scale) and LSE [n, Sq]."""
+    from concurrent.futures import ThreadPoolExecutor
+    q, k, v = decoded(inp, "q"), decoded(inp, "k"), decoded(inp, "v")
+    group = inp.H // inp.H_kv
+
+    def one(bh):
+        b, h = bh
+        return oracle.attention_head(q[b, :, h], k[b, :, h // group], v[b, :, h // group], inp.scale, inp.mask)
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        res = list(ex.map(one, heads))
+    return np.stack([r[0] for r in res]) * inp.o_scale, np.stack([r[1] for r in res])
+
+
 def compare(name: str, got_bits: np.ndarray, dtype: str, expected: np.ndarray, got_lse=None, expected_lse=None,
-            tol: Optional[float] = None):
-    """Element-by-element check of the decoded GPU output against the oracle; returns the max error."""
+            tol: Optional[float] = None, plain: bool = False):
+    """Element-by-element check of the decoded GPU output against the oracle; returns the max error.
+
+    plain: for fp8, also hold the raw max-abs error (not only the error beyond the best e4m3
+    output) to the tolerance; used where |O| is small enough for that bound to be reachable."""
     tol = TOL[dtype] if tol is None else tol
     got = oracle.decode(got_bits, dtype)
     assert got.shape == expected.shape, (got.shape, expected.shape)
@@ -141,6 +161,8 @@ def compare(name: str, got_bits: np.ndarray, dtype: str, expected: np.ndarray, g
         err_beyond = float((np.abs(got - expected) - np.abs(best - expected)).max())
         rel_floor = float(np.linalg.norm(best - expected) / max(np.linalg.norm(expected), 1e-30))
         msg += f", beyond the best e4m3 output {err_beyond:.3e}, best output's rel fro {rel_floor:.3e}"
+        if plain:
+            assert err <= tol, msg + " (plain max-abs bound)"
         err = err_beyond
         rel_bound = rel_floor + REL_TOL[dtype]
     if got_lse is not None:

@@ -52,7 +52,7 @@ def call(**kw):
     (dict(varlen=fmha.make_varlen(P, P, -1, 16)), 2),
     (dict(dtype=3), 3), (dict(dtype=-1), 3), (dict(mask=4), 3), (dict(mask=-1), 3),
     (dict(Sq=1 << 22, H=64, H_kv=64, D=128), 3),
-    (dict(dtype="f8e4m3", D=32), 3), (dict(H=1 << 16, H_kv=1 << 16, D=128, Sq=1, Sk=1), 3),
+    (dict(dtype="f8e4m3", D=32, q=P + 2), 4), (dict(H=1 << 16, H_kv=1 << 16, D=128, Sq=1, Sk=1), 3),
     (dict(H=1 << 15, H_kv=1, D=128, Sq=1, Sk=1), 3),
     (dict(q=P + 2), 4), (dict(o=P + 8), 4), (dict(lse=P + 2), 4),
     (dict(scale=0.0), 5), (dict(scale=-0.1), 5), (dict(scale=float("inf")), 5), (dict(scale=float("nan")), 5),
@@ -123,6 +123,19 @@ def test_splitkv_workspace_size_packed_uses_total_rows():
     need = fmha.fmha_fwd_splitkv_workspace_size(3, 4, 3000, 8, 2, 64, vl)
     assert need > 0 and need % (7 * 8 * 65 * 4) == 0
     assert fmha.fmha_fwd_splitkv_workspace_size(3, 4, 3000, 6, 4, 64) == 0  # H % H_kv != 0
+
+
+def test_splitkv_workspace_size_ignores_kv_bytes():
+    # a cache of 2^20 keys x 8 heads x 128 dims (2 GiB of K): too large for the contiguous kernels'
+    # 32-bit offsets, but the paged entry point takes it and needs the same workspace as 8192 keys
+    # split the same number of ways
+    need = fmha.fmha_fwd_splitkv_workspace_size(1, 1, 1 << 20, 32, 8, 128)
+    assert need > 0 and need % (32 * 129 * 4) == 0
+    assert call_skv(Sk=1 << 20, H=32, H_kv=8, D=128, workspace_bytes=need) == 3  # contiguous: refused
+    pk = fmha.make_paged_kv(P, P, 1 << 13, 128, 1 << 13, "bf16")
+    assert fmha.fmha_fwd_splitkv_paged(q=P, k_cache=P, v_cache=P, o=P, lse=None, B=1, Sq=1, Sk=1 << 20, H=32, H_kv=8,
+                                       D=128, scale=0.125, mask="none", dtype="bf16", paged=pk, workspace=P,
+                                       workspace_bytes=need - 1) == 5  # passes the shape checks, one byte short
 
 
 # ----------------------------------------------------------------------------------------------
