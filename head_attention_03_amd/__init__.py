@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     fmha_bwd_workspace_size,
     fmha_fwd,
     fmha_fwd_splitkv,
+    fmha_fwd_splitkv_noalloc,
     fmha_fwd_splitkv_paged,
     fmha_paged_kv,
     fmha_fwd_splitkv_workspace_size,

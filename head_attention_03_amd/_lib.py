@@ -17,10 +17,10 @@ LIB_PATH = os.path.join(_HERE, "libfmha.so")
 DTYPES = {"f16": 0, "bf16": 1, "f8e4m3": 2}
 MASKS = {"none": 0, "residual": 1, "causal_qbegin": 2, "causal_qend": 3}
 STATUS = {0: "FMHA_OK", 1: "FMHA_ERR_NULL_POINTER", 2: "FMHA_ERR_INVALID_SHAPE", 3: "FMHA_ERR_UNSUPPORTED",
-          4: "FMHA_ERR_MISALIGNED", 5: "FMHA_ERR_INVALID_ARGUMENT", 6: "FMHA_ERR_HIP"}
+          4: "FMHA_ERR_MISALIGNED", 5: "FMHA_ERR_INVALID_ARGUMENT", 6: "FMHA_ERR_HIP", 7: "FMHA_ERR_SCRATCH_TOO_SMALL"}
 # every symbol include/fmha.h declares
-EXPORTS = ("fmha_fwd", "fmha_fwd_splitkv", "fmha_fwd_splitkv_workspace_size", "fmha_fwd_splitkv_paged", "fmha_bwd",
-           "fmha_bwd_workspace_size", "fmha_status_string", "fmha_version")
+EXPORTS = ("fmha_fwd", "fmha_fwd_splitkv", "fmha_fwd_splitkv_noalloc", "fmha_fwd_splitkv_workspace_size",
+           "fmha_fwd_splitkv_paged", "fmha_bwd", "fmha_bwd_workspace_size", "fmha_status_string", "fmha_version")
 
 
 class FmhaError(RuntimeError):
@@ -57,6 +57,9 @@ def load() -> ctypes.CDLL:
     lib.fmha_fwd_splitkv.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int32] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.POINTER(fmha_varlen), ctypes.c_void_p,
         ctypes.c_size_t, ctypes.c_void_p]
+    lib.fmha_fwd_splitkv_noalloc.restype = ctypes.c_int
+    lib.fmha_fwd_splitkv_noalloc.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int32] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.POINTER(fmha_varlen), ctypes.c_void_p]
     lib.fmha_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fmha_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int32] * 6 + [ctypes.POINTER(fmha_varlen)]
     lib.fmha_fwd_splitkv_paged.restype = ctypes.c_int
@@ -119,6 +122,19 @@ def fmha_fwd_splitkv(q, k, v, o, lse, B: int, Sq: int, Sk: int, H: int, H_kv: in
     return int(lib.fmha_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Sq), int(Sk), int(H),
                                     int(H_kv), int(D), float(scale), mask, dtype, float(o_scale), vl, _ptr(workspace),
                                     int(workspace_bytes), _stream(stream)))
+
+
+def fmha_fwd_splitkv_noalloc(q, k, v, o, lse, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int, scale: float,
+                             mask, dtype, o_scale: float = 1.0, varlen: Optional[fmha_varlen] = None,
+                             stream=None) -> int:
+    """Call the allocation-free split-KV C entry point (library-owned scratch); returns the fmha_status code."""
+    lib = load()
+    mask = MASKS[mask] if isinstance(mask, str) else int(mask)
+    dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    vl = ctypes.byref(varlen) if varlen is not None else None
+    return int(lib.fmha_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Sq), int(Sk),
+                                            int(H), int(H_kv), int(D), float(scale), mask, dtype, float(o_scale), vl,
+                                            _stream(stream)))
 
 
 def fmha_fwd_splitkv_workspace_size(B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int,

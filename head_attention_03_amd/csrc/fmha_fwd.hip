@@ -889,7 +889,8 @@ const char* fmha_status_string(fmha_status s) {
     case FMHA_ERR_UNSUPPORTED: return "unsupported (dtype or mask out of range, or tensor too large for 32-bit offsets)";
     case FMHA_ERR_MISALIGNED: return "misaligned pointer (q, k, v, o need 16 bytes, lse needs 4)";
     case FMHA_ERR_INVALID_ARGUMENT: return "invalid argument (scale must be finite and > 0, o_scale finite)";
-    case FMHA_ERR_HIP: return "HIP kernel launch failed";
+    case FMHA_ERR_HIP: return "HIP kernel launch failed, or the scratch array's device address is unavailable";
+    case FMHA_ERR_SCRATCH_TOO_SMALL: return "shape needs more workspace than the 32 MiB static scratch array";
   }
   return "unknown status";
 }

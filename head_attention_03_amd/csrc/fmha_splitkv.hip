@@ -536,6 +536,10 @@ hipError_t launch(const Params& p, const MergeParams& mp, int grid, hipStream_t 
 // --------------------------------------------------------------------------------------
 // C ABI
 // --------------------------------------------------------------------------------------
+// Scratch of fmha_fwd_splitkv_noalloc (see scratch_address below): 32 MiB per device.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 namespace {
 
 // The shape checks fmha_fwd makes, and the split plan.  Returns FMHA_OK with the plan filled.
@@ -589,26 +593,34 @@ fmha_status splitkv_plan(const void* q, const void* k, const void* v, const void
   return FMHA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
-                                       const fmha_varlen* varlen) {
-  fmha::skv::Params p;
-  int64_t grid = 0;
-  size_t bytes = 0;
-  // The workspace holds per-split partial rows of Q's shape, whatever the K/V bytes: planned as
-  // for a paged cache, which skips the contiguous K/V offset bound (the entry points check it).
-  const fmha_status st = splitkv_plan(nullptr, nullptr, nullptr, nullptr, nullptr, B, Sq, Sk, H, H_kv, D,
-                                      FMHA_MASK_NONE, FMHA_DTYPE_BF16, varlen, &p, &grid, &bytes, true);
-  return st == FMHA_OK ? bytes : 0;
+// ------------------------------------------------------------------------------------
+// scratch of the allocation-free entry point
+// ------------------------------------------------------------------------------------
+// The split partials of fmha_fwd_splitkv_noalloc live in this library-owned array: one copy on
+// every device the library runs on, held until the process ends.  In host code `scratch` is only
+// a stand-in for the symbol; its device address on the current device comes from
+// hipGetSymbolAddress, resolved on the first call on each device and kept per device.
+// Device address of `scratch` on the current device, or nullptr if the runtime cannot give it.
+void* scratch_address() {
+  static std::atomic<uintptr_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  if (dev < 64) {
+    const uintptr_t a = cache[dev].load(std::memory_order_acquire);
+    if (a) return (void*)a;
+  }
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  if (dev < 64) cache[dev].store((uintptr_t)ptr, std::memory_order_release);
+  return ptr;
 }
 
-fmha_status fmha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Sq,
-                             int32_t Sk, int32_t H, int32_t H_kv, int32_t D, float scale, fmha_mask mask,
-                             fmha_dtype dtype, float o_scale, const fmha_varlen* varlen, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+// fmha_fwd_splitkv, with the workspace either the caller's or (library_scratch) this library's
+// static array on the current device.
+fmha_status splitkv_run(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Sq,
+                        int32_t Sk, int32_t H, int32_t H_kv, int32_t D, float scale, fmha_mask mask, fmha_dtype dtype,
+                        float o_scale, const fmha_varlen* varlen, void* workspace, size_t workspace_bytes,
+                        bool library_scratch, hipStream_t stream) {
   using namespace fmha::skv;
   const bool packed = varlen != nullptr;
   const bool no_keys = packed ? varlen->total_length_k == 0 : Sk == 0;  // k and v may then be NULL
@@ -622,6 +634,12 @@ fmha_status fmha_fwd_splitkv(const void* q, const void* k, const void* v, void* 
   if (st != FMHA_OK) return st;
   if (!(scale > 0.0f) || !isfinite(scale) || !isfinite(o_scale)) return FMHA_ERR_INVALID_ARGUMENT;
   if (B == 0 || H == 0 || Sq == 0 || (packed && varlen->total_length_q == 0)) return FMHA_OK;
+  if (library_scratch) {
+    if (need > kScratchBytes) return FMHA_ERR_SCRATCH_TOO_SMALL;
+    workspace = scratch_address();
+    if (!workspace) return FMHA_ERR_HIP;
+    workspace_bytes = kScratchBytes;
+  }
   if (!workspace) return FMHA_ERR_NULL_POINTER;
   if ((uintptr_t)workspace & 15) return FMHA_ERR_MISALIGNED;
   if (workspace_bytes < need) return FMHA_ERR_INVALID_ARGUMENT;
@@ -660,6 +678,38 @@ fmha_status fmha_fwd_splitkv(const void* q, const void* k, const void* v, void* 
     if (D == 128) err = fmha::skv::launch<fmha::kF16, 128>(p, mp, (int)grid, stream);
   }
   return err == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
+                                       const fmha_varlen* varlen) {
+  fmha::skv::Params p;
+  int64_t grid = 0;
+  size_t bytes = 0;
+  // The workspace holds per-split partial rows of Q's shape, whatever the K/V bytes: planned as
+  // for a paged cache, which skips the contiguous K/V offset bound (the entry points check it).
+  const fmha_status st = splitkv_plan(nullptr, nullptr, nullptr, nullptr, nullptr, B, Sq, Sk, H, H_kv, D,
+                                      FMHA_MASK_NONE, FMHA_DTYPE_BF16, varlen, &p, &grid, &bytes, true);
+  return st == FMHA_OK ? bytes : 0;
+}
+
+fmha_status fmha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Sq,
+                             int32_t Sk, int32_t H, int32_t H_kv, int32_t D, float scale, fmha_mask mask,
+                             fmha_dtype dtype, float o_scale, const fmha_varlen* varlen, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return splitkv_run(q, k, v, o, lse, B, Sq, Sk, H, H_kv, D, scale, mask, dtype, o_scale, varlen, workspace,
+                     workspace_bytes, false, stream);
+}
+
+fmha_status fmha_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                                     int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D, float scale,
+                                     fmha_mask mask, fmha_dtype dtype, float o_scale, const fmha_varlen* varlen,
+                                     hipStream_t stream) {
+  return splitkv_run(q, k, v, o, lse, B, Sq, Sk, H, H_kv, D, scale, mask, dtype, o_scale, varlen, nullptr, 0, true,
+                     stream);
 }
 
 fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

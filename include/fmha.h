@@ -69,7 +69,10 @@ typedef enum {
                                     more) */
   FMHA_ERR_MISALIGNED = 4,       /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   FMHA_ERR_INVALID_ARGUMENT = 5, /* scale not finite and > 0, or o_scale not finite */
-  FMHA_ERR_HIP = 6               /* the kernel launch failed (hipGetLastError) */
+  FMHA_ERR_HIP = 6,              /* the kernel launch failed (hipGetLastError), or the device address
+                                    of the library's scratch array could not be obtained */
+  FMHA_ERR_SCRATCH_TOO_SMALL = 7 /* fmha_fwd_splitkv_noalloc: the shape needs more workspace than
+                                    the library's static scratch array holds (32 MiB) */
 } fmha_status;
 
 /* Packed variable-length batch, after CUTLASS's VariableLength {max_length,
@@ -151,6 +154,25 @@ fmha_status fmha_fwd_splitkv(const void* q, const void* k, const void* v, void* 
                              float scale, fmha_mask mask, fmha_dtype dtype, float o_scale,
                              const fmha_varlen* varlen, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * fmha_fwd_splitkv_noalloc -- fmha_fwd_splitkv (same arguments without the workspace, same
+ * kernels, same split plan, bit-identical results) for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The split partials go to a static array that the library owns, 32 MiB on every device it runs
+ * on, held until the process ends.  The call allocates nothing (no hipMalloc, no hipFree).
+ *   Shapes whose fmha_fwd_splitkv_workspace_size(...) exceeds 32 MiB -> FMHA_ERR_SCRATCH_TOO_SMALL
+ *   (nothing launched); other errors as fmha_fwd_splitkv.  The first call on a device looks up the
+ *   array's device address there (FMHA_ERR_HIP if the runtime cannot give it).
+ * All calls on one device share its array, and each call overwrites what the last one left there
+ * before reading it (no part of it needs to start at zero).  Calls enqueued on one stream run one
+ * after the other; calls that may overlap in time on one device (several streams, several host
+ * threads) race on the array and must not be issued.
+ */
+fmha_status fmha_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
+                                     float scale, fmha_mask mask, fmha_dtype dtype, float o_scale,
+                                     const fmha_varlen* varlen, hipStream_t stream);
 
 /* Workspace bytes fmha_fwd_splitkv and fmha_fwd_splitkv_paged need for this shape (host
  * arithmetic only: no device call; the packed form reads only varlen->total_length_q).  The

@@ -29,8 +29,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert fmha.fmha_version() >= 100
-    for s in range(7):
-        assert fmha.fmha_status_string(s)
+    for s in range(8):
+        assert fmha.fmha_status_string(s) and fmha.fmha_status_string(s) != "unknown status"
     assert fmha.fmha_status_string(0) == "ok"
     assert fmha.fmha_status_string(99) == "unknown status"
 
@@ -123,6 +123,37 @@ def test_splitkv_workspace_size_packed_uses_total_rows():
     need = fmha.fmha_fwd_splitkv_workspace_size(3, 4, 3000, 8, 2, 64, vl)
     assert need > 0 and need % (7 * 8 * 65 * 4) == 0
     assert fmha.fmha_fwd_splitkv_workspace_size(3, 4, 3000, 6, 4, 64) == 0  # H % H_kv != 0
+
+
+# ---- allocation-free split-KV entry point: host validation (nothing here reaches the device) ----
+def call_noalloc(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Sq=1, Sk=300, H=4, H_kv=2, D=64, scale=0.125, mask="none",
+             dtype="f16", o_scale=1.0, varlen=None, stream=None)
+    a.update(kw)
+    return fmha.fmha_fwd_splitkv_noalloc(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(v=None), 1), (dict(B=-1), 2), (dict(D=96), 2), (dict(dtype="f8e4m3", D=128), 3),
+    (dict(q=P + 4), 4), (dict(scale=0.0), 5),
+    # 64 sequences x 16 new tokens x 64 heads x D 128: the partials need more than the 32 MiB scratch
+    (dict(B=64, Sq=16, Sk=8192, H=64, H_kv=8, D=128), 7),
+])
+def test_noalloc_invalid_arguments_are_rejected(kw, status):
+    assert call_noalloc(**kw) == status
+
+
+def test_noalloc_limit_is_the_workspace_size():
+    # the largest shapes are refused exactly when the caller-workspace entry point would need more
+    # than 32 MiB of workspace
+    big = (64, 16, 8192, 64, 8, 128)
+    assert fmha.fmha_fwd_splitkv_workspace_size(*big) > 32 << 20
+    assert fmha.fmha_fwd_splitkv_workspace_size(16, 1, 8192, 32, 8, 128) <= 32 << 20
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Sq=0)])
+def test_noalloc_empty_problems_return_ok_without_launch(kw):
+    assert call_noalloc(**kw) == 0
 
 
 def test_splitkv_workspace_size_ignores_kv_bytes():
