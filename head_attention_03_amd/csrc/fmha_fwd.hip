@@ -204,24 +204,44 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   int n_stream = 0;  // K/V tiles of the whole stream
   for (int k = 0; k < n_items; ++k) n_stream += item_tiles(k);
 
+  // Buffer descriptors are rebased as the work moves: Q and O per q-tile (at its first row), K
+  // and V per tile window (at the tile a load cursor stands on), each bounded by the end of the
+  // sequence, so every in-descriptor offset stays small however long the sequence is.
   const uint32_t qstride = (uint32_t)p.H * D * E;     // bytes between rows of one head
   const uint32_t kstride = (uint32_t)p.H_kv * D * E;
-  const size_t q_base = ((size_t)q_row0 * p.H + h) * D * E;
+  const char* q_seq = (const char*)p.q + ((size_t)q_row0 * p.H + h) * D * E;
+  char* o_seq = (char*)p.o + ((size_t)q_row0 * p.H + h) * D * E;
   const size_t k_base = ((size_t)k_row0 * p.H_kv + kvh) * D * E;
-  const uint32_t q_bytes = Sq_b > 0 ? (uint32_t)(Sq_b - 1) * qstride + RB : 0;
-  const uint32_t k_bytes = Sk_b > 0 ? (uint32_t)(Sk_b - 1) * kstride + RB : 0;
-  const i32x4 rq = make_rsrc_words((const char*)p.q + q_base, q_bytes);
-  const i32x4 rk = make_rsrc_words((const char*)p.k + k_base, k_bytes);
-  const i32x4 rv = make_rsrc_words((const char*)p.v + k_base, k_bytes);
-  const auto ro = make_rsrc((const char*)p.o + q_base, q_bytes);
+  const char* k_seq = (const char*)p.k + k_base;
+  const char* v_seq = (const char*)p.v + k_base;
+  const uint64_t q_bytes = Sq_b > 0 ? (uint64_t)(Sq_b - 1) * qstride + RB : 0;
+  const uint64_t k_bytes = Sk_b > 0 ? (uint64_t)(Sk_b - 1) * kstride + RB : 0;
+  // bytes of a sequence from byte `from` on (0 past its end; a bound of 2^31 is far beyond the
+  // three tiles or one q-tile a descriptor is ever used for)
+  auto rest = [](uint64_t bytes, uint64_t from) __attribute__((always_inline)) {
+    const uint64_t r = from < bytes ? bytes - from : 0;
+    return (uint32_t)(r < 0x80000000ull ? r : 0x80000000ull);
+  };
+  auto q_rsrc = [&](int row0) __attribute__((always_inline)) {  // Q rows from row0 on
+    const uint64_t from = (uint64_t)row0 * qstride;
+    return make_rsrc_words(q_seq + from, rest(q_bytes, from));
+  };
+  auto o_rsrc = [&](int row0) __attribute__((always_inline)) {  // O rows from row0 on
+    const uint64_t from = (uint64_t)row0 * qstride;
+    return make_rsrc(o_seq + from, rest(q_bytes, from));
+  };
+  auto kv_rsrc = [&](const char* seq, uint64_t from) __attribute__((always_inline)) {  // K or V from byte `from`
+    return make_rsrc_words(seq + from, rest(k_bytes, from));
+  };
 
   // per item and wave: first row, this lane's query row, the first tile that some row of
   // the wave does not see completely (the mask is applied from there on), and the last key
   // visible to this lane's query, less the lane's key offset 4 h32 inside a tile.  The first
   // row of an item sees the fewest keys, so item_full(k), the first tile that some row of
   // the item does not see completely, is the least w_full of its waves.
-  int qw0, qi, w_full, vis_last;
+  int iq0, qw0, qi, w_full, vis_last;
   auto set_rows = [&](int k) __attribute__((always_inline)) {
+    iq0 = item_q0(k);
     qw0 = item_q0(k) + 32 * rblk;
     qi = qw0 + l32;
     w_full = 0x7fffffff;  // a wave with no row in the sequence: its output is dropped anyway
@@ -247,7 +267,8 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   const uint32_t q_lds = lds0 + (uint32_t)(NSTAGE * STAGE + wave_u * 32 * RB);
   const int rblk_u = 2 * (wave_u & 3) + (wave_u >> 2);  // rblk, in a scalar register
   auto load_q = [&](int k) __attribute__((always_inline)) {
-    const uint32_t row0 = (uint32_t)(item_q0(k) + 32 * rblk_u) * qstride;
+    const i32x4 rq = q_rsrc(item_q0(k));
+    const uint32_t row0 = (uint32_t)(32 * rblk_u) * qstride;
 #pragma unroll
     for (int i = 0; i < QBLK; ++i) {
       const int pos = 64 * i + lane;  // 16-byte chunk position inside the wave's block
@@ -278,13 +299,24 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   const uint32_t tile_bytes = (uint32_t)BN * kstride;
   constexpr uint32_t kStages = NSTAGE * STAGE;
   static_assert(7 * 1024 < STAGE, "a wave's block offset stays inside the first stage");
+  // The K descriptor starts at byte k_at of the sequence's K rows and the cursor's K tile lies
+  // lk_off bytes past it; k_at only moves when lk_off reaches 2^30 (sequences past 1 GiB), and
+  // back to 0 at a q-tile change after such a move.  V follows K one tile behind: at each advance
+  // it takes over K's offset, and its descriptor is the V one at K's base of the step before.
+  // These moves happen in special steps only; a plain step finds both bases unchanged.
   int lt = 0, ln = item_tiles(0), litem = 0;
-  uint32_t lk_off = 0, lv_off = 0u - tile_bytes;
+  uint64_t k_at = 0;
+  uint32_t lk_off = 0, lv_off = 0u - tile_bytes;  // (V before the first tile: out of bounds)
+  i32x4 rk = kv_rsrc(k_seq, 0), rv = kv_rsrc(v_seq, 0), rv_next = rv;
+  bool k_base_moved = false;                 // the last advance moved K's base
+  constexpr uint32_t kRebase = 0x40000000u;  // far below 2^31 less three tiles
   uint32_t l_st = lds0 + (uint32_t)wave_u * 1024;
   auto advance = [&]() __attribute__((always_inline)) {
     lv_off = lk_off;
+    rv = rv_next;
     l_st += STAGE;
     if (l_st >= lds0 + kStages) l_st -= kStages;
+    k_base_moved = false;
     if ((lt + 1 < ln) | (litem + 1 >= n_items)) {
       ++lt;
       lk_off += tile_bytes;
@@ -293,6 +325,17 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       lt = 0;
       lk_off = 0;
       ln = item_tiles(litem);
+      k_base_moved = k_at != 0;
+      k_at = 0;
+    }
+    if (lk_off >= kRebase) {
+      k_at += lk_off;
+      lk_off = 0;
+      k_base_moved = true;
+    }
+    if (k_base_moved) {
+      rk = kv_rsrc(k_seq, k_at);
+      rv_next = kv_rsrc(v_seq, k_at);
     }
   };
   uint32_t ld_off[2][LPP];  // per-lane byte offsets inside a tile of this wave's blocks
@@ -663,6 +706,8 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // (and one LSE store where due) and clears the item state.
   constexpr int NST = 2 * NDB;
   auto epilogue = [&]() __attribute__((always_inline)) {
+    const auto ro = o_rsrc(iq0);
+    const uint32_t orow = (uint32_t)(qi - iq0) * qstride;  // this lane's row inside the q-tile
     const float l_tot = F8 ? acc_l[0] : acc_l[0] + wave_row_sum(l_run + l_run2);
     const float inv = l_tot > 0.0f ? p.o_scale / l_tot : 0.0f;
 #pragma unroll
@@ -683,7 +728,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
           auto r = __builtin_amdgcn_permlane32_swap(pack_f8x4(x0[0], x0[1], x0[2], x0[3]),
                                                     pack_f8x4(x1[0], x1[1], x1[2], x1[3]), false, false);
           const i32x2 w = {(int)r[0], (int)r[1]};
-          __builtin_amdgcn_raw_buffer_store_b64(w, ro, (uint32_t)qi * qstride + byte, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(w, ro, orow + byte, 0, 0);
         } else {
           auto r0 = __builtin_amdgcn_permlane32_swap(T::pack(acc_o[db][4 * g0] * inv, acc_o[db][4 * g0 + 1] * inv),
                                                      T::pack(acc_o[db][4 * g1] * inv, acc_o[db][4 * g1 + 1] * inv),
@@ -692,7 +737,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
               T::pack(acc_o[db][4 * g0 + 2] * inv, acc_o[db][4 * g0 + 3] * inv),
               T::pack(acc_o[db][4 * g1 + 2] * inv, acc_o[db][4 * g1 + 3] * inv), false, false);
           const i32x4 w = {(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]};
-          __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)qi * qstride + byte, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(w, ro, orow + byte, 0, 0);
         }
       }
     // (fp8: the LSE takes the fp32 sum, which a 3-bit-mantissa rounding would move by up to ~0.06)
@@ -755,9 +800,11 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // special steps with the full bookkeeping.  plain_end() is the end of the run of plain
   // steps that starts at step u (u itself when step u is special).
   auto plain_end = [&](int u) __attribute__((always_inline)) {
-    if ((t == 0) & (k > 0)) return u;
+    if (((t == 0) & (k > 0)) | k_base_moved) return u;
     int lim = k + 1 == n_items ? n_stream : u - t + nt - 3;
     lim = min(lim, u - t + nfull);
+    // the K offset stays below the rebase point through the run (a special step rebases)
+    lim = min(lim, u + (int)((kRebase - 1 - lk_off) / tile_bytes));
     return lim > u ? lim : u;
   };
   auto plain_advance = [&]() __attribute__((always_inline)) {
@@ -917,14 +964,12 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
   if (!(scale > 0.0f) || !isfinite(scale) || !isfinite(o_scale)) return FMHA_ERR_INVALID_ARGUMENT;
 
   const int64_t esz = dtype == FMHA_DTYPE_F8E4M3 ? 1 : 2;
-  // every per-sequence byte offset must fit the 31-bit range of a buffer descriptor
-  const int64_t rows_q = packed ? varlen->total_length_q : Sq;
-  const int64_t rows_k = packed ? varlen->total_length_k : Sk;
+  // The kernel rebases its buffer descriptors per q-tile and per K/V tile window, so sequences
+  // may be of any length; what one descriptor spans (three K/V tiles, one q-tile of 256 rows)
+  // must stay inside the 31-bit offset range, and row indices inside int32.
   const int64_t lim = (int64_t)1 << 31;
-  if (rows_q * H * D * esz >= lim || rows_k * H_kv * D * esz >= lim) return FMHA_ERR_UNSUPPORTED;
-  // tiles requested one before and two past the keys, and the rows of a partial last q-tile
-  // past the end of a sequence, must not wrap the 32-bit offset
   if ((int64_t)3 * (esz == 1 ? 2 * kBN : kBN) * H_kv * D * esz >= lim || (int64_t)kBM * H * D * esz >= lim) return FMHA_ERR_UNSUPPORTED;
+  if (!packed && ((int64_t)B * Sq >= lim || (int64_t)B * Sk >= lim)) return FMHA_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || Sq == 0 || (packed && varlen->total_length_q == 0)) return FMHA_OK;
 
   Params p;

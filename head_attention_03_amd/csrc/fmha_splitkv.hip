@@ -120,9 +120,12 @@ struct MergeParams {
 // split kernel: grid = B * H_kv * mblks * n_splits workgroups of kThreads
 // KV8: K and V are e4m3 (a quantised cache); they are widened to the 16-bit type of Q exactly
 // (every e4m3 value is a bf16 and an fp16 value) as the MFMA operands are read from LDS.
-template <int DT, int D, bool KV8, bool PAGED>
+// Q8 (with KV8): Q is e4m3 as well, widened to bf16 (DT) the same way: e4m3 inputs throughout,
+// computed on the 16-bit matrix cores with the probabilities in bf16; the merge writes e4m3.
+template <int DT, int D, bool KV8, bool PAGED, bool Q8 = false>
 __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
-  constexpr int E = 2;               // bytes per Q element
+  static_assert(!Q8 || KV8, "e4m3 queries come with an e4m3 K/V");
+  constexpr int E = Q8 ? 1 : 2;      // bytes per Q element
   constexpr int EK = KV8 ? 1 : 2;    // bytes per K/V element
   constexpr int RB = D * E;          // bytes per Q row
   constexpr int RBK = D * EK;        // bytes per K/V row
@@ -232,7 +235,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
 
   // Paged cache: when the split's keys lie in at most 64 pages, lane j holds the table entry of
   // the split's j-th page, loaded once here, and each tile takes its page with a lane read
-  // instead of a scalar load it would wait for (waited for below, behind the Q rows).
+  // instead of a scalar load it would wait for.  The load is waited for once, unconditionally,
+  // behind the Q rows below: the tile loads are invisible to the compiler, and a use it could
+  // not prove waited for would make it drain every request in flight (vmcnt(0)) in the loop.
   const int lp_first = paged ? k0 >> p.page_shift : 0;
   const bool pre = PAGED && n_tiles > 0 && ((k1 - 1) >> p.page_shift) - lp_first < 64;
   int page_v = 0;
@@ -247,10 +252,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
     const int rj = mblk * kRows + j;
     const int hj = kvh * p.group + rj / p.Sq, qj = rj % p.Sq;
     // rows past the group, or past the sequence, fall outside the descriptor and read 0
-    const uint32_t src = rj < p.M ? (uint32_t)qj * qstride + (uint32_t)hj * RB + (((pos % CPR) ^ swz<CPR>(j)) * 16)
+    const int chunk = (pos % CPR) ^ (Q8 ? swz8<CPR>(j) : swz<CPR>(j));
+    const uint32_t src = rj < p.M ? (uint32_t)qj * qstride + (uint32_t)hj * RB + chunk * 16
                                   : q_bytes;
     lds_load16(rq, src, q_lds + 1024 * i);
   }
+  if constexpr (PAGED) asm volatile("" : "+v"(page_v));  // the one wait for page_v (and the Q rows)
 
   // per-lane LDS offsets: Q (and 16-bit K) row l32, chunk h32 of each k-step; V^T transpose
   // read (as fmha_fwd).  e4m3 K/V tiles use fmha_fwd's fp8 row swizzle: K row l32, 8 bytes at
@@ -286,7 +293,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
     if (paged) {
       const int ps = 1 << p.page_shift;
       const int lp = kt >> p.page_shift;
-      const int phys = pre ? __builtin_amdgcn_readlane(page_v, lp - lp_first) : p.block_table[(size_t)b * p.bt_stride + lp];
+      // (longer splits: a scalar load through the constant address space, waited on lgkmcnt,
+      // which the tile loads in flight do not count toward)
+      const int phys = pre ? __builtin_amdgcn_readlane(page_v, lp - lp_first)
+                           : ((const __attribute__((address_space(4))) int32_t*)p.block_table)[(size_t)b * p.bt_stride + lp];
       const bool ok = (unsigned)phys < (unsigned)p.num_pages;
       const int valid = min(ps, Sk_b - (lp << p.page_shift));  // >= 1: the tile starts inside the sequence
       const size_t pb = ok ? ((size_t)phys * ps * p.H_kv + kvh) * RBK : 0;
@@ -315,7 +325,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
   wait_tiles<NLD, STG - 1>(n_w);
   i32x4 qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const lds_i32x4*)(uintptr_t)((q_lds + q_lane) ^ (32 * ks));
+  for (int ks = 0; ks < KS; ++ks) {
+    if constexpr (Q8)  // e4m3 rows are swizzled and read like an e4m3 K tile, then widened
+      qf[ks] = widen8(*(const lds_i32x2*)(uintptr_t)((q_lds + l32 * RB + swz8<CPR>(l32) * 16 + 8 * h32) ^ (16 * ks)));
+    else
+      qf[ks] = *(const lds_i32x4*)(uintptr_t)((q_lds + q_lane) ^ (32 * ks));
+  }
 
   f32x16 acc_o[NDB];
 #pragma unroll
@@ -471,8 +486,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
     p.lse_part[part] = l_all > 0.0f ? (m_all + __builtin_amdgcn_logf(l_all)) * 0.69314718055994531f : -__builtin_inff();
 }
 
-// merge kernel: D / 4 threads per row, each 4 consecutive dims
-template <int DT, int D>
+// merge kernel: D / 4 threads per row, each 4 consecutive dims.  OUT8: e4m3 output, saturated
+// to the largest finite value and rounded to nearest even (as fmha_fwd's fp8 output).
+template <int DT, int D, bool OUT8 = false>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   constexpr int TPR = D / 4;
   const int t = blockIdx.x * 256 + threadIdx.x;
@@ -497,9 +513,15 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     }
   }
   const float f = wsum > 0.0f ? p.o_scale / wsum : 0.0f;
-  typedef Elem<DT> T;
-  const uint32_t lo = T::pack(acc.x * f, acc.y * f), hi = T::pack(acc.z * f, acc.w * f);
-  *(i32x2*)((char*)p.o + ((size_t)row * D + 4 * part) * 2) = i32x2{(int)lo, (int)hi};
+  if constexpr (OUT8) {
+    auto sat = [](float x) { return __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f); };
+    *(uint32_t*)((char*)p.o + (size_t)row * D + 4 * part) =
+        pack_f8x4(sat(acc.x * f), sat(acc.y * f), sat(acc.z * f), sat(acc.w * f));
+  } else {
+    typedef Elem<DT> T;
+    const uint32_t lo = T::pack(acc.x * f, acc.y * f), hi = T::pack(acc.z * f, acc.w * f);
+    *(i32x2*)((char*)p.o + ((size_t)row * D + 4 * part) * 2) = i32x2{(int)lo, (int)hi};
+  }
   if (p.lse && part == 0) {
     const int q = row / p.H, h = row - q * p.H;  // row = (query row) * H + head
     const size_t idx = p.total_q > 0 ? (size_t)h * p.total_q + q : ((size_t)(q / p.Sq) * p.H + h) * p.Sq + q % p.Sq;
@@ -520,13 +542,13 @@ inline void plan(int64_t units, int64_t Sk, int64_t target, int32_t* n_splits, i
   *n_splits = (int32_t)(Sk > 0 ? (Sk + c - 1) / c : 1);
 }
 
-template <int DT, int D, bool KV8 = false, bool PAGED = false>
+template <int DT, int D, bool KV8 = false, bool PAGED = false, bool Q8 = false>
 hipError_t launch(const Params& p, const MergeParams& mp, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((split_kernel<DT, D, KV8, PAGED>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((split_kernel<DT, D, KV8, PAGED, Q8>), dim3(grid), dim3(kThreads), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t threads = (int64_t)mp.rows * (D / 4);
-  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, mp);
+  hipLaunchKernelGGL((merge_kernel<DT, D, Q8>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, mp);
   return hipGetLastError();
 }
 
@@ -555,7 +577,10 @@ fmha_status splitkv_plan(const void* q, const void* k, const void* v, const void
   if (packed && (varlen->total_length_q < 0 || varlen->total_length_k < 0)) return FMHA_ERR_INVALID_SHAPE;
   if ((int)dtype < 0 || (int)dtype > 2) return FMHA_ERR_UNSUPPORTED;
   if ((int)mask < 0 || (int)mask > 3) return FMHA_ERR_UNSUPPORTED;
-  if (dtype == FMHA_DTYPE_F8E4M3) return FMHA_ERR_UNSUPPORTED;  // 16-bit types only
+  // e4m3 queries (with an e4m3 K/V) run the e4m3-cache kernels, which need rows of 64 bytes or more
+  const bool q8 = dtype == FMHA_DTYPE_F8E4M3;
+  if (q8 && D == 32) return FMHA_ERR_UNSUPPORTED;
+  const bool k8 = kv8 || q8;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FMHA_ERR_MISALIGNED;
   if ((uintptr_t)lse & 3) return FMHA_ERR_MISALIGNED;
   const int64_t rows_q = packed ? varlen->total_length_q : Sq;
@@ -563,7 +588,8 @@ fmha_status splitkv_plan(const void* q, const void* k, const void* v, const void
   const int64_t lim = (int64_t)1 << 31;
   // per-sequence byte offsets (tiles run up to one wave-tile round past a split) fit 31 bits;
   // a paged cache addresses each page on its own
-  if (rows_q * H * D * 2 >= lim || (!paged && (rows_k + kWaves * kTN * kStages) * H_kv * D * 2 >= lim))
+  const int64_t qe = q8 ? 1 : 2, ke = k8 ? 1 : 2;
+  if (rows_q * H * D * qe >= lim || (!paged && (rows_k + kWaves * kTN * kStages) * H_kv * D * ke >= lim))
     return FMHA_ERR_UNSUPPORTED;
   const int64_t q_rows = packed ? (int64_t)varlen->total_length_q : (int64_t)B * Sq;
   const int64_t group = H > 0 ? H / H_kv : 1;
@@ -571,7 +597,7 @@ fmha_status splitkv_plan(const void* q, const void* k, const void* v, const void
   const int64_t mblks = (M + kRows - 1) / kRows;
   // The workspace is sized for the larger split target, so one size serves both cache types.
   int32_t n_splits = 1, chunk = kWaves * kTN, ws_splits = 1, ws_chunk = kWaves * kTN;
-  plan((int64_t)B * H_kv * mblks, Sk, kv8 ? kTargetWgs8 : kTargetWgs, &n_splits, &chunk);
+  plan((int64_t)B * H_kv * mblks, Sk, k8 ? kTargetWgs8 : kTargetWgs, &n_splits, &chunk);
   plan((int64_t)B * H_kv * mblks, Sk, kTargetWgs8, &ws_splits, &ws_chunk);
   const int64_t rows = q_rows * H;
   if (rows >= lim || (int64_t)ws_splits * rows * D >= lim * 2) return FMHA_ERR_UNSUPPORTED;
@@ -668,7 +694,10 @@ fmha_status splitkv_run(const void* q, const void* k, const void* v, void* o, fl
   mp.o_scale = o_scale;
 
   hipError_t err = hipSuccess;
-  if (dtype == FMHA_DTYPE_BF16) {
+  if (dtype == FMHA_DTYPE_F8E4M3) {  // e4m3 Q, K, V widened to bf16 for the matrix cores
+    if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64, true, false, true>(p, mp, (int)grid, stream);
+    if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128, true, false, true>(p, mp, (int)grid, stream);
+  } else if (dtype == FMHA_DTYPE_BF16) {
     if (D == 32) err = fmha::skv::launch<fmha::kBF16, 32>(p, mp, (int)grid, stream);
     if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64>(p, mp, (int)grid, stream);
     if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128>(p, mp, (int)grid, stream);
@@ -732,6 +761,7 @@ fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const voi
   if (ps < kTN || ps > (1 << 16) || (ps & (ps - 1))) return FMHA_ERR_INVALID_SHAPE;
   if (!kv8 && paged->kv_dtype != dtype) return FMHA_ERR_UNSUPPORTED;
   if (kv8 && D == 32) return FMHA_ERR_UNSUPPORTED;  // e4m3 rows of 32 bytes: not built
+  const bool q8 = dtype == FMHA_DTYPE_F8E4M3;     // (e4m3 queries need an e4m3 cache)
   if (paged->max_pages_per_seq < 0 || paged->num_pages < 0) return FMHA_ERR_INVALID_SHAPE;
   if (!no_keys && (paged->num_pages < 1 || (int64_t)paged->max_pages_per_seq * ps < Sk)) return FMHA_ERR_INVALID_SHAPE;
   if ((int64_t)ps * H_kv * D * 2 >= ((int64_t)1 << 31)) return FMHA_ERR_UNSUPPORTED;
@@ -770,7 +800,10 @@ fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const voi
   if (no_keys) {
     // An empty cache: the block table and the lengths may be NULL, and no key is read.  The
     // contiguous kernels (no table) give every row O = 0 and LSE = -inf, whatever the cache type.
-    if (dtype == FMHA_DTYPE_BF16) {
+    if (q8) {
+      if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64, true, false, true>(p, mp, (int)grid, stream);
+      if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128, true, false, true>(p, mp, (int)grid, stream);
+    } else if (dtype == FMHA_DTYPE_BF16) {
       if (D == 32) err = fmha::skv::launch<fmha::kBF16, 32>(p, mp, (int)grid, stream);
       if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64>(p, mp, (int)grid, stream);
       if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128>(p, mp, (int)grid, stream);
@@ -780,7 +813,10 @@ fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const voi
       if (D == 128) err = fmha::skv::launch<fmha::kF16, 128>(p, mp, (int)grid, stream);
     }
   } else if (kv8) {
-    if (dtype == FMHA_DTYPE_BF16) {
+    if (q8) {
+      if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64, true, true, true>(p, mp, (int)grid, stream);
+      if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128, true, true, true>(p, mp, (int)grid, stream);
+    } else if (dtype == FMHA_DTYPE_BF16) {
       if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64, true, true>(p, mp, (int)grid, stream);
       if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128, true, true>(p, mp, (int)grid, stream);
     } else {

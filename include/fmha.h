@@ -63,10 +63,13 @@ typedef enum {
   FMHA_ERR_NULL_POINTER = 1,     /* q, o, or (when there are keys) k or v is NULL, or only one
                                     cu_seqlens pointer is set */
   FMHA_ERR_INVALID_SHAPE = 2,    /* negative sizes, H % H_kv != 0, D not in {32, 64, 128}, totals < 0 */
-  FMHA_ERR_UNSUPPORTED = 3,      /* dtype/mask enum out of range, or a tensor too large for 32-bit
-                                    offsets (any tensor of 2^31 bytes or more, or three K/V tiles --
-                                    192 16-bit or 384 e4m3 rows -- or 256 Q rows of 2^31 bytes or
-                                    more) */
+  FMHA_ERR_UNSUPPORTED = 3,      /* dtype/mask enum out of range, or a problem too large for the
+                                    kernels' 32-bit offsets.  fmha_fwd rebases its offsets per
+                                    q-tile and per K/V tile, so sequences may be of any length; it
+                                    refuses only three K/V tiles (192 16-bit or 384 e4m3 rows) or
+                                    256 Q rows of 2^31 bytes or more, and dense B * Sq or B * Sk of
+                                    2^31 rows or more.  fmha_fwd_splitkv and fmha_bwd refuse any
+                                    tensor of one sequence of 2^31 bytes or more. */
   FMHA_ERR_MISALIGNED = 4,       /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   FMHA_ERR_INVALID_ARGUMENT = 5, /* scale not finite and > 0, or o_scale not finite */
   FMHA_ERR_HIP = 6,              /* the kernel launch failed (hipGetLastError), or the device address
@@ -144,7 +147,11 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
  *                    contents on entry do not matter and are overwritten (calls that
  *                    overlap in time must not share it)
  *   workspace_bytes  its size
- *   dtype            FMHA_DTYPE_F16 or FMHA_DTYPE_BF16 (fp8: FMHA_ERR_UNSUPPORTED)
+ *   dtype            FMHA_DTYPE_F16, FMHA_DTYPE_BF16, or FMHA_DTYPE_F8E4M3 with D 64 or 128: e4m3 q,
+ *                    k, v and o, the per-tensor dequantisation scales folded into scale and o_scale as
+ *                    for fmha_fwd, the output saturated to +-448.  e4m3 values widen exactly to bf16,
+ *                    so the fp8 call runs on the 16-bit matrix cores with its probabilities in bf16
+ *                    (fp8 with D == 32: FMHA_ERR_UNSUPPORTED).
  * Errors as fmha_fwd, and: workspace NULL -> FMHA_ERR_NULL_POINTER, not 16-byte aligned
  * -> FMHA_ERR_MISALIGNED, smaller than needed -> FMHA_ERR_INVALID_ARGUMENT (checked only
  * when there is work).
@@ -264,11 +271,13 @@ typedef struct {
  * are dense ([B, Sq, H, D], [B, H, Sq]); Sk is the most keys of any sequence (it sizes the
  * splits, and max_pages_per_seq * page_size must reach it).  The causal-qend offset of sequence b
  * is seqlens_k[b] - Sq.  workspace: fmha_fwd_splitkv_workspace_size(B, Sq, Sk, H, H_kv, D, NULL)
- * bytes.  dtype (q and o): FMHA_DTYPE_F16 or FMHA_DTYPE_BF16.
+ * bytes.  dtype (q and o): FMHA_DTYPE_F16 or FMHA_DTYPE_BF16, or FMHA_DTYPE_F8E4M3 over an e4m3 cache
+ * (q and o e4m3 as in fmha_fwd_splitkv; D 64 or 128).
  * Errors as fmha_fwd_splitkv, and: paged NULL, or (when Sk > 0) k_cache, v_cache, block_table or
  * seqlens_k NULL -> FMHA_ERR_NULL_POINTER; page_size not a power of two in [32, 65536],
  * max_pages_per_seq * page_size < Sk, or num_pages < 1 -> FMHA_ERR_INVALID_SHAPE; kv_dtype neither
- * dtype nor FMHA_DTYPE_F8E4M3, or an e4m3 cache with D == 32 -> FMHA_ERR_UNSUPPORTED.
+ * dtype nor FMHA_DTYPE_F8E4M3 (e4m3 queries need an e4m3 cache), or an e4m3 cache with D == 32 ->
+ * FMHA_ERR_UNSUPPORTED.
  */
 fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                                    int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D, float scale,

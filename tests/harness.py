@@ -299,6 +299,6 @@ def oracle_paged(inp, block_table=None, k_cache=None):
     vc = oracle.decode(to_bits(inp.v_cache), kvt) * inp.v_scale
     if k_cache is not None and kc.shape[0] > vc.shape[0]:
         vc = np.concatenate([vc, np.zeros((kc.shape[0] - vc.shape[0],) + vc.shape[1:])])
-    q = oracle.decode(to_bits(inp.q), inp.dtype)
+    q = oracle.decode(to_bits(inp.q), inp.dtype) * inp.q_scale
     bt = inp.block_table if block_table is None else block_table
     return oracle.attention_paged(q, kc, vc, bt, inp.seqlens_k, inp.scale, inp.mask, o_scale=inp.o_scale)

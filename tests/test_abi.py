@@ -51,7 +51,7 @@ def call(**kw):
     (dict(H=3, H_kv=2), 2), (dict(H_kv=0), 2), (dict(D=48), 2), (dict(D=256), 2), (dict(D=0), 2),
     (dict(varlen=fmha.make_varlen(P, P, -1, 16)), 2),
     (dict(dtype=3), 3), (dict(dtype=-1), 3), (dict(mask=4), 3), (dict(mask=-1), 3),
-    (dict(Sq=1 << 22, H=64, H_kv=64, D=128), 3),
+    (dict(B=1 << 10, Sq=1 << 21, H=64, H_kv=64, D=128), 3),  # 2^31 query rows: past int32 row indices
     (dict(dtype="f8e4m3", D=32, q=P + 2), 4), (dict(H=1 << 16, H_kv=1 << 16, D=128, Sq=1, Sk=1), 3),
     (dict(H=1 << 15, H_kv=1, D=128, Sq=1, Sk=1), 3),
     (dict(q=P + 2), 4), (dict(o=P + 8), 4), (dict(lse=P + 2), 4),
@@ -85,7 +85,7 @@ def call_skv(**kw):
     (dict(q=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(workspace=None), 1),
     (dict(varlen=fmha.make_varlen(P, None, 1, 300)), 1),
     (dict(B=-1), 2), (dict(H=3, H_kv=2), 2), (dict(D=96), 2),
-    (dict(dtype="f8e4m3", D=128), 3), (dict(dtype=7), 3), (dict(mask=9), 3),
+    (dict(dtype="f8e4m3", D=32), 3), (dict(dtype=7), 3), (dict(mask=9), 3),
     (dict(Sk=1 << 22, H=64, H_kv=64, D=128), 3),
     (dict(q=P + 4), 4), (dict(lse=P + 1), 4), (dict(workspace=P + 8), 4),
     (dict(scale=0.0), 5), (dict(o_scale=float("nan")), 5), (dict(workspace_bytes=100), 5),
@@ -134,7 +134,7 @@ def call_noalloc(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(q=None), 1), (dict(v=None), 1), (dict(B=-1), 2), (dict(D=96), 2), (dict(dtype="f8e4m3", D=128), 3),
+    (dict(q=None), 1), (dict(v=None), 1), (dict(B=-1), 2), (dict(D=96), 2), (dict(dtype="f8e4m3", D=32), 3),
     (dict(q=P + 4), 4), (dict(scale=0.0), 5),
     # 64 sequences x 16 new tokens x 64 heads x D 128: the partials need more than the 32 MiB scratch
     (dict(B=64, Sq=16, Sk=8192, H=64, H_kv=8, D=128), 7),
@@ -232,7 +232,10 @@ def call_paged(**kw):
     (dict(paged=fmha.make_paged_kv(P, P, 4, 1 << 17, 8, "bf16")), 2),
     (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 8, "f16")), 3), (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 8, 7)), 3),
     (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 8, "f8e4m3"), D=32), 3),
-    (dict(dtype="f8e4m3"), 3), (dict(H=3), 2), (dict(D=48), 2),
+    (dict(dtype="f8e4m3"), 3),  # e4m3 queries over a bf16 cache
+    (dict(dtype="f8e4m3", paged=fmha.make_paged_kv(P, P, 4, 128, 8, "f8e4m3"), D=32), 3),
+    (dict(dtype="f8e4m3", paged=fmha.make_paged_kv(P, P, 4, 128, 8, "f8e4m3"), q=P + 4), 4),  # accepted up to alignment
+    (dict(H=3), 2), (dict(D=48), 2),
     (dict(k_cache=P + 8), 4), (dict(workspace=P + 8), 4),
     (dict(scale=0.0), 5), (dict(workspace_bytes=16), 5),
     (dict(B=0), 0), (dict(Sk=0, k_cache=None, v_cache=None, paged=fmha.make_paged_kv(None, None, 0, 128, 0, "bf16"), B=0), 0),

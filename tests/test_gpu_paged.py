@@ -47,6 +47,23 @@ def test_paged_decode(case):
     compare(f"paged {case}", res.o_bits, dtype, o, res.lse, lse)
 
 
+@pytest.mark.parametrize("case", [
+    (4, 1, [4097, 1, 300, 0], 32, 8, 128, "none", 128),
+    (3, 4, [1000, 64, 2500], 16, 2, 64, "causal_qend", 32),
+    (2, 2, [2112, 500], 8, 8, 128, "none", 32),  # a split over more than 64 pages: table read per tile
+], ids=lambda c: f"B{c[0]}-q{c[1]}-H{c[3]}/{c[4]}-D{c[5]}-{c[6]}-p{c[7]}")
+def test_paged_fp8_queries(case):
+    # e4m3 queries and output over an e4m3 cache (NaN codes in the pages no sequence owns)
+    B, Sq, lk, H, H_kv, D, mask, ps = case
+    inp = make_paged(5150 + sum(lk) + ps, B, Sq, lk, H, H_kv, D, "f8e4m3", ps, mask=mask, o_scale=0.5,
+                     kv_dtype="f8e4m3")
+    log(f"[case] paged fp8 {case} seed={inp.seed} pages={inp.num_pages}")
+    res = run_paged(inp)
+    assert res.status == 0
+    o, lse = oracle_paged(inp)
+    compare(f"paged fp8 {case}", res.o_bits, "f8e4m3", o, res.lse, lse)
+
+
 def test_paged_equals_contiguous_bitwise():
     # the same split plan and tile order as fmha_fwd_splitkv on the gathered (packed) keys
     import head_attention_03_amd as fmha

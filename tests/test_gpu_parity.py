@@ -339,3 +339,63 @@ def test_planted_oracle_mistake_is_detected():
         wrong[0, :, h] = (e / e.sum(1, keepdims=True)) @ v[0, :, h]
     err = np.abs(oracle.decode(res.o_bits, "f16") - wrong).max()
     assert err > 10 * TOL["f16"], err
+
+
+# ----------------------------------------------------------------------------------------------
+# sequences whose tensors exceed 32-bit byte offsets (descriptors rebased per q-tile and per K/V
+# tile window); inputs drawn on the device, rows checked one at a time against the oracle
+# ----------------------------------------------------------------------------------------------
+def _long_rows_case(name, inp, picks):
+    dev = torch.device("cuda:0")
+    log(f"[case] {name}: B={inp.B} Sq={inp.Sq} Sk={inp.Sk} H={inp.H}/{inp.H_kv} D={inp.D} {inp.mask} "
+        f"seed={inp.seed} ({inp.k.numel() * inp.k.element_size() / 2**30:.2f} GiB per K/V tensor)")
+    o = torch.empty_like(inp.q)
+    lse = torch.empty((inp.B, inp.H, inp.Sq), dtype=torch.float32, device=dev)
+    import head_attention_03_amd as fmha
+    st = fmha.fmha_fwd(inp.q, inp.k, inp.v, o, lse, inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D, inp.kernel_scale,
+                       inp.mask, inp.dtype, 1.0, None, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert st == 0, fmha.fmha_status_string(st)
+    group = inp.H // inp.H_kv
+    heads = sorted({h for _, h, _ in picks})
+    got, exp_o, got_lse, exp_lse = [], [], [], []
+    for h in heads:  # the oracle reads back exactly the stored values of one head at a time
+        rows = [(b, i) for b, hh, i in picks if hh == h]
+        kvh = h // group
+        k_h = oracle.decode(to_bits(inp.k[:, :, kvh:kvh + 1].cpu()), inp.dtype)
+        v_h = oracle.decode(to_bits(inp.v[:, :, kvh:kvh + 1].cpu()), inp.dtype)
+        q_h = oracle.decode(to_bits(inp.q[:, :, h:h + 1].cpu()), inp.dtype)
+        o_rows, l_rows = oracle.attention_rows(q_h, k_h, v_h, inp.scale, inp.mask, [(b, 0, i) for b, i in rows])
+        exp_o.append(o_rows)
+        exp_lse.append(l_rows)
+        got.append(np.stack([to_bits(o[b, i, h].cpu()) for b, i in rows]))
+        got_lse.append(np.array([float(lse[b, h, i]) for b, i in rows]))
+        del k_h, v_h, q_h
+    compare(f"{name} ({sum(len(x) for x in got)} rows)", np.concatenate(got), inp.dtype, np.concatenate(exp_o),
+            np.concatenate(got_lse), np.concatenate(exp_lse))
+
+
+def test_long_prefill_131072_keys():
+    # B=1, H=64, D=128, 131072 queries and keys: 2 GiB per tensor, 4 MiB rows of all heads
+    from workloads import make_dense_on_device
+    inp = make_dense_on_device(3300, 1, 131072, 131072, 64, 64, 128, "bf16", mask="causal_qbegin")
+    S = inp.Sq
+    rng = np.random.default_rng(3300)
+    rows = [0, 1, 255, 256, 65535, 65536, S - 257, S - 256, S - 2, S - 1] + [int(x) for x in rng.integers(0, S, 6)]
+    picks = [(0, h, i) for h in (0, 37, 63) for i in rows]
+    _long_rows_case("long prefill 131072", inp, picks)
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_keys_beyond_4gib_per_tensor():
+    # 270336 keys x 64 heads x D 128 (4.1 GiB per K/V tensor): K/V offsets past 2^32, reached
+    # by rows aligned to the last key
+    from workloads import make_dense_on_device
+    inp = make_dense_on_device(3301, 1, 1000, 270336, 64, 64, 128, "f16", mask="causal_qend")
+    rng = np.random.default_rng(3301)
+    rows = [0, 1, 255, 256, 511, 512, 998, 999] + [int(x) for x in rng.integers(0, 1000, 4)]
+    picks = [(0, h, i) for h in (1, 62) for i in rows]
+    _long_rows_case("keys beyond 4 GiB", inp, picks)
+    del inp
+    torch.cuda.empty_cache()

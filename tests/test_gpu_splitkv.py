@@ -83,3 +83,33 @@ def test_splitkv_bitwise_repeatable():
     inp = make_dense(3500, 3, 1, 9000, 16, 2, 128, "f16", mask="none")
     runs = [run_dense(inp, want_lse=True, splitkv=True) for _ in range(2)]
     assert np.array_equal(runs[0].o_bits, runs[1].o_bits) and np.array_equal(runs[0].lse, runs[1].lse)
+
+
+# e4m3 Q, K and V (per-tensor scales folded into scale and o_scale), e4m3 output with output
+# scale 0.5: the fp8 tolerance of fmha_fwd
+DECODE_FP8 = [
+    # (B, Sq, Sk, H, H_kv, D, mask)
+    (4, 1, 4097, 32, 8, 128, "none"),
+    (2, 4, 1000, 16, 2, 64, "causal_qend"),
+    (3, 1, 37, 8, 8, 128, "none"),
+    (2, 16, 3000, 8, 2, 128, "residual"),
+    (1, 130, 100, 4, 2, 64, "causal_qend"),   # rows without keys: O = 0, LSE = -inf
+    (8, 1, 16384, 32, 8, 128, "causal_qend"),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_FP8, ids=lambda c: f"B{c[0]}-q{c[1]}-k{c[2]}-H{c[3]}/{c[4]}-D{c[5]}-{c[6]}")
+def test_splitkv_fp8_decode(case):
+    B, Sq, Sk, H, H_kv, D, mask = case
+    _dense(f"fp8 {case}", make_dense(3150 + Sk + Sq, B, Sq, Sk, H, H_kv, D, "f8e4m3", mask=mask, o_scale=0.5))
+
+
+def test_splitkv_fp8_varlen():
+    lq = [1, 2, 0, 3]
+    lk = [5000, 1, 0, 777]
+    inp = make_varlen(3460, lq, lk, 16, 4, 128, "f8e4m3", mask="causal_qend", o_scale=0.5, poison_pads=True)
+    log(f"[case] splitkv fp8 varlen seqlens_q={lq} seqlens_k={lk}")
+    res = run_varlen(inp, want_lse=True, splitkv=True)
+    assert res.status == 0
+    o, lse = oracle_varlen(inp)
+    compare("splitkv fp8 varlen", res.o_bits[inp.pad_q:], inp.dtype, o, res.lse, lse)

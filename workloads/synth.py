@@ -216,6 +216,34 @@ def make_dense(seed: int, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int, d
                        scale=float(scale), o_scale=float(o_scale), seed=seed, q_scale=sq, k_scale=sk, v_scale=sv)
 
 
+def make_dense_on_device(seed: int, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int, dtype: str,
+                         mask: str = "none", device="cuda:0") -> DenseInputs:
+    """Dense 16-bit inputs too large to draw on the host in reasonable time (gigabytes per tensor):
+    i.i.d. N(0, 1) drawn in float32 by torch's seeded generator on ``device`` (Philox, in the
+    order Q, K, V), rounded to the storage type (round to nearest even), and left on the device.
+    A different stream from ``make_dense`` for the same seed; the tests read back the exact stored
+    values of the rows they check."""
+    if dtype not in ("f16", "bf16"):
+        raise ValueError("device-drawn inputs are 16-bit")
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+
+    def draw(shape):
+        out = torch.empty(shape, dtype=TORCH_DTYPES[dtype], device=device)
+        rows = max(1, (1 << 28) // max(1, int(np.prod(shape[2:])) * shape[0]))  # ~1 GiB of float32 at a time
+        for r0 in range(0, shape[1], rows):
+            r1 = min(shape[1], r0 + rows)
+            out[:, r0:r1] = torch.randn((shape[0], r1 - r0) + tuple(shape[2:]), generator=g, device=device,
+                                        dtype=torch.float32).to(TORCH_DTYPES[dtype])
+        return out
+
+    q = draw((B, Sq, H, D))
+    k = draw((B, Sk, H_kv, D))
+    v = draw((B, Sk, H_kv, D))
+    return DenseInputs(q=q, k=k, v=v, B=B, Sq=Sq, Sk=Sk, H=H, H_kv=H_kv, D=D, dtype=dtype, mask=mask,
+                       scale=1.0 / math.sqrt(D), o_scale=1.0, seed=seed)
+
+
 def make_grad(seed: int, shape: Sequence[int], dtype: str) -> torch.Tensor:
     """Upstream gradient dO for the backward pass: N(0, 1) float32 from its own stream, cast to dtype."""
     t, _ = _to_storage(draw_normal(np.random.default_rng(seed), shape), dtype)
@@ -282,7 +310,7 @@ def make_paged(seed: int, B: int, Sq: int, seqlens_k: Sequence[int], H: int, H_k
     num_pages = sum(pages_b) + int(extra_pages)
     max_pages = max(pages_b + [1])
     kv_dtype = kv_dtype or dtype
-    q, _ = _to_storage(draw_normal(rng, (B, Sq, H, D)), dtype)
+    q, sq = _to_storage(draw_normal(rng, (B, Sq, H, D)), dtype)
     k32 = draw_normal(rng, (num_pages, page_size, H_kv, D))
     v32 = draw_normal(rng, (num_pages, page_size, H_kv, D))
     perm = rng.permutation(num_pages).astype(np.int32)
@@ -317,7 +345,8 @@ def make_paged(seed: int, B: int, Sq: int, seqlens_k: Sequence[int], H: int, H_k
         scale = 1.0 / math.sqrt(D)
     return PagedInputs(q=q, k_cache=kc, v_cache=vc, block_table=table, seqlens_k=lk, page_size=int(page_size), B=B,
                        Sq=Sq, H=H, H_kv=H_kv, D=D, dtype=dtype, mask=mask, scale=float(scale),
-                       o_scale=float(o_scale), seed=seed, k_scale=float(sk), v_scale=float(sv), kv_dtype=kv_dtype)
+                       o_scale=float(o_scale), seed=seed, q_scale=float(sq), k_scale=float(sk), v_scale=float(sv),
+                       kv_dtype=kv_dtype)
 
 
 def make_varlen(seed: int, seqlens_q: Sequence[int], seqlens_k: Sequence[int], H: int, H_kv: int, D: int,
