@@ -51,7 +51,10 @@
 // * Work order: with several q-tiles per workgroup, causal q-tiles are paired heavy with
 //   light (n-1-j with j) so every workgroup gets the same number of K/V tiles; with one,
 //   heaviest first.  Workgroups of one (sequence, head group) land on the same XCD so they
-//   share K/V in that XCD's L2.
+//   share K/V in that XCD's L2; with several q-tiles each, the workgroups of one (sequence,
+//   head) are dispatched side by side, so they run at the same time and stream its K/V tiles
+//   together, and the host lowers the q-tiles per workgroup where that keeps the K/V streamed
+//   by an XCD's resident workgroups inside its L2.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -94,6 +97,7 @@ struct Params {
   int32_t causal;   // 1 for both causal masks
   int32_t qend;     // causal aligned to the last key
   int32_t xcd_per;  // (sequence, head) pairs per XCD when B*H % 8 == 0, else 0
+  int32_t ngrp;     // workgroups per (sequence, head)
   float scale_log2; // scale * log2(e)
   float o_scale;
 };
@@ -155,8 +159,13 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   int bh, grp;
   if (p.xcd_per) {  // round-robin dispatch puts workgroup x on XCD x % 8
     const int slot = x >> 3;
-    grp = slot / p.xcd_per;
-    bh = (x & 7) * p.xcd_per + slot % p.xcd_per;
+    if (p.ipw > 1) {  // the workgroups of one (sequence, head) side by side
+      grp = slot % p.ngrp;
+      bh = (x & 7) * p.xcd_per + slot / p.ngrp;
+    } else {  // the heaviest q-tile of every (sequence, head) first
+      grp = slot / p.xcd_per;
+      bh = (x & 7) * p.xcd_per + slot % p.xcd_per;
+    }
   } else {
     grp = x / BH;
     bh = x % BH;
@@ -999,10 +1008,30 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
   ipw = ipw < 1 ? 1 : ipw > 8 ? 8 : ipw;
   if (ipw > n_qtiles) ipw = n_qtiles;
   if (p.causal && ipw > 1) ipw &= ~(int64_t)1;
-  p.ipw = (int32_t)ipw;
-  const int64_t grid = BH * ((n_qtiles + ipw - 1) / ipw);
-  if (grid >= lim) return FMHA_ERR_UNSUPPORTED;
   p.xcd_per = (BH % 8 == 0) ? (int32_t)(BH / 8) : 0;
+  if (p.xcd_per && ipw > 2) {
+    // Every q-tile of a workgroup streams the whole (causal: visible) K/V of its head again,
+    // and the workgroups of one head, dispatched side by side, share that stream in L2 while
+    // they run together.  Fewer q-tiles per workgroup mean more workgroups per head and fewer
+    // heads on an XCD at once: take the largest halving of ipw (down to 2) at which the K/V
+    // heads the XCD's resident workgroups (one per CU) stream fit its 4 MiB L2, if any does.
+    const int64_t per_xcd = cus / 8 > 0 ? cus / 8 : 1;
+    const int64_t kv_head_bytes = (int64_t)2 * Sk * D * esz;
+    for (int64_t w = ipw; w >= 2; w /= 2) {
+      const int64_t we = p.causal ? (w & ~(int64_t)1) : w;
+      const int64_t per_head = (n_qtiles + we - 1) / we;
+      int64_t heads = (per_xcd + per_head - 1) / per_head;
+      if (heads > p.xcd_per) heads = p.xcd_per;
+      if ((heads + p.group - 1) / p.group * kv_head_bytes <= ((int64_t)4 << 20)) {
+        ipw = we;
+        break;
+      }
+    }
+  }
+  p.ipw = (int32_t)ipw;
+  p.ngrp = (int32_t)((n_qtiles + ipw - 1) / ipw);
+  const int64_t grid = BH * p.ngrp;
+  if (grid >= lim) return FMHA_ERR_UNSUPPORTED;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   p.o_scale = o_scale;
 

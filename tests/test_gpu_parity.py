@@ -118,14 +118,26 @@ def test_bitwise_repeatable():
 # several q-tiles per workgroup: enough (sequence, head, q-tile) items that every workgroup runs
 # two or more of them as one K/V stream (item changes, one- and two-tile items, ragged tiles)
 # ----------------------------------------------------------------------------------------------
-def _items_per_workgroup(B, H, Sq, mask):
+def _items_per_workgroup(B, H, Sq, mask, Sk=0, H_kv=1, D=128, esz=2):
     """The launch rule of the library: q-tiles of 256 rows, about one workgroup per compute unit,
-    at most 8 per workgroup, pairs when causal."""
+    at most 8 per workgroup, pairs when causal; then, when B*H is a multiple of 8, the largest
+    halving (down to 2) at which the K/V heads that an XCD's resident workgroups stream fit 4 MiB."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     n_qt = (Sq + 255) // 256
+    causal = mask.startswith("causal")
     ipw = max(1, min(8, B * H * n_qt // cus, n_qt))
-    if mask.startswith("causal") and ipw > 1:
+    if causal and ipw > 1:
         ipw &= ~1
+    if (B * H) % 8 == 0 and ipw > 2:
+        per_xcd, xcd_per, group = max(1, cus // 8), B * H // 8, H // H_kv
+        w = ipw
+        while w >= 2:
+            we = w & ~1 if causal else w
+            heads = min(xcd_per, -(-per_xcd // -(-n_qt // we)))
+            if -(-heads // group) * 2 * Sk * D * esz <= 4 << 20:
+                ipw = we
+                break
+            w //= 2
     return ipw
 
 
@@ -142,7 +154,7 @@ MULTI_ITEM = [
 @pytest.mark.parametrize("case", MULTI_ITEM, ids=lambda c: f"S{c[1]}x{c[2]}-H{c[3]}/{c[4]}-D{c[5]}-{c[6]}-{c[7]}")
 def test_several_qtiles_per_workgroup(case):
     B, Sq, Sk, H, H_kv, D, dtype, mask = case
-    ipw = _items_per_workgroup(B, H, Sq, mask)
+    ipw = _items_per_workgroup(B, H, Sq, mask, Sk, H_kv, D, 1 if dtype == "f8e4m3" else 2)
     log(f"[multi-item] {ipw} q-tiles per workgroup")
     assert ipw >= 2, "the case no longer covers several q-tiles per workgroup"
     _dense_case(f"multi-item {case}", make_dense(2900 + Sq + Sk, B, Sq, Sk, H, H_kv, D, dtype, mask=mask))
@@ -151,14 +163,14 @@ def test_several_qtiles_per_workgroup(case):
 @pytest.mark.parametrize("D", [32, 128])
 @pytest.mark.parametrize("mask", ["none", "causal_qend"])
 def test_several_qtiles_per_workgroup_fp8(mask, D):
-    assert _items_per_workgroup(1, 128, 1100, mask) >= 2
+    assert _items_per_workgroup(1, 128, 1100, mask, 300, 16, D, 1) >= 2
     inp = make_dense(2950 + D, 1, 1100, 300, 128, 16, D, "f8e4m3", mask=mask, o_scale=0.5)
     _dense_case(f"multi-item fp8 D{D} {mask}", inp)
 
 
 def test_several_qtiles_per_workgroup_repeatable():
     inp = make_dense(2960, 1, 1000, 700, 128, 32, 128, "bf16", mask="causal_qend")
-    assert _items_per_workgroup(1, 128, 1000, "causal_qend") >= 2
+    assert _items_per_workgroup(1, 128, 1000, "causal_qend", 700, 32, 128) >= 2
     runs = [run_dense(inp, want_lse=True) for _ in range(2)]
     assert np.array_equal(runs[1].o_bits, runs[0].o_bits) and np.array_equal(runs[1].lse, runs[0].lse)
 
