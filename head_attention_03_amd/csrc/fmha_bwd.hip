@@ -18,7 +18,7 @@
 //   and dO rows held as MFMA B operands in registers.  It first forms the rows' statistics,
 //   delta_i and LSE_i * log2(e) (+inf for a row with no key), from its dO fragment and the same
 //   fragment of O (the walk-through's row sum of O * dO, so it needs no kernel of its own), and
-//   stores them in a workspace of 64-row blocks [lse2[64], delta[64]] for the dK/dV kernel; the
+//   stores them in a workspace of 64-row blocks [lse2[64], -delta[64]] for the dK/dV kernel; the
 //   rows past a sequence's end in its last block get +inf and 0, so that kernel reads whole
 //   blocks and padding rows yield P = 0.  64-key K/V tiles stream through a 3-stage
 //   LDS ring (LDS-direct loads, one barrier per tile).  S^T = K Q^T and dP^T = V dO^T run on
@@ -27,12 +27,14 @@
 //   ds_read_b64_tr_b16 (the key order of the accumulator rows).  dQ is owned by one wave, so it
 //   is scaled and converted in registers and stored once: the fp32 conversion step of the
 //   walk-through folds into the epilogue.
-// * dkdv_kernel: a workgroup owns 128 keys of one (sequence, K/V head), 32 per wave, with K and
-//   V held as B operands in registers; 64-row Q/dO tiles (and their row statistics) stream
-//   through the ring for every query head of the GQA group.  S = Q K^T and dP = dO V^T put the
-//   wave's keys in the accumulator columns, so P and dS are directly the B operands of
-//   dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read transposed from LDS.  dK and dV
-//   of a K/V head sum over its group's query heads inside one workgroup.
+// * dkdv_kernel: a workgroup owns 128 keys of one (sequence, K/V head) in four 32-key blocks,
+//   each served by two waves on one SIMD: a P-wave holding K and a dS-wave holding V as B
+//   operands in registers.  64-row Q/dO tiles (and their row statistics) stream through LDS
+//   for every query head of the GQA group.  S = Q K^T and dP = dO V^T put the wave's keys in
+//   the accumulator columns, so P and dS are directly the B operands of dV^T += dO^T P
+//   (P-wave) and dK^T += Q^T dS (dS-wave), with dO^T and Q^T read transposed from LDS; P
+//   passes from the P-wave to the dS-wave through LDS, one step behind.  dK and dV of a K/V
+//   head sum over its group's query heads inside one workgroup.
 // Masks, varlen and GQA follow fmha_fwd: buffer descriptors bounded to the sequence (rows past
 // either end read 0 and are not written), the causal offset Sk_b - Sq_b for causal-qend, and
 // tiles that no row of a wave sees skipped by that wave.
@@ -41,6 +43,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fmha.h"
 #include "fmha_device.h"
 
@@ -48,12 +52,13 @@ namespace fmha {
 namespace bwd {
 
 constexpr int kAuxRows = 64;                 // rows per block of the row-statistics workspace
-constexpr int kAuxBlock = 2 * kAuxRows * 4;  // bytes per block: lse2[64], then delta[64]
+constexpr int kAuxBlock = 2 * kAuxRows * 4;  // bytes per block: lse2[64], then -delta[64]
 constexpr int kStages = 3;                   // LDS ring depth of both main kernels
 
-constexpr int kKvWaves = 4;             // dK/dV kernel: waves per workgroup, 32 keys each
+constexpr int kKvBlocks = 4;            // dK/dV kernel: 32-key blocks per workgroup
+constexpr int kKvWaves = 2 * kKvBlocks; // a P-wave and a dS-wave per key block
 constexpr int kKvThreads = 64 * kKvWaves;
-constexpr int kKvN = 32 * kKvWaves;     // keys per workgroup
+constexpr int kKvN = 32 * kKvBlocks;    // keys per workgroup
 constexpr int kKvM = kAuxRows;          // query rows per streamed tile
 
 constexpr int kQWaves = 8;              // dQ kernel: waves per workgroup, 32 query rows each
@@ -64,6 +69,7 @@ constexpr int kQN = 64;                 // keys per streamed tile
 constexpr int kSchedMfma = 0x008;  // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedDsRead = 0x100;
 constexpr int kPrefetch = 6;       // LDS reads kept in flight ahead of the MFMAs
+constexpr int kChunksAhead = 1;    // dK/dV kernel: 16-row chunks of transposed reads in flight
 
 struct Params {
   const void* q;
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_kernel(const Params p) {
     if (h32 == 0 && (qi & ~(kAuxRows - 1)) < sq.Sq_b) {
       float* blk = p.aux + (size_t)(aux_seq_base(p, b, sq.q_row0) + h * p.aux_hstride + qi / kAuxRows) * (kAuxBlock / 4);
       blk[qi % kAuxRows] = lse2;
-      blk[kAuxRows + qi % kAuxRows] = delta;
+      blk[kAuxRows + qi % kAuxRows] = -delta;
     }
   }
 
@@ -386,6 +392,16 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_kernel(const Params p) {
 // ------------------------------------------------------------------------------------------
 // dK/dV kernel: grid = B * H_kv * n_tiles workgroups of kKvThreads
 // ------------------------------------------------------------------------------------------
+// Two waves share each SIMD and the same 32 keys.  The P-wave (waves 0-3) holds K and forms
+// S = Q K^T, P and dV^T += dO^T P; it leaves P, rounded to the 16-bit type as the dV product
+// consumes it, in LDS.  The dS-wave (waves 4-7) holds V and forms dP - delta = dO V^T - delta
+// (the MFMAs accumulate onto -delta, read from the statistics block straight into the
+// accumulators); one step later, after the barrier that publishes P, it forms
+// dS = P (dP - delta) and dK^T += Q^T dS.  Each
+// wave thus runs half of the four products of a tile (32 MFMAs per 64-row step), and the
+// vector work of one wave (the exponentials, or the dS products) issues while the other
+// wave's MFMAs run.  Q tiles stay in LDS one step longer than dO tiles for the dS-wave's
+// transposed reads: 4 Q slots, 3 dO slots, 2 P slots.
 template <int DT, int D>
 __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
   constexpr int E = 2;
@@ -394,22 +410,26 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
   constexpr int TILE = kKvM * RB;    // bytes per Q or dO tile
   constexpr int TBLK = TILE / 1024;
   constexpr int LPW = 2 * TBLK / kKvWaves;  // Q and dO loads per wave per step
-  constexpr int AUXW = 1024;                // a wave's copy of the step's statistics block
-  constexpr int STAGE = 2 * TILE + kKvWaves * AUXW;
-  constexpr int NLD = LPW + 1;              // loads per wave per step
+  constexpr int QSLOTS = 4, DOSLOTS = 3;
+  constexpr int AUX_AT = (QSLOTS + DOSLOTS) * TILE;  // 4 statistics blocks of 1 KiB
+  constexpr int P_AT = AUX_AT + 4 * 1024;            // 2 slots of P: 32 keys x 64 rows per key block
+  constexpr int PBLK = 32 * kKvM * E;
+  constexpr int PSLOT = kKvBlocks * PBLK;
   constexpr int KS = D / 16;
   constexpr int NDB = D / 32;
   static_assert(TILE % 1024 == 0 && (2 * TBLK) % kKvWaves == 0 && LPW >= 1, "whole loads per wave");
-  static_assert(NLD < 32, "vmcnt range");
+  static_assert(LPW + 1 < 32, "vmcnt range");
   typedef Elem<DT> T;
 
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[P_AT + 2 * PSLOT];
   const uint32_t ring = (uint32_t)(uintptr_t)(lds_void*)lds;
 
   const int lane = threadIdx.x & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int l32 = lane & 31;
   const int h32 = lane >> 5;
+  const bool ds_wave = wave_u >= kKvBlocks;  // wave-uniform role
+  const int kblk = wave_u & (kKvBlocks - 1);
 
   int bkv, grp;
   decode_unit(p, p.B * p.H_kv, &bkv, &grp);
@@ -419,8 +439,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
   const int kb0 = grp * kKvN;  // key tile 0 sees the most rows: heaviest first
   if (kb0 >= sq.Sk_b) return;
   const int off = p.qend ? sq.Sk_b - sq.Sq_b : 0;
-  const int kw0 = kb0 + 32 * wave_u;  // this wave's keys
-  const int key = kw0 + l32;          // this lane's key
+  const int kw0 = kb0 + 32 * kblk;  // this wave's keys
+  const int key = kw0 + l32;        // this lane's key
   // rows below kb0 - off see no key of the workgroup
   const int qt_first = p.causal ? max(0, kb0 - off) / kKvM : 0;
   const int n_qt = (sq.Sq_b + kKvM - 1) / kKvM;
@@ -436,23 +456,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
   const i32x4 rq = make_rsrc_words((const char*)p.q + q_base, q_bytes);
   const i32x4 rdo = make_rsrc_words((const char*)p.dout + q_base, q_bytes);
   const i32x4 raux = make_rsrc_words(p.aux, p.aux_bytes);
-  const auto rk = make_rsrc((const char*)p.k + k_base, k_bytes);
-  const auto rv = make_rsrc((const char*)p.v + k_base, k_bytes);
-  const auto rdk = make_rsrc((const char*)p.dk + k_base, k_bytes);
-  const auto rdv = make_rsrc((const char*)p.dv + k_base, k_bytes);
-
-  // the wave's K and V rows as B operands (key l32, dims 16 ks + 8 h32 ..); keys past the
-  // sequence read 0 (their columns are never stored)
-  i32x4 kf[KS], vf[KS];
-  const uint32_t frag = (uint32_t)key * kstride + 16 * h32;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = load_b128(rk, frag + 32 * ks);
-    vf[ks] = load_b128(rv, frag + 32 * ks);
-  }
 
   // tile loads: load g of a step (0 .. 2 TBLK - 1; Q first, then dO) is wave g % kKvWaves's;
-  // each wave also copies the step's statistics block into its own 1 KiB of the stage
+  // wave 0 also copies the step's statistics block (and the next one, unused) into LDS
   uint32_t ld_off[LPW], ld_dst[LPW];
   bool ld_do[LPW];
 #pragma unroll
@@ -463,25 +469,54 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
     const int j = pos / CPR;
     ld_off[i] = (uint32_t)j * qstride + (((pos % CPR) ^ swz<CPR>(j)) * 16);
     ld_do[i] = g >= TBLK;
-    ld_dst[i] = (uint32_t)((g >= TBLK ? TILE : 0) + 1024 * gi);
+    ld_dst[i] = (uint32_t)(1024 * gi);
   }
   const int aux_b = aux_seq_base(p, b, sq.q_row0);
-  const uint32_t aux_dst = (uint32_t)(2 * TILE + wave_u * AUXW);
+  auto q_slot = [&](int t) __attribute__((always_inline)) { return ring + (uint32_t)((t % QSLOTS) * TILE); };
+  auto do_slot = [&](int t) __attribute__((always_inline)) {
+    return ring + (uint32_t)((QSLOTS + t % DOSLOTS) * TILE);
+  };
+  auto aux_slot = [&](int t) __attribute__((always_inline)) { return ring + (uint32_t)(AUX_AT + (t % 4) * 1024); };
+  auto p_slot = [&](int t) __attribute__((always_inline)) {
+    return ring + (uint32_t)(P_AT + (t & 1) * PSLOT + kblk * PBLK);
+  };
   auto load_step = [&](int t) __attribute__((always_inline)) {
     const int hi = t / nq;
     const int qt = qt_first + t - hi * nq;
     const int hq = kvh * p.group + hi;
     const uint32_t base = (uint32_t)(qt * kKvM) * qstride + (uint32_t)hq * RB;
-    const uint32_t st = ring + (uint32_t)((t % kStages) * STAGE);
+    const uint32_t sq_ = q_slot(t), sd = do_slot(t);
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) lds_load16(ld_do[i] ? rdo : rq, base + ld_off[i], st + ld_dst[i]);
-    const uint32_t blk = (uint32_t)(aux_b + hq * p.aux_hstride + qt);
-    lds_load16(raux, blk * kAuxBlock + 16 * lane, st + aux_dst);
+    for (int i = 0; i < LPW; ++i) lds_load16(ld_do[i] ? rdo : rq, base + ld_off[i], (ld_do[i] ? sd : sq_) + ld_dst[i]);
+    if (wave_u == 0) {
+      const uint32_t blk = (uint32_t)(aux_b + hq * p.aux_hstride + qt);
+      lds_load16(raux, blk * kAuxBlock + 16 * lane, aux_slot(t));
+    }
+  };
+  // first row of step t's tile, and whether no row of it sees this wave's keys
+  auto step_q0 = [&](int t) __attribute__((always_inline)) { return (qt_first + t % nq) * kKvM; };
+  auto skipped = [&](int t) __attribute__((always_inline)) {
+    return p.causal && step_q0(t) + kKvM - 1 + off < kw0;
   };
   if (n_steps > 0) load_step(0);
   if (n_steps > 1) load_step(1);
 
-  // per-lane LDS offsets: row-wise A reads of Q and dO, transposed reads of both
+  // the wave's K (P-wave) or V (dS-wave) rows as B operands (key l32, dims 16 ks + 8 h32 ..);
+  // keys past the sequence read 0 (their columns are never stored).  They are waited for
+  // here, together with the first two tiles: the compiler does not count the tile loads, so a
+  // wait it placed inside the loop would drain the tiles in flight at every step.
+  i32x4 kvf[KS];
+  {
+    const auto rkv = make_rsrc((const char*)(ds_wave ? p.v : p.k) + k_base, k_bytes);
+    const uint32_t frag = (uint32_t)key * kstride + 16 * h32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kvf[ks] = load_b128(rkv, frag + 32 * ks);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(kvf[ks]));
+  }
+
+  // per-lane LDS offsets: row-wise A reads of Q and dO, transposed reads of both, and this
+  // lane's 32 bytes of a 32-row half of P (two 1 KiB planes of 16 bytes per lane)
   const uint32_t r_lane = l32 * RB + ((h32 ^ swz<CPR>(l32)) * 16);
   const int g16 = (lane >> 4) & 1;
   const int s16 = lane & 15;
@@ -489,91 +524,157 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
   const int t_part = 2 * g16 + ((s16 & 3) >> 1);
   const uint32_t t_lane0 = t_row0 * RB + ((t_part ^ swz<CPR>(t_row0)) * 16) + 8 * (s16 & 1);
   const uint32_t t_lane1 = (t_row0 + 8) * RB + ((t_part ^ swz<CPR>(t_row0 + 8)) * 16) + 8 * (s16 & 1);
+  const uint32_t p_lane = 16 * lane;
 
-  f32x16 acc_k[NDB], acc_v[NDB];
+  f32x16 acc[NDB];  // dV^T (P-wave) or dK^T (dS-wave): 32 dims x the wave's 32 keys per block
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    acc_k[db] = f32x16{};
-    acc_v[db] = f32x16{};
-  }
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
   const float sl2 = p.scale_log2;
 
-  for (int t = 0; t < n_steps; ++t) {
-    if (t + 1 < n_steps)
-      wait_vmcnt<NLD>();
-    else
-      wait_vmcnt<0>();
-    phase_barrier();  // step t is in LDS for every wave; stage (t + 2) % 3 is free
-    if (t + 2 < n_steps) load_step(t + 2);
-    const int hi = t / nq;
-    const int q0 = (qt_first + t - hi * nq) * kKvM;
-    if (p.causal && q0 + kKvM - 1 + off < kw0) continue;  // no row of the tile sees the wave's keys
-    const uint32_t st = ring + (uint32_t)((t % kStages) * STAGE);
+  // Element r of a half qb's 32x32 block of S, dP, P or dS is row q0 + 32 qb + 4 h32 +
+  // 8 (r / 4) + r % 4, key `key`.  MFMAs over one 16-row chunk of a half take P or dS packed in
+  // that order, against the matching transposed read of dO or Q.  The reads of chunk
+  // c + kChunksAhead are issued before the MFMAs of chunk c (pinned by scheduling barriers:
+  // left alone, the compiler reuses one set of registers and waits for each read right before
+  // its MFMA).
+  auto chunk_mma = [&](uint32_t tile, const uint32_t (&pk)[16]) __attribute__((always_inline)) {
+    constexpr int CA = kChunksAhead;
+    i32x4 a[CA + 1][NDB];
+#pragma unroll
+    for (int c = 0; c < CA; ++c)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) a[c][db] = read_tr(tile + t_lane0, tile + t_lane1, db, (uint32_t)(16 * c * RB));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (c + CA < 4) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          a[(c + CA) % (CA + 1)][db] = read_tr(tile + t_lane0, tile + t_lane1, db, (uint32_t)(16 * (c + CA) * RB));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const i32x4 bp = {(int)pk[4 * c], (int)pk[4 * c + 1], (int)pk[4 * c + 2], (int)pk[4 * c + 3]};
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] = T::mma(a[c % (CA + 1)][db], bp, acc[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
-    // S = Q K^T and dP = dO V^T: element r of block qb is row q0 + 32 qb + 4 h32 + 8 (r / 4) +
-    // r % 4, key `key`
-    // Per 32-row half qb of the tile: S and dP, then P and dS with the rows' statistics
-    // (padding rows: lse2 = +inf, delta = 0, so P = 0), then dV^T += dO^T P and dK^T += Q^T dS
-    // over the half's 32 rows.  Element r of a half's blocks is row q0 + 32 qb + 4 h32 +
-    // 8 (r / 4) + r % 4, key `key`.
-    const bool special = p.causal && q0 < kw0 + 31 - off;
-    const int lim = key - off - q0 - 4 * h32;  // keep element r iff 32 qb + 8 (r / 4) + r % 4 >= lim
-    const uint32_t sa = st + aux_dst;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16 c2[2] = {};  // S, dP
+  if (!ds_wave) {
+    // ---- P-wave: S, P (to LDS), dV ------------------------------------------------------
+    for (int t = 0; t < n_steps; ++t) {
+      if (t + 1 < n_steps) {
+        if (wave_u == 0) wait_vmcnt<LPW + 1>(); else wait_vmcnt<LPW>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      phase_barrier();  // step t is in LDS; the slots of step t + 2 are free
+      if (t + 2 < n_steps) load_step(t + 2);
+      if (skipped(t)) continue;
+      const int q0 = step_q0(t);
+      const uint32_t sq_ = q_slot(t);
+      f32x16 c2[2] = {};  // S of the two halves
       {
-        const uint32_t r0 = st + r_lane + (uint32_t)(32 * qb * RB);
-        const uint32_t base[2] = {r0, r0 + TILE};
-        row_chains<DT, KS, 2>(c2, base, kf, vf);
+        const uint32_t base[2] = {sq_ + r_lane, sq_ + r_lane + (uint32_t)(32 * RB)};
+        row_chains<DT, KS, 2>(c2, base, kvf, kvf);
       }
-      uint32_t pp[8], pd[8];
+      // P = exp2(scale log2(e) s - lse2), 0 where masked (padding rows: lse2 = +inf)
+      const bool special = p.causal && q0 < kw0 + 31 - off;
+      const int lim = key - off - q0 - 4 * h32;  // keep element r iff 32 qb + 8 (r / 4) + r % 4 >= lim
+      const uint32_t sa = aux_slot(t);
+      const uint32_t ps = p_slot(t);
+      uint32_t pp[16];
+      auto softmax = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t ra = sa + 4 * (32 * qb + 8 * g + 4 * h32);
-        const i32x4 l4 = *(const lds_i32x4*)(uintptr_t)ra;
-        const i32x4 d4 = *(const lds_i32x4*)(uintptr_t)(ra + 4 * kAuxRows);
-        float pr[4], ds[4];
+        for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int e = 4 * g + u;
-          pr[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(c2[0][e], sl2, -__builtin_bit_cast(float, (int)l4[u])));
-          if (special) pr[u] = 32 * qb + 8 * g + u >= lim ? pr[u] : 0.0f;
-          ds[u] = pr[u] * (c2[1][e] - __builtin_bit_cast(float, (int)d4[u]));
+          for (int g = 0; g < 4; ++g) {
+            const i32x4 l4 = *(const lds_i32x4*)(uintptr_t)(sa + 4 * (32 * qb + 8 * g + 4 * h32));
+            float pr[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              pr[u] = __builtin_amdgcn_exp2f(
+                  __builtin_fmaf(c2[qb][4 * g + u], sl2, -__builtin_bit_cast(float, (int)l4[u])));
+              if constexpr (decltype(masked)::value) pr[u] = 32 * qb + 8 * g + u >= lim ? pr[u] : 0.0f;
+            }
+            pp[8 * qb + 2 * g] = T::pack(pr[0], pr[1]);
+            pp[8 * qb + 2 * g + 1] = T::pack(pr[2], pr[3]);
+          }
         }
-        pp[2 * g] = T::pack(pr[0], pr[1]);
-        pp[2 * g + 1] = T::pack(pr[2], pr[3]);
-        pd[2 * g] = T::pack(ds[0], ds[1]);
-        pd[2 * g + 1] = T::pack(ds[2], ds[3]);
-      }
+      };
+      if (special)
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {  // 16-row chunk 2 qb + ch
-        const i32x4 bp = {(int)pp[4 * ch], (int)pp[4 * ch + 1], (int)pp[4 * ch + 2], (int)pp[4 * ch + 3]};
-        const i32x4 bd = {(int)pd[4 * ch], (int)pd[4 * ch + 1], (int)pd[4 * ch + 2], (int)pd[4 * ch + 3]};
-        const uint32_t rows = (uint32_t)(16 * (2 * qb + ch) * RB);
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          acc_v[db] = T::mma(read_tr(st + TILE + t_lane0, st + TILE + t_lane1, db, rows), bp, acc_v[db]);
-          acc_k[db] = T::mma(read_tr(st + t_lane0, st + t_lane1, db, rows), bd, acc_k[db]);
+        for (int pl = 0; pl < 2; ++pl) {
+          const i32x4 w = {(int)pp[8 * qb + 4 * pl], (int)pp[8 * qb + 4 * pl + 1], (int)pp[8 * qb + 4 * pl + 2],
+                           (int)pp[8 * qb + 4 * pl + 3]};
+          *(lds_i32x4*)(uintptr_t)(ps + (uint32_t)(2048 * qb + 1024 * pl) + p_lane) = w;
+        }
+      chunk_mma(do_slot(t), pp);  // dV^T += dO^T P
+    }
+    if (n_steps > 0) phase_barrier();  // the dS-wave's last step reads the last P
+  } else {
+    // ---- dS-wave: dP, then one step later dS and dK ---------------------------------------
+    f32x16 dp[2] = {};  // dP - delta of the previous step's tile
+    auto ds_step = [&](int t) __attribute__((always_inline)) {  // dS and dK of step t's tile
+      const uint32_t ps = p_slot(t);
+      uint32_t pd[16];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        uint32_t pr[8];
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) {
+          const i32x4 w = *(const lds_i32x4*)(uintptr_t)(ps + (uint32_t)(2048 * qb + 1024 * pl) + p_lane);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pr[4 * pl + i] = (uint32_t)w[i];
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t a = pr[2 * g], c = pr[2 * g + 1];
+          pd[8 * qb + 2 * g] = T::pack(T::lo(a) * dp[qb][4 * g], T::hi(a) * dp[qb][4 * g + 1]);
+          pd[8 * qb + 2 * g + 1] = T::pack(T::lo(c) * dp[qb][4 * g + 2], T::hi(c) * dp[qb][4 * g + 3]);
         }
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
+      chunk_mma(q_slot(t), pd);  // dK^T += Q^T dS
+    };
+    for (int t = 0; t < n_steps; ++t) {
+      if (t + 1 < n_steps)
+        wait_vmcnt<LPW>();
+      else
+        wait_vmcnt<0>();
+      phase_barrier();  // step t is in LDS, and P of step t - 1
+      if (t + 2 < n_steps) load_step(t + 2);
+      if (t > 0 && !skipped(t - 1)) ds_step(t - 1);
+      if (skipped(t)) continue;
+      const uint32_t sd = do_slot(t);
+      const uint32_t sa = aux_slot(t) + 4 * kAuxRows;  // -delta of the tile's rows
 #pragma unroll
-      for (int i = 0; i < 4 * NDB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      }
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const i32x4 d4 = *(const lds_i32x4*)(uintptr_t)(sa + 4 * (32 * qb + 8 * g + 4 * h32));
+#pragma unroll
+          for (int u = 0; u < 4; ++u) dp[qb][4 * g + u] = __builtin_bit_cast(float, (int)d4[u]);
+        }
+      const uint32_t base[2] = {sd + r_lane, sd + r_lane + (uint32_t)(32 * RB)};
+      row_chains<DT, KS, 2>(dp, base, kvf, kvf);
+    }
+    if (n_steps > 0) {
+      phase_barrier();
+      if (!skipped(n_steps - 1)) ds_step(n_steps - 1);
     }
   }
 
-  // dK = scale * acc_k, dV = acc_v: lane holds key `key` (keys past the sequence are dropped
-  // by the descriptor)
+  // dK = scale * acc (dS-wave), dV = acc (P-wave): lane holds key `key` (keys past the
+  // sequence are dropped by the descriptor)
+  const auto rout = make_rsrc((char*)(ds_wave ? p.dk : p.dv) + k_base, k_bytes);
+  const float f = ds_wave ? p.scale : 1.0f;
   const uint32_t at = (uint32_t)key * kstride;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    store_block<DT>(acc_k[db], p.scale, rdk, at + 64 * db, h32);
-    store_block<DT>(acc_v[db], 1.0f, rdv, at + 64 * db, h32);
-  }
+  for (int db = 0; db < NDB; ++db) store_block<DT>(acc[db], f, rout, at + 64 * db, h32);
 }
 
 template <int DT, int D>
