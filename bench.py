@@ -79,8 +79,9 @@ def workload_slug(c: dict) -> str:
 
 
 def measured_traffic(c: dict):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload,
-    if it was taken on the current kernel source (else None)."""
+    """Bytes per launch that left the L2 (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated; Infinity
+    Cache hits included, so an upper bound of the HBM traffic) from the committed counter summary of
+    this workload, if it was taken on the current kernel source (else None)."""
     try:
         prefix = "fmha_" if c.get("entry") == "bwd" else "fmha_fwd_"
         rec = json.load(open(os.path.join(PROFILES, f"{prefix}{workload_slug(c)}_traffic.json")))
@@ -88,7 +89,7 @@ def measured_traffic(c: dict):
         return None
     if rec.get("kernel_source_sha256_16") != kernel_source_hash(c.get("entry", "fwd")):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("l2_miss_bytes_per_launch")
 
 
 def algorithmic_bytes(inp, want_lse: bool) -> float:
