@@ -59,4 +59,4 @@ from .backward import (  # noqa: F401
     attention_head_backward,
     sum_o_do,
 )
-from .paged import attention_paged, gather_pages  # noqa: F401
+from .paged import append_paged, attention_paged, gather_pages  # noqa: F401

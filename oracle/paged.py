@@ -18,6 +18,14 @@ layout, so this module takes the plainest one, a block table:
   any sequence.
 
 The attention itself is the forward definition of oracle.attention on the gathered keys.
+
+``append_paged`` is the step before a decode call that the walk-through's generation section
+describes as the kernel's default mode (its "--cache-only" option turns it off): the new tokens'
+K and V are inserted into the cache.  The pages fix no positions; the reading here is that
+``seqlens_k`` already counts the new tokens, so that the decode call's causal-qend offset
+(seqlens_k[b] - Sq) lines the new queries up with their own keys: new row i of sequence b is key
+seqlens_k[b] - S_new + i.  Rows that would land before key 0, past the block table, or in a page
+number outside [0, num_pages) are dropped, like the table entries the attention reads as zeros.
 """
 from __future__ import annotations
 
@@ -54,3 +62,24 @@ def attention_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, blo
         for h in range(H):
             o[b, :, h], lse[b, h] = attention_head(q[b, :, h], kb[:, h // group], vb[:, h // group], scale, mask)
     return o_scale * o, lse
+
+
+def append_paged(k_cache: np.ndarray, v_cache: np.ndarray, block_table: np.ndarray, seqlens_k: Sequence[int],
+                 k_new: np.ndarray, v_new: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Caches [num_pages, page_size, H_kv, D] after inserting k_new, v_new [B, S_new, H_kv, D] (any
+    element type: values are copied as they are).  Returns new arrays; the inputs are unchanged."""
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    num_pages, page_size = kc.shape[0], kc.shape[1]
+    B, S_new = k_new.shape[0], k_new.shape[1]
+    max_pages = block_table.shape[1]
+    for b in range(B):
+        for i in range(S_new):
+            pos = int(seqlens_k[b]) - S_new + i  # key index of new row i
+            if pos < 0 or pos >= max_pages * page_size:
+                continue
+            page = int(block_table[b, pos // page_size])
+            if not 0 <= page < num_pages:
+                continue
+            kc[page, pos % page_size] = k_new[b, i]
+            vc[page, pos % page_size] = v_new[b, i]
+    return kc, vc

@@ -150,3 +150,85 @@ def test_planted_paged_mistake_is_caught(name):
         except (AssertionError, ValueError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"mutation {name!r} passed every pin"
+
+
+# ----------------------------------------------------------------------------------------------
+# append_paged: inserting the new tokens' K/V before a decode step
+# ----------------------------------------------------------------------------------------------
+def test_append_hand_example():
+    # 3 pages of 2 rows, one head, one dim; sequence 0 owns pages [2, 0] and 3 keys, the last two
+    # of which are new: key 1 -> page 2 row 1, key 2 -> page 0 row 0 (worked out by hand)
+    kc = np.arange(6, dtype=np.int16).reshape(3, 2, 1, 1)
+    vc = (100 + np.arange(6, dtype=np.int16)).reshape(3, 2, 1, 1)
+    bt = np.array([[2, 0]], dtype=np.int32)
+    k_new = np.array([[[[10]], [[11]]]], dtype=np.int16)
+    v_new = np.array([[[[20]], [[21]]]], dtype=np.int16)
+    k2, v2 = oracle_paged.append_paged(kc, vc, bt, [3], k_new, v_new)
+    assert k2[:, :, 0, 0].tolist() == [[11, 1], [2, 3], [4, 10]]
+    assert v2[:, :, 0, 0].tolist() == [[21, 101], [102, 103], [104, 20]]
+    assert kc[:, :, 0, 0].tolist() == [[0, 1], [2, 3], [4, 5]]  # inputs unchanged
+
+
+@pytest.mark.parametrize("page_size", [2, 4, 8])
+def test_append_then_gather_is_old_keys_then_new_rows(page_size):
+    rng = np.random.default_rng(31 + page_size)
+    B, S_new, H_kv, D = 3, 3, 2, 4
+    seqlens = [S_new, 7, 13]  # the first sequence is all new
+    n_pages = [-(-s // page_size) for s in seqlens]
+    num_pages = sum(n_pages) + 2
+    perm = rng.permutation(num_pages)
+    bt = np.full((B, max(n_pages)), -1, dtype=np.int32)
+    n = 0
+    for b in range(B):
+        for i in range(n_pages[b]):
+            bt[b, i] = perm[n]
+            n += 1
+    kc, vc = _cache(rng, num_pages, page_size, H_kv, D)
+    k_new, v_new = rng.standard_normal((B, S_new, H_kv, D)), rng.standard_normal((B, S_new, H_kv, D))
+    k2, v2 = oracle_paged.append_paged(kc, vc, bt, seqlens, k_new, v_new)
+    for b in range(B):
+        L = seqlens[b]
+        for new, old, cache in ((k_new, kc, k2), (v_new, vc, v2)):
+            got = oracle_paged.gather_pages(cache, bt[b], L, page_size)
+            before = oracle_paged.gather_pages(old, bt[b], L, page_size)
+            np.testing.assert_array_equal(got[:L - S_new], before[:L - S_new])
+            np.testing.assert_array_equal(got[L - S_new:], new[b])
+    # pages no sequence owns, and rows past each sequence's end, are untouched
+    owned = np.zeros(kc.shape[:2], dtype=bool)
+    for b in range(B):
+        for j in range(seqlens[b]):
+            owned[bt[b, j // page_size], j % page_size] = True
+    np.testing.assert_array_equal(k2[~owned], kc[~owned])
+    np.testing.assert_array_equal(v2[~owned], vc[~owned])
+
+
+def test_append_drops_rows_outside_the_table():
+    rng = np.random.default_rng(5)
+    kc, vc = _cache(rng, 4, 2, 1, 2)
+    k_new, v_new = rng.standard_normal((2, 3, 1, 2)), rng.standard_normal((2, 3, 1, 2))
+    # sequence 0: only one key, so new rows 0 and 1 would lie before key 0; sequence 1: its
+    # second page entry is -1 and the third is past num_pages
+    bt = np.array([[1, -1, 9], [3, -1, 9]], dtype=np.int32)
+    k2, v2 = oracle_paged.append_paged(kc, vc, bt, [1, 5], k_new, v_new)
+    exp_k = kc.copy()
+    exp_k[1, 0] = k_new[0, 2]  # sequence 0, key 0
+    # sequence 1: keys 2, 3 -> page -1 (dropped), key 4 -> page 9 (dropped)
+    np.testing.assert_array_equal(k2, exp_k)
+    exp_v = vc.copy()
+    exp_v[1, 0] = v_new[0, 2]
+    np.testing.assert_array_equal(v2, exp_v)
+
+
+def test_append_planted_off_by_one_is_caught():
+    # a version that writes new row i at seqlens_k - S_new + i + 1 breaks the gather invariant
+    rng = np.random.default_rng(8)
+    kc, vc = _cache(rng, 3, 4, 1, 2)
+    bt = np.array([[0, 2]], dtype=np.int32)
+    k_new, v_new = rng.standard_normal((1, 2, 1, 2)), rng.standard_normal((1, 2, 1, 2))
+    wrong = kc.copy()
+    for i in range(2):
+        pos = 6 - 2 + i + 1
+        wrong[bt[0, pos // 4], pos % 4] = k_new[0, i]
+    right, _ = oracle_paged.append_paged(kc, vc, bt, [6], k_new, v_new)
+    assert not np.array_equal(oracle_paged.gather_pages(wrong, bt[0], 6, 4)[4:], k_new[0])
+    np.testing.assert_array_equal(oracle_paged.gather_pages(right, bt[0], 6, 4)[4:], k_new[0])
