@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     fmha_fwd_splitkv_noalloc,
     fmha_fwd_splitkv_paged,
     fmha_paged_kv,
+    fmha_paged_kv_append,
     fmha_fwd_splitkv_workspace_size,
     fmha_status_string,
     fmha_varlen,

@@ -20,7 +20,7 @@ STATUS = {0: "FMHA_OK", 1: "FMHA_ERR_NULL_POINTER", 2: "FMHA_ERR_INVALID_SHAPE",
           4: "FMHA_ERR_MISALIGNED", 5: "FMHA_ERR_INVALID_ARGUMENT", 6: "FMHA_ERR_HIP", 7: "FMHA_ERR_SCRATCH_TOO_SMALL"}
 # every symbol include/fmha.h declares
 EXPORTS = ("fmha_fwd", "fmha_fwd_splitkv", "fmha_fwd_splitkv_noalloc", "fmha_fwd_splitkv_workspace_size",
-           "fmha_fwd_splitkv_paged", "fmha_bwd", "fmha_bwd_workspace_size", "fmha_status_string", "fmha_version")
+           "fmha_fwd_splitkv_paged", "fmha_paged_kv_append", "fmha_bwd", "fmha_bwd_workspace_size", "fmha_status_string", "fmha_version")
 
 
 class FmhaError(RuntimeError):
@@ -66,6 +66,9 @@ def load() -> ctypes.CDLL:
     lib.fmha_fwd_splitkv_paged.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int32] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.POINTER(fmha_paged_kv), ctypes.c_void_p,
         ctypes.c_size_t, ctypes.c_void_p]
+    lib.fmha_paged_kv_append.restype = ctypes.c_int
+    lib.fmha_paged_kv_append.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int32] * 4 + [
+        ctypes.POINTER(fmha_paged_kv), ctypes.c_void_p]
     lib.fmha_bwd.restype = ctypes.c_int
     lib.fmha_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int32] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.POINTER(fmha_varlen), ctypes.c_void_p, ctypes.c_size_t,
@@ -161,6 +164,15 @@ def fmha_fwd_splitkv_paged(q, k_cache, v_cache, o, lse, B: int, Sq: int, Sk: int
     return int(lib.fmha_fwd_splitkv_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), int(B), int(Sq),
                                           int(Sk), int(H), int(H_kv), int(D), float(scale), mask, dtype,
                                           float(o_scale), pk, _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def fmha_paged_kv_append(k_cache, v_cache, k_new, v_new, B: int, S_new: int, H_kv: int, D: int,
+                         paged: Optional[fmha_paged_kv] = None, stream=None) -> int:
+    """Call the paged-cache append C entry point; returns the fmha_status code."""
+    lib = load()
+    pk = ctypes.byref(paged) if paged is not None else None
+    return int(lib.fmha_paged_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), int(B), int(S_new),
+                                        int(H_kv), int(D), pk, _stream(stream)))
 
 
 def fmha_bwd(q, k, v, o, dout, lse, dq, dk, dv, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int, scale: float,

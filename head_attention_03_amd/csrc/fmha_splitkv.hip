@@ -552,6 +552,43 @@ hipError_t launch(const Params& p, const MergeParams& mp, int grid, hipStream_t 
   return hipGetLastError();
 }
 
+
+// ------------------------------------------------------------------------------------------
+// Cache append: the new tokens' K and V rows into their pages (the generation kernel's default
+// mode in the CUTLASS walk-through, as opposed to its --cache-only reads).  One workgroup per
+// new row (sequence b, token i), 16 bytes per thread and step; new row i of sequence b is key
+// seqlens_k[b] - S_new + i.  A row whose key lies before 0 or past the block table, or whose
+// page number is outside [0, num_pages), is not written, so no table entry can send a store
+// outside the cache.
+// ------------------------------------------------------------------------------------------
+struct AppendParams {
+  char* k_cache;
+  char* v_cache;
+  const char* k_new;  // [B, S_new, H_kv, D]
+  const char* v_new;
+  const int32_t* block_table;
+  const int32_t* seqlens_k;
+  int32_t S_new, max_pages, page_size, num_pages;
+  uint32_t row_bytes;  // H_kv * D * element size, a multiple of 16
+};
+
+constexpr int kAppendThreads = 256;
+
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(const AppendParams p) {
+  const int b = blockIdx.x / p.S_new;
+  const int i = blockIdx.x - b * p.S_new;
+  const int64_t pos = (int64_t)p.seqlens_k[b] - p.S_new + i;
+  if (pos < 0 || pos >= (int64_t)p.max_pages * p.page_size) return;
+  const int page = p.block_table[(size_t)b * p.max_pages + (size_t)(pos / p.page_size)];
+  if (page < 0 || page >= p.num_pages) return;
+  const size_t dst = ((size_t)page * p.page_size + (size_t)(pos % p.page_size)) * p.row_bytes;
+  const size_t src = (size_t)blockIdx.x * p.row_bytes;
+  for (uint32_t off = 16u * threadIdx.x; off < p.row_bytes; off += 16u * kAppendThreads) {
+    *(i32x4*)(p.k_cache + dst + off) = *(const i32x4*)(p.k_new + src + off);
+    *(i32x4*)(p.v_cache + dst + off) = *(const i32x4*)(p.v_new + src + off);
+  }
+}
+
 }  // namespace skv
 }  // namespace fmha
 
@@ -833,6 +870,39 @@ fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const voi
     if (D == 128) err = fmha::skv::launch<fmha::kF16, 128, false, true>(p, mp, (int)grid, stream);
   }
   return err == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
+}
+
+fmha_status fmha_paged_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new, int32_t B,
+                                 int32_t S_new, int32_t H_kv, int32_t D, const fmha_paged_kv* paged,
+                                 hipStream_t stream) {
+  if (!paged) return FMHA_ERR_NULL_POINTER;
+  if (B < 0 || S_new < 0 || H_kv < 1) return FMHA_ERR_INVALID_SHAPE;
+  if (D != 32 && D != 64 && D != 128) return FMHA_ERR_INVALID_SHAPE;
+  if ((int)paged->kv_dtype < 0 || (int)paged->kv_dtype > 2) return FMHA_ERR_UNSUPPORTED;
+  const int32_t ps = paged->page_size;
+  if (ps < 32 || ps > 65536 || (ps & (ps - 1)) != 0 || paged->max_pages_per_seq < 1 || paged->num_pages < 1)
+    return FMHA_ERR_INVALID_SHAPE;
+  if (B == 0 || S_new == 0) return FMHA_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !paged->block_table || !paged->seqlens_k)
+    return FMHA_ERR_NULL_POINTER;
+  if (((uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)k_new | (uintptr_t)v_new) & 15) return FMHA_ERR_MISALIGNED;
+  const int64_t row_bytes = (int64_t)H_kv * D * (paged->kv_dtype == FMHA_DTYPE_F8E4M3 ? 1 : 2);
+  if ((int64_t)B * S_new >= ((int64_t)1 << 31) || row_bytes >= ((int64_t)1 << 31)) return FMHA_ERR_UNSUPPORTED;
+  fmha::skv::AppendParams p;
+  p.k_cache = (char*)k_cache;
+  p.v_cache = (char*)v_cache;
+  p.k_new = (const char*)k_new;
+  p.v_new = (const char*)v_new;
+  p.block_table = paged->block_table;
+  p.seqlens_k = paged->seqlens_k;
+  p.S_new = S_new;
+  p.max_pages = paged->max_pages_per_seq;
+  p.page_size = ps;
+  p.num_pages = paged->num_pages;
+  p.row_bytes = (uint32_t)row_bytes;
+  hipLaunchKernelGGL(fmha::skv::append_kernel, dim3((unsigned)((int64_t)B * S_new)), dim3(fmha::skv::kAppendThreads), 0,
+                     stream, p);
+  return hipGetLastError() == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
 }
 
 }  // extern "C"

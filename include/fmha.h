@@ -284,6 +284,34 @@ fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const voi
                                    fmha_mask mask, fmha_dtype dtype, float o_scale, const fmha_paged_kv* paged,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * fmha_paged_kv_append -- insert the new tokens' K and V into a paged cache, the step before a
+ * decode call over it: the CUTLASS generation kernel's default mode, which inserts the new
+ * tokens' K/V, as opposed to its --cache-only mode, which only reads the cache (trdm.cn
+ * walk-through "CUTLASS Blackwell FMHA 示例完全解析", section on the generation kernel and its
+ * options).
+ *   k_cache, v_cache  the cache of paged (see fmha_paged_kv), written in place
+ *   k_new, v_new      device [B, S_new, H_kv, D] dense, 16-byte aligned, of the cache's element
+ *                     type paged->kv_dtype (an e4m3 cache takes e4m3 rows, quantised by the caller
+ *                     with the cache's scales); bytes are copied unchanged
+ *   paged->seqlens_k  keys of each sequence counting the new tokens: new row i of sequence b
+ *                     becomes key seqlens_k[b] - S_new + i, so that a following
+ *                     fmha_fwd_splitkv_paged call with Sq = S_new and causal-qend aligns each new
+ *                     query with its own key
+ * Rows whose key would lie before key 0 or past max_pages_per_seq * page_size, or whose table
+ * entry is outside [0, num_pages), are not written.  Two new rows that the table maps to the same
+ * cache row race (either may win).  Asynchronous on stream; nothing is allocated.
+ * Errors: paged NULL, or (B * S_new > 0) k_cache, v_cache, k_new, v_new, block_table or seqlens_k
+ * NULL -> FMHA_ERR_NULL_POINTER; B or S_new negative, H_kv < 1, D not 32, 64 or 128, page_size not
+ * a power of two in [32, 65536], max_pages_per_seq < 1 or num_pages < 1 -> FMHA_ERR_INVALID_SHAPE;
+ * kv_dtype not a fmha_dtype, B * S_new or H_kv * D * element size at or past 2^31 ->
+ * FMHA_ERR_UNSUPPORTED; a pointer not 16-byte aligned -> FMHA_ERR_MISALIGNED.  B or S_new 0: FMHA_OK,
+ * nothing launched.
+ */
+fmha_status fmha_paged_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new, int32_t B,
+                                 int32_t S_new, int32_t H_kv, int32_t D, const fmha_paged_kv* paged,
+                                 hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fmha_status_string(fmha_status status);
 

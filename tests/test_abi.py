@@ -242,3 +242,29 @@ def call_paged(**kw):
 ])
 def test_paged_rejects_bad_arguments(kw, status):
     assert call_paged(**kw) == status
+
+
+# ----------------------------------------------------------------------------------------------
+# fmha_paged_kv_append: host validation (every case returns before any launch)
+# ----------------------------------------------------------------------------------------------
+def call_append(**kw):
+    pk = kw.pop("paged", fmha.make_paged_kv(P, P, 4, 128, 8, "bf16"))
+    a = dict(k_cache=P, v_cache=P, k_new=P, v_new=P, B=2, S_new=1, H_kv=2, D=128, paged=pk, stream=None)
+    a.update(kw)
+    return fmha.fmha_paged_kv_append(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(paged=None), 1), (dict(k_cache=None), 1), (dict(v_cache=None), 1), (dict(k_new=None), 1),
+    (dict(v_new=None), 1),
+    (dict(paged=fmha.make_paged_kv(None, P, 4, 128, 8, "bf16")), 1), (dict(paged=fmha.make_paged_kv(P, None, 4, 128, 8, "bf16")), 1),
+    (dict(B=-1), 2), (dict(S_new=-1), 2), (dict(H_kv=0), 2), (dict(D=48), 2),
+    (dict(paged=fmha.make_paged_kv(P, P, 4, 96, 8, "bf16")), 2), (dict(paged=fmha.make_paged_kv(P, P, 4, 16, 8, "bf16")), 2),
+    (dict(paged=fmha.make_paged_kv(P, P, 0, 128, 8, "bf16")), 2), (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 0, "bf16")), 2),
+    (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 8, 7)), 3),
+    (dict(B=1 << 16, S_new=1 << 15), 3), (dict(H_kv=1 << 23), 3),
+    (dict(k_cache=P + 8), 4), (dict(v_new=P + 4), 4),
+    (dict(B=0), 0), (dict(S_new=0), 0), (dict(B=0, k_cache=None, k_new=None), 0),
+])
+def test_append_rejects_bad_arguments(kw, status):
+    assert call_append(**kw) == status

@@ -156,3 +156,70 @@ def test_paged_decode_e4m3_cache(case):
     assert res.status == 0
     o, lse = oracle_paged(inp)
     compare(f"paged e4m3 cache {case}", res.o_bits, dtype, o, res.lse, lse)
+
+
+# ----------------------------------------------------------------------------------------------
+# fmha_paged_kv_append: the new tokens' K/V into the cache (bit for bit against the oracle's
+# append), then the decode step over it against the attention oracle
+# ----------------------------------------------------------------------------------------------
+APPEND = [
+    # (B, S_new, seqlens_k counting the new tokens, H, H_kv, D, dtype, kv_dtype, page_size)
+    (4, 1, [4097, 1, 300, 129], 32, 8, 128, "bf16", "bf16", 128),   # one token; page edges; a 1-key cache
+    (3, 4, [1000, 2, 2500], 16, 2, 64, "f16", "f16", 32),            # 4 tokens across a page edge; 2 keys < 4 rows
+    (2, 16, [3000, 33], 8, 2, 32, "bf16", "bf16", 64),               # 16 tokens, D = 32
+    (2, 1, [300, 77], 8, 2, 128, "bf16", "f8e4m3", 64),             # e4m3 cache: rows quantised by the caller
+]
+
+
+def _append(inp, k_new, v_new, block_table=None):
+    """Runs fmha_paged_kv_append on device copies of the caches; returns (status, k_cache, v_cache) on the CPU."""
+    import head_attention_03_amd as fmha
+    dev = torch.device("cuda:0")
+    kc, vc = inp.k_cache.to(dev), inp.v_cache.to(dev)
+    bt = torch.from_numpy(np.ascontiguousarray(inp.block_table if block_table is None else block_table)).to(dev)
+    sl = torch.from_numpy(inp.seqlens_k).to(dev)
+    pk = fmha.make_paged_kv(bt, sl, bt.shape[1], inp.page_size, inp.num_pages, inp.kv_dtype or inp.dtype)
+    st = fmha.fmha_paged_kv_append(kc, vc, k_new.to(dev), v_new.to(dev), inp.B, k_new.shape[1], inp.H_kv, inp.D, pk,
+                                   torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return st, kc.cpu(), vc.cpu()
+
+
+@pytest.mark.parametrize("case", APPEND, ids=lambda c: f"B{c[0]}-new{c[1]}-H{c[3]}/{c[4]}-D{c[5]}-{c[7]}-p{c[8]}")
+def test_paged_append_then_decode(case):
+    import dataclasses
+    from oracle import append_paged
+    from workloads import make_new_rows
+    B, S_new, lk, H, H_kv, D, dtype, kv_dtype, ps = case
+    inp = make_paged(5400 + sum(lk) + ps, B, S_new, lk, H, H_kv, D, dtype, ps, mask="causal_qend", kv_dtype=kv_dtype)
+    k_new, v_new = make_new_rows(inp.seed + 1, B, S_new, H_kv, D, kv_dtype, inp.k_scale, inp.v_scale)
+    log(f"[case] append {case} seed={inp.seed} pages={inp.num_pages}")
+    st, kc, vc = _append(inp, k_new, v_new)
+    assert st == 0
+    ek, ev = append_paged(to_bits(inp.k_cache), to_bits(inp.v_cache), inp.block_table, inp.seqlens_k,
+                          to_bits(k_new), to_bits(v_new))
+    assert np.array_equal(to_bits(kc), ek) and np.array_equal(to_bits(vc), ev), "cache differs from the oracle's append"
+    # the decode step over the appended cache: the new queries see their own keys (causal-qend)
+    after = dataclasses.replace(inp, k_cache=kc, v_cache=vc)
+    res = run_paged(after)
+    assert res.status == 0
+    o, lse = oracle_paged(after)
+    compare(f"append+decode {case}", res.o_bits, dtype, o, res.lse, lse)
+
+
+def test_paged_append_drops_rows_without_a_page():
+    # the page that would take the new rows of sequence 1 is -1 in the table, and sequence 0's
+    # entry points past the cache: both appends are dropped, the cache is unchanged there
+    from oracle import append_paged
+    from workloads import make_new_rows
+    inp = make_paged(5450, 2, 4, [300, 70], 8, 2, 64, "f16", 64, poison=False)
+    k_new, v_new = make_new_rows(5451, 2, 4, 2, 64, "f16")
+    bt = inp.block_table.copy()
+    bt[1, 69 // 64] = -1
+    bt[0, 299 // 64] = inp.num_pages + 5
+    st, kc, vc = _append(inp, k_new, v_new, block_table=bt)
+    assert st == 0
+    ek, ev = append_paged(to_bits(inp.k_cache), to_bits(inp.v_cache), bt, inp.seqlens_k, to_bits(k_new),
+                          to_bits(v_new))
+    assert np.array_equal(to_bits(kc), ek) and np.array_equal(to_bits(vc), ev)
+    assert np.array_equal(ek, to_bits(inp.k_cache)) and np.array_equal(ev, to_bits(inp.v_cache))

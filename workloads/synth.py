@@ -349,6 +349,19 @@ def make_paged(seed: int, B: int, Sq: int, seqlens_k: Sequence[int], H: int, H_k
                        kv_dtype=kv_dtype)
 
 
+def make_new_rows(seed: int, B: int, S_new: int, H_kv: int, D: int, kv_dtype: str, k_scale: float = 1.0,
+                  v_scale: float = 1.0):
+    """K and V rows of S_new new tokens per sequence, [B, S_new, H_kv, D] in the cache's storage type:
+    N(0, 1) drawn K then V; an e4m3 cache's rows are quantised with the cache's scales."""
+    rng = np.random.default_rng(seed)
+    k32, v32 = draw_normal(rng, (B, S_new, H_kv, D)), draw_normal(rng, (B, S_new, H_kv, D))
+    if kv_dtype == "f8e4m3":
+        k = (torch.from_numpy(k32) / k_scale).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+        v = (torch.from_numpy(v32) / v_scale).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+        return k, v
+    return torch.from_numpy(k32).to(TORCH_DTYPES[kv_dtype]), torch.from_numpy(v32).to(TORCH_DTYPES[kv_dtype])
+
+
 def make_varlen(seed: int, seqlens_q: Sequence[int], seqlens_k: Sequence[int], H: int, H_kv: int, D: int,
                 dtype: str, mask: str = "none", scale: Optional[float] = None, o_scale: float = 1.0,
                 poison_pads: bool = False, rng: Optional[np.random.Generator] = None) -> VarlenInputs:
