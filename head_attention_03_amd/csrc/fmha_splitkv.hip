@@ -486,6 +486,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
     p.lse_part[part] = l_all > 0.0f ? (m_all + __builtin_amdgcn_logf(l_all)) * 0.69314718055994531f : -__builtin_inff();
 }
 
+constexpr int kMergeChunk = 8;  // splits merged per round of loads
+
 // merge kernel: D / 4 threads per row, each 4 consecutive dims.  OUT8: e4m3 output, saturated
 // to the largest finite value and rounded to nearest even (as fmha_fwd's fp8 output).
 template <int DT, int D, bool OUT8 = false>
@@ -495,21 +497,44 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const int row = t / TPR;
   const int part = t % TPR;
   if (row >= p.rows) return;
+  // Splits in chunks of kMergeChunk, each chunk's LSEs and partial rows requested together (a
+  // loop of dependent loads, one split at a time, took several memory round trips per split);
+  // across chunks the running sum is rescaled to the new maximum.  With one chunk this is
+  // exactly the two-pass merge: the maximum first, then the weighted sum in split order.
   float mx = -__builtin_inff();
-  for (int s = 0; s < p.n_splits; ++s) mx = __builtin_fmaxf(mx, p.lse_part[(size_t)s * p.rows + row]);
   float wsum = 0.0f;
   float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (mx != -__builtin_inff()) {
-    for (int s = 0; s < p.n_splits; ++s) {
-      const float ls = p.lse_part[(size_t)s * p.rows + row];
-      if (ls == -__builtin_inff()) continue;  // a split that saw no key of this row
-      const float w = __expf(ls - mx);
-      const float4 os = *(const float4*)(p.o_part + ((size_t)s * p.rows + row) * D + 4 * part);
+  for (int s0 = 0; s0 < p.n_splits; s0 += kMergeChunk) {
+    float ls[kMergeChunk];
+    float4 os[kMergeChunk];
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j)
+      ls[j] = s0 + j < p.n_splits ? p.lse_part[(size_t)(s0 + j) * p.rows + row] : -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j)
+      if (s0 + j < p.n_splits) os[j] = *(const float4*)(p.o_part + ((size_t)(s0 + j) * p.rows + row) * D + 4 * part);
+    float cm = mx;
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) cm = __builtin_fmaxf(cm, ls[j]);
+    if (cm == -__builtin_inff()) continue;  // no split so far saw a key of this row
+    if (cm != mx) {  // rescale what came before to the new maximum
+      const float r = mx == -__builtin_inff() ? 0.0f : __expf(mx - cm);
+      wsum *= r;
+      acc.x *= r;
+      acc.y *= r;
+      acc.z *= r;
+      acc.w *= r;
+      mx = cm;
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) {
+      if (ls[j] == -__builtin_inff()) continue;  // a split that saw no key of this row (or none)
+      const float w = __expf(ls[j] - mx);
       wsum += w;
-      acc.x += w * os.x;
-      acc.y += w * os.y;
-      acc.z += w * os.z;
-      acc.w += w * os.w;
+      acc.x += w * os[j].x;
+      acc.y += w * os[j].y;
+      acc.z += w * os[j].z;
+      acc.w += w * os[j].w;
     }
   }
   const float f = wsum > 0.0f ? p.o_scale / wsum : 0.0f;
