@@ -223,3 +223,16 @@ def test_paged_append_drops_rows_without_a_page():
                           to_bits(v_new))
     assert np.array_equal(to_bits(kc), ek) and np.array_equal(to_bits(vc), ev)
     assert np.array_equal(ek, to_bits(inp.k_cache)) and np.array_equal(ev, to_bits(inp.v_cache))
+
+
+@pytest.mark.parametrize("config_id", [8, 9])
+def test_paged_full_size_workloads(config_id):
+    # the paged decode workloads the benchmark times (the decode shape over 128-key pages in random
+    # order; 16-bit and e4m3 caches): every output element and every LSE
+    from workloads import make_config
+    inp = make_config(config_id)
+    log(f"[case] paged workload {config_id} seed={inp.seed} pages={inp.num_pages} kv={inp.kv_dtype}")
+    res = run_paged(inp)
+    assert res.status == 0
+    o, lse = oracle_paged(inp)
+    compare(f"paged workload {config_id}", res.o_bits, inp.dtype, o, res.lse, lse)

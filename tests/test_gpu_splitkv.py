@@ -113,3 +113,10 @@ def test_splitkv_fp8_varlen():
     assert res.status == 0
     o, lse = oracle_varlen(inp)
     compare("splitkv fp8 varlen", res.o_bits[inp.pad_q:], inp.dtype, o, res.lse, lse)
+
+
+def test_splitkv_full_size_decode_workload():
+    # the decode workload the benchmark times (16 sequences, one new token against 8192 keys, GQA
+    # 32/8, D128 bf16, LSE), in its launch configuration: every output element and every LSE
+    from workloads import make_config
+    _dense("decode workload", make_config(6))
