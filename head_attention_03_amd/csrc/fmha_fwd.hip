@@ -31,7 +31,8 @@
 //   and fed straight back to the matrix cores (the counterpart of the article's section
 //   "Ps 寄存器重排").  The V^T operand comes from the row-major V tile through
 //   ds_read_b64_tr_b16 transpose reads.
-// * exp2 with scale*log2(e) folded into one FMA per score.  The running maximum is only
+// * exp2 with scale*log2(e) folded into one FMA per score (fp8 without an LSE: that FMA
+//   builds the fp32 bit pattern of 2^x, kF8ExpCentre below).  The running maximum is only
 //   raised when a tile's maximum exceeds it by more than 2^8 (a lazy rescale in the spirit
 //   of the article's section "lazy rescale": probabilities stay <= 256, far inside the
 //   range of the 16-bit and fp8 operand types, and the O rescale is skipped for most tiles).
@@ -77,6 +78,25 @@ constexpr int kBN = 64;           // keys per K/V tile (16-bit; fp8 tiles hold 2
 // landing among the subnormals.  The shift cancels in O = sum p v / sum p; the LSE removes it.
 constexpr float kF8Shift = 6.0f;
 constexpr float kF8Threshold = 2.0f;
+// fp8 without an LSE forms 2^x from its fp32 bit pattern (Schraudolph's exponential: N. N.
+// Schraudolph, "A fast, compact approximation of the exponential function", Neural
+// Computation 11(4), 1999).  The integer 2^23 (x + 127 - c), read as a float, is
+// 2^floor(x - c) (1 + frac(x - c)): 2^x with the mantissa interpolated linearly between
+// powers of two, within a factor 1.0615 of it; c = log2(sqrt(1.0615)) centres that error at
+// +-3.03%.  The e4m3 conversion that follows rounds to 3 mantissa bits anyway (+-6.25%), so
+// each probability stays within 9.4% of 2^x, subnormals included, for one FMA and one
+// float-to-integer conversion instead of an FMA and a v_exp_f32 (8 cycles per wave64
+// instruction on gfx950, twice an FMA).  With an LSE the exact v_exp_f32 path is kept: the
+// LSE takes the fp32 row sum of the probabilities.
+constexpr float kF8ExpCentre = 0.0430357f;
+
+// pack_f8x4 written over an old register value: both halves are replaced, so the register
+// needs no zeroing move first.
+__device__ inline uint32_t pack_f8x4_over(uint32_t old, float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
 constexpr int kSchedMfma = 0x008;    // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedDsRead = 0x100;
 constexpr int kPrefetch = 6;         // fp8: LDS reads kept in flight ahead of the MFMAs
@@ -355,7 +375,10 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       const int b = 16 * i + 8 * pp + wave_u;
       const int pos = (b % KBLK) * 64 + lane;  // 16-byte chunk position inside the tile
       const int j = pos / CPR;
-      ld_off[pp][i] = (uint32_t)j * kstride + (((pos % CPR) ^ sw(j)) * 16);
+      // fp8 V tiles: LDS row j holds key row j with bits 2 and 3 swapped, so that the
+      // transposed reads hand each lane the keys of its own probabilities (see pv_mma).
+      const int jg = (F8 && b >= KBLK && (((j >> 2) ^ (j >> 3)) & 1)) ? j ^ 12 : j;
+      ld_off[pp][i] = (uint32_t)jg * kstride + (((pos % CPR) ^ sw(j)) * 16);
     }
   // load i of phase parity pp for the cursor's L(c) into stage c % 3
   auto load_unit = [&](int pp, int i) __attribute__((always_inline)) {
@@ -387,6 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   float l_run2 = 0.0f;
   constexpr bool VSUM = !F8 || LSE_SUM;  // keep the VALU row sum
   const float sl2 = p.scale_log2;
+  const float sl2_bits = 8388608.0f * sl2;  // fp8 without an LSE: 2^23 scale log2(e)
 
   // Per-lane LDS byte offsets.  The swizzle only touches chunk bits that the k-step (K) or
   // the d-block (V) index leaves clear, so every read address is one of these bases XOR a
@@ -399,8 +423,9 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   // 16-bit V transpose read (ds_read_b64_tr_b16): row 4 h32 + s16 / 4 of a 16-row group (and
   // that row + 8), 8 bytes at column 16 g16 + 4 (s16 % 4).
   // fp8 (ds_read_b64_tr_b8, which hands lane j of each 16-lane group byte j % 8 of the words
-  // of lanes j / 8, j / 8 + 2, ..): lane l supplies row 8 h32 + s16 / 2 of a 16-row chunk,
-  // 8 bytes at column 16 g16 + 8 (s16 % 2), and gets column l32 of rows 8 h32 + 0..7.
+  // of lanes j / 8, j / 8 + 2, ..): lane l supplies LDS row 8 h32 + s16 / 2 of a 16-row chunk,
+  // 8 bytes at column 16 g16 + 8 (s16 % 2), and gets column l32 of LDS rows 8 h32 + 0..7
+  // (keys 8 (r / 4) + 4 h32 + r % 4, r = 0..7, of the chunk: the V rows are stored permuted).
   const int v_row0 = F8 ? 8 * h32 + (s16 >> 1) : 4 * h32 + (s16 >> 2);
   const int v_part = F8 ? g16 : 2 * g16 + ((s16 & 3) >> 1);
   const int v_lane0 = TILE + v_row0 * RB + ((v_part ^ sw(v_row0)) * 16) + 8 * (s16 & 1);
@@ -435,8 +460,11 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     s[jb] = mma_f8(a, b, s[jb]);
   };
   // fp8: one PV MFMA, d-block i % NDB and 64-key half kh = i / NDB of the 128-key tile; byte
-  // 8 c + r of either operand is key 64 kh + 16 c + 8 h32 + r (the probabilities are regrouped
-  // to this order at the end of the softmax, and the transposed V reads deliver it).
+  // 8 c + r of either operand is key 64 kh + 16 c + 8 (r / 4) + 4 h32 + r % 4: the order in
+  // which the softmax packs the probabilities (4 per register, straight from the accumulator
+  // layout).  Transposed read c hands lane l column l32 of LDS rows 16 c + 8 h32 + 0..7, and
+  // the V tile stores key row j at LDS row j with bits 2 and 3 swapped, so those LDS rows hold
+  // exactly these keys, and the probabilities need no exchange between lanes.
   auto pv_mma = [&](uint32_t va0, int i) __attribute__((always_inline)) {
     const int db = i % NDB, kh = i / NDB;
     i32x2 t[4];
@@ -627,6 +655,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       m_run = m_new;
     }
     const float m_use = (m_run == -__builtin_inff() ? 0.0f : m_run) - (F8 ? kF8Shift : 0.0f);
+    const float bits_add = 8388608.0f * (127.0f - kF8ExpCentre - m_use);
     // exponentials, packing and VALU row sums (fp32; none for a masked 16-bit tile, which the
     // matrix cores sum; fp8: only for an LSE)
     auto exps = [&](auto masked_tag) __attribute__((always_inline)) {
@@ -636,10 +665,22 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {  // scores 4 qd .. 4 qd + 3: keys 8 qd + 4 h32 + 0..3
           float e[4];
+          if constexpr (F8 && !VSUM) {
+            // 2^x from the bits 2^23 (x + 127 - c) (kF8ExpCentre).  v_cvt_u32_f32 saturates:
+            // a masked score (-inf) or one far below the row max gives +0.
 #pragma unroll
-          for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][4 * qd + u], sl2, -m_use));
-          if constexpr (F8) {
-            pk[jb][qd] = pack_f8x4(e[0], e[1], e[2], e[3]);
+            for (int u = 0; u < 4; ++u) {
+              const float y = __builtin_fmaf(s[jb][4 * qd + u], sl2_bits, bits_add);
+              uint32_t bits;
+              asm("v_cvt_u32_f32 %0, %1" : "=v"(bits) : "v"(y));
+              e[u] = __builtin_bit_cast(float, bits);
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][4 * qd + u], sl2, -m_use));
+          }
+          if constexpr (F8) {  // (the old value is overwritten whole: no zeroing move)
+            pk[jb][qd] = pack_f8x4_over(pk[jb][qd], e[0], e[1], e[2], e[3]);
           } else {
             pk[jb][2 * qd] = T::pack(e[0], e[1]);
             pk[jb][2 * qd + 1] = T::pack(e[2], e[3]);
@@ -664,18 +705,6 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     } else {
       pk_masked = false;
       exps(std::false_type{});
-    }
-    if constexpr (F8) {
-      // Regroup to 8 consecutive keys per lane and 16-key chunk (the fp8 PV operand order):
-      // lane h32 = 0 trades its keys 8..11 of each chunk for keys 4..7 of lane l + 32.
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          auto r = __builtin_amdgcn_permlane32_swap(pk[jb][2 * m], pk[jb][2 * m + 1], false, false);
-          pk[jb][2 * m] = r[0];
-          pk[jb][2 * m + 1] = r[1];
-        }
     }
     // Pin the results here: the compiler may otherwise sink the tail of this arithmetic past
     // the phase barrier, into the matrix phase that follows on this wave.

@@ -13,7 +13,7 @@ import torch
 import oracle
 from harness import (TOL, compare, decoded, log, oracle_dense, oracle_dense_heads, oracle_varlen, run_dense,
                      run_varlen)
-from workloads import make_config, make_dense, make_varlen, to_bits
+from workloads import make_config, make_dense, make_dense_sink, make_varlen, to_bits
 from workloads.synth import O_SENTINEL_BITS
 
 pytestmark = pytest.mark.gpu
@@ -50,11 +50,25 @@ def test_dense_masks_dims(dtype, D, mask):
     _dense_case(f"dense {dtype} D{D} {mask}", inp)
 
 
+@pytest.mark.parametrize("want_lse", [True, False], ids=["lse", "nolse"])
 @pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("mask", MASKS)
-def test_fp8_masks_dims(D, mask):
+def test_fp8_masks_dims(D, mask, want_lse):
+    # without an LSE the kernel forms the probabilities from their fp32 bit pattern, with one
+    # exact v_exp_f32 per score
     inp = make_dense(2400 + D, 2, 200, 333, 4, 2, D, "f8e4m3", mask=mask, o_scale=0.5)
-    _dense_case(f"dense fp8 D{D} {mask}", inp)
+    _dense_case(f"dense fp8 D{D} {mask} lse={want_lse}", inp, want_lse=want_lse)
+
+
+@pytest.mark.parametrize("want_lse", [True, False], ids=["lse", "nolse"])
+@pytest.mark.parametrize("sink_logit,mask", [(6.0, "none"), (9.0, "none"), (12.0, "none"), (9.0, "causal_qend")])
+def test_fp8_attention_sink(sink_logit, mask, want_lse):
+    # One key per row scores sink_logit nats above the rest, so much of a 4096-key row's
+    # weight lies 9-20 binades below its maximum, among the e4m3 subnormals of P.
+    # Probabilities that drop those weights (an e4m3 code linear in x, clipped at the
+    # smallest normal) miss the tolerance here: a CPU model of them errs by ~0.16 against 0.06.
+    inp = make_dense_sink(2470, 1, 64, 4096, 2, 2, 128, "f8e4m3", sink_logit, mask=mask, o_scale=0.5)
+    _dense_case(f"fp8 sink {sink_logit} {mask} lse={want_lse}", inp, want_lse=want_lse)
 
 
 def test_fp8_gqa_more_queries_than_keys():

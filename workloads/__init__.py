@@ -15,6 +15,7 @@ from .synth import (  # noqa: F401
     make_paged,
     PagedInputs,
     make_dense,
+    make_dense_sink,
     make_dense_on_device,
     make_varlen,
     make_config,

@@ -216,6 +216,26 @@ def make_dense(seed: int, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int, d
                        scale=float(scale), o_scale=float(o_scale), seed=seed, q_scale=sq, k_scale=sk, v_scale=sv)
 
 
+def make_dense_sink(seed: int, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int, dtype: str,
+                    sink_logit: float, mask: str = "none", o_scale: float = 1.0) -> DenseInputs:
+    """Dense inputs with an attention sink: key 0 of every sequence and K/V head scores about
+    ``sink_logit`` (natural-log units, at scale 1/sqrt(D)) above the other keys for every query,
+    so most of a long row's weights sit many binades below its maximum.  Q, K, V are drawn as in
+    ``make_dense`` (N(0, 1), order Q, K, V); then dim 0 of every query is raised by 4 and dim 0 of
+    key 0 is set to sink_logit sqrt(D) / 4, before the conversion to the storage type."""
+    rng = np.random.default_rng(seed)
+    q = draw_normal(rng, (B, Sq, H, D))
+    k = draw_normal(rng, (B, Sk, H_kv, D))
+    v = draw_normal(rng, (B, Sk, H_kv, D))
+    q[..., 0] += 4.0
+    if Sk > 0:
+        k[:, 0, :, 0] = sink_logit * math.sqrt(D) / 4.0
+    (q, sq), (k, sk), (v, sv) = (_to_storage(x, dtype) for x in (q, k, v))
+    return DenseInputs(q=q, k=k, v=v, B=B, Sq=Sq, Sk=Sk, H=H, H_kv=H_kv, D=D, dtype=dtype, mask=mask,
+                       scale=1.0 / math.sqrt(D), o_scale=float(o_scale), seed=seed, q_scale=sq, k_scale=sk,
+                       v_scale=sv)
+
+
 def make_dense_on_device(seed: int, B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int, dtype: str,
                          mask: str = "none", device="cuda:0") -> DenseInputs:
     """Dense 16-bit inputs too large to draw on the host in reasonable time (gigabytes per tensor):
