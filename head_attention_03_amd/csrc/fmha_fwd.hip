@@ -90,6 +90,25 @@ constexpr float kF8Threshold = 2.0f;
 // LSE takes the fp32 row sum of the probabilities.
 constexpr float kF8ExpCentre = 0.0430357f;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Row-sum MFMAs on the accumulator type of each path (fp8: f32x4 of a 16x16x128 product;
+// 16-bit: f32x16 of the 32x32x16 product).  The other path never calls the other one.
+template <class Acc>
+__device__ inline Acc rowsum_f8(i32x8 ones, i32x8 p, Acc c) {
+  if constexpr (sizeof(Acc) == sizeof(f32x4))
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, p, c, 0, 0, 0, 127, 0, 127);
+  else
+    return c;
+}
+template <class T, class Acc>
+__device__ inline Acc rowsum_16(i32x4 ones, i32x4 p, Acc c) {
+  if constexpr (sizeof(Acc) == sizeof(f32x16))
+    return T::mma(ones, p, c);
+  else
+    return c;
+}
+
 // pack_f8x4 written over an old register value: both halves are replaced, so the register
 // needs no zeroing move first.
 __device__ inline uint32_t pack_f8x4_over(uint32_t old, float a, float b, float c, float d) {
@@ -398,14 +417,21 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   bool pk_masked = false;           // 16-bit: pk holds a masked tile, whose row sum the matrix cores add
   float m_run = -__builtin_inff();  // running max of scale*log2(e)*s for query l32
   // Row sums on the matrix cores: an all-ones A operand against the probability operand of
-  // the PV product, so every element of acc_l holds the row sum of this lane's query over the
+  // the PV product, so element 0 of acc_l holds the row sum of this lane's query over the
   // rounded probabilities that O is built from (exact in fp32).  fp8 sums every tile there
-  // (its matrix phase is half as long as the softmax, so the MFMA is the cheap place); the
-  // 16-bit paths only the tiles that needed the mask (4 MFMAs after the tile's PV product),
-  // where a row with few visible keys must be normalised by exactly the weights of its
-  // numerator, and add the fp32 probabilities of fully visible tiles on the vector ALU
-  // (l_run + l_run2), where the longer 16-bit matrix phase hides them.
-  f32x16 acc_l = {};
+  // (one 16x16x128 MFMA per 64 keys, see pv_mma); the 16-bit paths only the tiles that
+  // needed the mask (4 MFMAs after the tile's PV product), where a row with few visible keys
+  // must be normalised by exactly the weights of its numerator, and add the fp32
+  // probabilities of fully visible tiles on the vector ALU (l_run + l_run2), where the
+  // longer 16-bit matrix phase hides them.
+  using AccL = std::conditional_t<F8, f32x4, f32x16>;
+  AccL acc_l = {};
+  // fp8: the A operand of the row-sum MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, where lane l
+  // holds A row l % 16 over k-block l / 16 and receives C rows 4 (l / 16) + 0..3 of column
+  // l % 16).  The probability operand puts query q = l % 32 in column q % 16 of k-blocks
+  // (q / 16) + {0, 2}, so A rows 0 and 8 take blocks 0 and 2 (queries 0..15), rows 4 and 12
+  // blocks 1 and 3 (queries 16..31), and every lane's C element 0 is its own query's sum.
+  const int f8_ones = (((lane & 3) == 0) && (((lane >> 2) ^ (lane >> 4)) & 1) == 0) ? 0x38383838 : 0;
   float l_run = 0.0f;  // this lane's part of the VALU row sum (l_run + l_run2)
   float l_run2 = 0.0f;
   constexpr bool VSUM = !F8 || LSE_SUM;  // keep the VALU row sum
@@ -476,10 +502,9 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     const i32x8 b = {(int)pk[2 * kh][0], (int)pk[2 * kh][1], (int)pk[2 * kh][2], (int)pk[2 * kh][3],
                      (int)pk[2 * kh + 1][0], (int)pk[2 * kh + 1][1], (int)pk[2 * kh + 1][2], (int)pk[2 * kh + 1][3]};
     acc_o[db] = mma_f8(a, b, acc_o[db]);
-    if (db == NDB - 1) {  // row sums of this half: e4m3 1.0 = 0x38
-      const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                          0x38383838, 0x38383838, 0x38383838, 0x38383838};
-      acc_l = mma_f8(ones, b, acc_l);
+    if (db == NDB - 1) {  // row sums of this half (e4m3 1.0 = 0x38): see f8_ones
+      const i32x8 ones = {f8_ones, f8_ones, f8_ones, f8_ones, f8_ones, f8_ones, f8_ones, f8_ones};
+      acc_l = rowsum_f8(ones, b, acc_l);
     }
   };
   constexpr int NQK = NJB * KS;              // MFMAs of S^T for one tile
@@ -608,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
         for (int jc = 0; jc < 4; ++jc) {
           const i32x4 bp = {(int)pk[jc >> 1][4 * (jc & 1)], (int)pk[jc >> 1][4 * (jc & 1) + 1],
                             (int)pk[jc >> 1][4 * (jc & 1) + 2], (int)pk[jc >> 1][4 * (jc & 1) + 3]};
-          acc_l = T::mma(ones, bp, acc_l);
+          acc_l = rowsum_16<T>(ones, bp, acc_l);
         }
       }
     }
@@ -789,7 +814,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
-    acc_l = f32x16{};
+    acc_l = AccL{};
     l_run = 0.0f;
     l_run2 = 0.0f;
     m_run = -__builtin_inff();
