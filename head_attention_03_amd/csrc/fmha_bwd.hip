@@ -198,7 +198,7 @@ __device__ inline void row_chains(f32x16 (&c)[NC], const uint32_t (&base)[NC], c
 // ------------------------------------------------------------------------------------------
 // dQ kernel: grid = B * H * n_tiles workgroups of kQThreads
 // ------------------------------------------------------------------------------------------
-template <int DT, int D>
+template <int DT, int D, bool WIDE>
 __global__ __launch_bounds__(kQThreads, 1) void dq_kernel(const Params p) {
   constexpr int E = 2;
   constexpr int RB = D * E;          // bytes per row
@@ -242,22 +242,22 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_kernel(const Params p) {
   const int wave_lim = p.causal ? min(sq.Sk_b - 1, qw0 + off) : sq.Sk_b - 1;
   const int wave_max = p.causal ? min(sq.Sk_b - 1, qw0 + 31 + off) : sq.Sk_b - 1;
 
+  // Byte offsets stay 32-bit however long the sequence: the Q, dO, O and dQ descriptors start
+  // at the workgroup's first row, and each K/V tile load gets descriptors that start at its tile.
   const uint32_t qstride = (uint32_t)p.H * RB;
   const uint32_t kstride = (uint32_t)p.H_kv * RB;
-  const size_t q_base = (size_t)sq.q_row0 * qstride;
+  const size_t q_base = ((size_t)sq.q_row0 + qt0) * qstride;
   const size_t k_base = ((size_t)sq.k_row0 * p.H_kv + kvh) * RB;
-  const uint32_t q_bytes = sq.Sq_b > 0 ? (uint32_t)sq.Sq_b * qstride : 0;
-  const uint32_t k_bytes = sq.Sk_b > 0 ? (uint32_t)(sq.Sk_b - 1) * kstride + RB : 0;
+  const uint32_t q_bytes = (uint32_t)min(sq.Sq_b - qt0, kQM) * qstride;
+  const size_t k_len = sq.Sk_b > 0 ? (size_t)(sq.Sk_b - 1) * kstride + RB : 0;  // bytes from k_base
   const auto rq = make_rsrc((const char*)p.q + q_base, q_bytes);
   const auto rdo = make_rsrc((const char*)p.dout + q_base, q_bytes);
   const auto rdq = make_rsrc((const char*)p.dq + q_base, q_bytes);
-  const i32x4 rk = make_rsrc_words((const char*)p.k + k_base, k_bytes);
-  const i32x4 rv = make_rsrc_words((const char*)p.v + k_base, k_bytes);
 
   // the wave's Q and dO rows as B operands (row l32, dims 16 ks + 8 h32 ..); rows past the
   // sequence read 0
   i32x4 qf[KS], dof[KS];
-  const uint32_t frag = (uint32_t)qi * qstride + (uint32_t)h * RB + 16 * h32;
+  const uint32_t frag = (uint32_t)(qi - qt0) * qstride + (uint32_t)h * RB + 16 * h32;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     qf[ks] = load_b128(rq, frag + 32 * ks);
@@ -306,11 +306,28 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_kernel(const Params p) {
     ld_v[i] = g >= TBLK;
     ld_dst[i] = (uint32_t)((g >= TBLK ? TILE : 0) + 1024 * gi);
   }
+  // K/V tiles: one descriptor pair over the sequence's keys when the host has seen that their
+  // byte offsets fit 31 bits; otherwise (WIDE) descriptors placed at each tile, a few scalar
+  // instructions more per tile (done always, they cost ~2% of the whole backward).
+  i32x4 rk_seq = {}, rv_seq = {};
+  if constexpr (!WIDE) {
+    rk_seq = make_rsrc_words((const char*)p.k + k_base, (uint32_t)k_len);
+    rv_seq = make_rsrc_words((const char*)p.v + k_base, (uint32_t)k_len);
+  }
   auto load_step = [&](int n) __attribute__((always_inline)) {
-    const uint32_t key0 = (uint32_t)(n * kQN) * kstride;
     const uint32_t st = ring + (uint32_t)((n % kStages) * STAGE);
+    if constexpr (!WIDE) {
+      const uint32_t key0 = (uint32_t)(n * kQN) * kstride;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) lds_load16(ld_v[i] ? rv : rk, key0 + ld_off[i], st + ld_dst[i]);
+      for (int i = 0; i < LPW; ++i) lds_load16(ld_v[i] ? rv_seq : rk_seq, key0 + ld_off[i], st + ld_dst[i]);
+    } else {  // descriptors over this tile's keys (rows past the sequence read 0)
+      const size_t key0 = (size_t)(n * kQN) * kstride;
+      const uint32_t bytes = k_len > key0 ? (uint32_t)min(k_len - key0, (size_t)kQN * kstride) : 0;
+      const i32x4 rk = make_rsrc_words((const char*)p.k + k_base + key0, bytes);
+      const i32x4 rv = make_rsrc_words((const char*)p.v + k_base + key0, bytes);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) lds_load16(ld_v[i] ? rv : rk, ld_off[i], st + ld_dst[i]);
+    }
   };
   if (n_steps > 0) load_step(0);
   if (n_steps > 1) load_step(1);
@@ -384,7 +401,7 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_kernel(const Params p) {
 
   // dQ = scale * acc: lane holds row qi (rows past the sequence are dropped by the descriptor)
   if (!wave_on) return;
-  const uint32_t at = (uint32_t)qi * qstride + (uint32_t)h * RB;
+  const uint32_t at = (uint32_t)(qi - qt0) * qstride + (uint32_t)h * RB;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) store_block<DT>(acc[db], p.scale, rdq, at + 64 * db, h32);
 }
@@ -402,7 +419,7 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_kernel(const Params p) {
 // vector work of one wave (the exponentials, or the dS products) issues while the other
 // wave's MFMAs run.  Q tiles stay in LDS one step longer than dO tiles for the dS-wave's
 // transposed reads: 4 Q slots, 3 dO slots, 2 P slots.
-template <int DT, int D>
+template <int DT, int D, bool WIDE>
 __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
   constexpr int E = 2;
   constexpr int RB = D * E;
@@ -447,15 +464,22 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
   const int nq = max(0, n_qt - qt_first);
   const int n_steps = nq * p.group;
 
+  // Byte offsets stay 32-bit however long the sequence: the K, V, dK and dV descriptors start at
+  // the workgroup's first key, and each Q/dO tile load gets descriptors that start at its tile.
   const uint32_t qstride = (uint32_t)p.H * RB;
   const uint32_t kstride = (uint32_t)p.H_kv * RB;
   const size_t q_base = (size_t)sq.q_row0 * qstride;
-  const size_t k_base = ((size_t)sq.k_row0 * p.H_kv + kvh) * RB;
-  const uint32_t q_bytes = sq.Sq_b > 0 ? (uint32_t)sq.Sq_b * qstride : 0;
-  const uint32_t k_bytes = sq.Sk_b > 0 ? (uint32_t)(sq.Sk_b - 1) * kstride + RB : 0;
-  const i32x4 rq = make_rsrc_words((const char*)p.q + q_base, q_bytes);
-  const i32x4 rdo = make_rsrc_words((const char*)p.dout + q_base, q_bytes);
+  const size_t k_base = ((size_t)sq.k_row0 + kb0) * kstride + (size_t)kvh * RB;
+  const uint32_t k_bytes = (uint32_t)(min(sq.Sk_b - kb0, kKvN) - 1) * kstride + RB;
   const i32x4 raux = make_rsrc_words(p.aux, p.aux_bytes);
+  // Q/dO tiles: one descriptor pair over the sequence's rows when the host has seen that their
+  // byte offsets fit 31 bits; otherwise (WIDE) descriptors placed at each tile
+  i32x4 rq_seq = {}, rdo_seq = {};
+  if constexpr (!WIDE) {
+    const uint32_t q_len = (uint32_t)sq.Sq_b * qstride;
+    rq_seq = make_rsrc_words((const char*)p.q + q_base, q_len);
+    rdo_seq = make_rsrc_words((const char*)p.dout + q_base, q_len);
+  }
 
   // tile loads: load g of a step (0 .. 2 TBLK - 1; Q first, then dO) is wave g % kKvWaves's;
   // wave 0 also copies the step's statistics block (and the next one, unused) into LDS
@@ -484,10 +508,20 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
     const int hi = t / nq;
     const int qt = qt_first + t - hi * nq;
     const int hq = kvh * p.group + hi;
-    const uint32_t base = (uint32_t)(qt * kKvM) * qstride + (uint32_t)hq * RB;
     const uint32_t sq_ = q_slot(t), sd = do_slot(t);
+    if constexpr (!WIDE) {
+      const uint32_t base = (uint32_t)(qt * kKvM) * qstride + (uint32_t)hq * RB;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) lds_load16(ld_do[i] ? rdo : rq, base + ld_off[i], (ld_do[i] ? sd : sq_) + ld_dst[i]);
+      for (int i = 0; i < LPW; ++i)
+        lds_load16(ld_do[i] ? rdo_seq : rq_seq, base + ld_off[i], (ld_do[i] ? sd : sq_) + ld_dst[i]);
+    } else {  // descriptors over the tile's rows of query head hq (rows past the sequence read 0)
+      const size_t base = q_base + (size_t)(qt * kKvM) * qstride + (size_t)hq * RB;
+      const uint32_t bytes = (uint32_t)(min(sq.Sq_b - qt * kKvM, kKvM) - 1) * qstride + RB;
+      const i32x4 rq = make_rsrc_words((const char*)p.q + base, bytes);
+      const i32x4 rdo = make_rsrc_words((const char*)p.dout + base, bytes);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) lds_load16(ld_do[i] ? rdo : rq, ld_off[i], (ld_do[i] ? sd : sq_) + ld_dst[i]);
+    }
     if (wave_u == 0) {
       const uint32_t blk = (uint32_t)(aux_b + hq * p.aux_hstride + qt);
       lds_load16(raux, blk * kAuxBlock + 16 * lane, aux_slot(t));
@@ -508,7 +542,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
   i32x4 kvf[KS];
   {
     const auto rkv = make_rsrc((const char*)(ds_wave ? p.v : p.k) + k_base, k_bytes);
-    const uint32_t frag = (uint32_t)key * kstride + 16 * h32;
+    const uint32_t frag = (uint32_t)(key - kb0) * kstride + 16 * h32;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kvf[ks] = load_b128(rkv, frag + 32 * ks);
 #pragma unroll
@@ -672,18 +706,22 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
   // sequence are dropped by the descriptor)
   const auto rout = make_rsrc((char*)(ds_wave ? p.dk : p.dv) + k_base, k_bytes);
   const float f = ds_wave ? p.scale : 1.0f;
-  const uint32_t at = (uint32_t)key * kstride;
+  const uint32_t at = (uint32_t)(key - kb0) * kstride;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) store_block<DT>(acc[db], f, rout, at + 64 * db, h32);
 }
 
 template <int DT, int D>
-hipError_t launch(Params p, int n_q_tiles, int n_k_tiles, bool have_q, bool have_k, hipStream_t stream) {
+hipError_t launch(Params p, int n_q_tiles, int n_k_tiles, bool have_q, bool have_k, bool wide_k, bool wide_q,
+                  hipStream_t stream) {
   if (have_q) {  // dQ and the row statistics; the dK/dV kernel after it reads the statistics
     const int64_t pairs = (int64_t)p.B * p.H;
     p.n_tiles = n_q_tiles;
     p.xcd_per = pairs % 8 == 0 ? (int32_t)(pairs / 8) : 0;
-    hipLaunchKernelGGL((dq_kernel<DT, D>), dim3((unsigned)(pairs * n_q_tiles)), dim3(kQThreads), 0, stream, p);
+    if (wide_k)
+      hipLaunchKernelGGL((dq_kernel<DT, D, true>), dim3((unsigned)(pairs * n_q_tiles)), dim3(kQThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((dq_kernel<DT, D, false>), dim3((unsigned)(pairs * n_q_tiles)), dim3(kQThreads), 0, stream, p);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -691,7 +729,12 @@ hipError_t launch(Params p, int n_q_tiles, int n_k_tiles, bool have_q, bool have
     const int64_t pairs = (int64_t)p.B * p.H_kv;
     p.n_tiles = n_k_tiles;
     p.xcd_per = pairs % 8 == 0 ? (int32_t)(pairs / 8) : 0;
-    hipLaunchKernelGGL((dkdv_kernel<DT, D>), dim3((unsigned)(pairs * n_k_tiles)), dim3(kKvThreads), 0, stream, p);
+    if (wide_q)
+      hipLaunchKernelGGL((dkdv_kernel<DT, D, true>), dim3((unsigned)(pairs * n_k_tiles)), dim3(kKvThreads), 0, stream,
+                         p);
+    else
+      hipLaunchKernelGGL((dkdv_kernel<DT, D, false>), dim3((unsigned)(pairs * n_k_tiles)), dim3(kKvThreads), 0, stream,
+                         p);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -705,11 +748,12 @@ fmha_status plan(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int
   if (H > 0 && (H_kv < 1 || H % H_kv != 0)) return FMHA_ERR_INVALID_SHAPE;
   if (D != 32 && D != 64 && D != 128) return FMHA_ERR_INVALID_SHAPE;
   if (packed && (varlen->total_length_q < 0 || varlen->total_length_k < 0)) return FMHA_ERR_INVALID_SHAPE;
-  const int64_t rows_q = packed ? varlen->total_length_q : Sq;
-  const int64_t rows_k = packed ? varlen->total_length_k : Sk;
   const int64_t lim = (int64_t)1 << 31;
-  // per-sequence byte offsets, up to one workgroup tile past the end, fit 31 bits
-  if ((rows_q + kQM) * H * D * 2 >= lim || (rows_k + kKvN) * H_kv * D * 2 >= lim) return FMHA_ERR_UNSUPPORTED;
+  // the kernels address one workgroup's rows (or one tile's) from a descriptor placed at them:
+  // those byte offsets fit 31 bits; a sequence may be any length
+  if ((int64_t)kQM * H * D * 2 >= lim || (int64_t)kKvN * H_kv * D * 2 >= lim ||
+      (int64_t)kKvM * H * D * 2 >= lim)
+    return FMHA_ERR_UNSUPPORTED;
   const int64_t nqb = (Sq + kAuxRows - 1) / kAuxRows;
   int64_t blocks;
   if (packed) {
@@ -809,16 +853,24 @@ fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o,
   p.xcd_per = 0;
   p.n_tiles = 0;
 
+  // Streams whose byte offsets from the start of one sequence could pass 31 bits (one tile to
+  // spare; packed batches bounded by their totals) take the kernels that place descriptors at
+  // every streamed tile: K/V in the dQ kernel, Q/dO in the dK/dV kernel.
+  const int64_t rows_q = packed ? varlen->total_length_q : Sq;
+  const int64_t rows_k = packed ? varlen->total_length_k : Sk;
+  const bool wide_k = (rows_k + kKvN) * H_kv * D * 2 >= lim;
+  const bool wide_q = (rows_q + kKvN) * H * D * 2 >= lim;
+
   hipError_t err = hipSuccess;
   const int nq = (int)n_q, nk = (int)n_k;
   if (dtype == FMHA_DTYPE_BF16) {
-    if (D == 32) err = launch<fmha::kBF16, 32>(p, nq, nk, have_q, have_k, stream);
-    if (D == 64) err = launch<fmha::kBF16, 64>(p, nq, nk, have_q, have_k, stream);
-    if (D == 128) err = launch<fmha::kBF16, 128>(p, nq, nk, have_q, have_k, stream);
+    if (D == 32) err = launch<fmha::kBF16, 32>(p, nq, nk, have_q, have_k, wide_k, wide_q, stream);
+    if (D == 64) err = launch<fmha::kBF16, 64>(p, nq, nk, have_q, have_k, wide_k, wide_q, stream);
+    if (D == 128) err = launch<fmha::kBF16, 128>(p, nq, nk, have_q, have_k, wide_k, wide_q, stream);
   } else {
-    if (D == 32) err = launch<fmha::kF16, 32>(p, nq, nk, have_q, have_k, stream);
-    if (D == 64) err = launch<fmha::kF16, 64>(p, nq, nk, have_q, have_k, stream);
-    if (D == 128) err = launch<fmha::kF16, 128>(p, nq, nk, have_q, have_k, stream);
+    if (D == 32) err = launch<fmha::kF16, 32>(p, nq, nk, have_q, have_k, wide_k, wide_q, stream);
+    if (D == 64) err = launch<fmha::kF16, 64>(p, nq, nk, have_q, have_k, wide_k, wide_q, stream);
+    if (D == 128) err = launch<fmha::kF16, 128>(p, nq, nk, have_q, have_k, wide_k, wide_q, stream);
   }
   return err == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
 }

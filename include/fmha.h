@@ -64,12 +64,15 @@ typedef enum {
                                     cu_seqlens pointer is set */
   FMHA_ERR_INVALID_SHAPE = 2,    /* negative sizes, H % H_kv != 0, D not in {32, 64, 128}, totals < 0 */
   FMHA_ERR_UNSUPPORTED = 3,      /* dtype/mask enum out of range, or a problem too large for the
-                                    kernels' 32-bit offsets.  fmha_fwd rebases its offsets per
-                                    q-tile and per K/V tile, so sequences may be of any length; it
-                                    refuses only three K/V tiles (192 16-bit or 384 e4m3 rows) or
-                                    256 Q rows of 2^31 bytes or more, and dense B * Sq or B * Sk of
-                                    2^31 rows or more.  fmha_fwd_splitkv and fmha_bwd refuse any
-                                    tensor of one sequence of 2^31 bytes or more. */
+                                    kernels' 32-bit offsets.  fmha_fwd and fmha_bwd address each
+                                    workgroup's rows and each streamed tile from descriptors placed
+                                    there, so sequences may be of any length: fmha_fwd refuses only
+                                    three K/V tiles (192 16-bit or 384 e4m3 rows) or 256 Q rows of
+                                    2^31 bytes or more, and dense B * Sq or B * Sk of 2^31 rows or
+                                    more; fmha_bwd refuses 256 query rows or 128 K/V rows of 2^31
+                                    bytes or more, or a statistics workspace of 2^31 bytes or more.
+                                    fmha_fwd_splitkv refuses any tensor of one sequence of 2^31
+                                    bytes or more. */
   FMHA_ERR_MISALIGNED = 4,       /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   FMHA_ERR_INVALID_ARGUMENT = 5, /* scale not finite and > 0, or o_scale not finite */
   FMHA_ERR_HIP = 6,              /* the kernel launch failed (hipGetLastError), or the device address

@@ -32,7 +32,11 @@ dO; Q = 0: uniform weights); invariants (sum of dK over the keys is 0, sum of dV
 sum of dO over rows with a key, unseen keys get no gradient, linearity in dO, sum_d O dO =
 sum_j P dP, GQA == MHA on repeated heads summed, packed == per-sequence); planted mistakes
 (dropped or sign-flipped softmax term, untransposed operands, missing or doubled scale, dP
-from K, GQA overwrite or wrong head, varlen key offset) fail the pins.
+from K, GQA overwrite or wrong head, varlen key offset) fail the pins.  The row-block form
+for sequences too long to hold S (attention_head_backward_rows) is pinned against autograd
+directly at several block sizes and on rows that see no key; its planted mistakes (dropped
+softmax term, dV from dS, dQ row off by one, block mask taken from row 0, dK without the
+scale) fail the pins too.
 
 Paged-cache pins (tests/test_oracle_paged.py): brute force with per-key page arithmetic and
 the plain softmax quotient; the dense forward oracle on a cache laid out in order; invariance
@@ -57,6 +61,7 @@ from .backward import (  # noqa: F401
     attention_backward_dense,
     attention_backward_varlen,
     attention_head_backward,
+    attention_head_backward_rows,
     sum_o_do,
 )
 from .paged import append_paged, attention_paged, gather_pages  # noqa: F401

@@ -38,7 +38,7 @@ from typing import Sequence, Tuple
 
 import numpy as np
 
-from .attention import attention_head
+from .attention import attention_head, visible_keys
 
 
 def attention_head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
@@ -56,6 +56,46 @@ def attention_head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.
     dq = scale * (ds @ k)
     dk = scale * (ds.T @ q)
     return dq, dk, dv
+
+
+def attention_head_backward_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
+                                 mask: str, q_rows: Sequence[int], k_rows: Sequence[int],
+                                 chunk: int = 1024) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One sequence and head too long to hold S whole: the gradients of attention_head_backward
+    at the query rows q_rows (dQ) and at the key rows k_rows (this head's part of dK and dV),
+    with S, P and dP formed for `chunk` query rows at a time (the same steps, row block by row
+    block; only the order of the sums over query rows changes).
+    Returns dQ [len(q_rows), D], dK [len(k_rows), D], dV [len(k_rows), D] (fp64)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    sq, sk, D = q.shape[0], k.shape[0], q.shape[1]
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    dq_rows = np.zeros((len(q_rows), D))
+    dk_rows = np.zeros((len(k_rows), D))
+    dv_rows = np.zeros((len(k_rows), D))
+    for r0 in range(0, sq, chunk):
+        r1 = min(sq, r0 + chunk)
+        # the forward's probabilities of rows r0 .. r1 - 1 (rows with no visible key: P = 0)
+        s = scale * (q[r0:r1] @ k.T)
+        vis = visible_keys(sq, sk, mask, rows=range(r0, r1))
+        has_key = vis.any(axis=1)
+        m = np.where(has_key, np.where(vis, s, -np.inf).max(axis=1, initial=-np.inf), 0.0)
+        e = np.where(vis, np.exp(np.where(vis, s, 0.0) - m[:, None]), 0.0)
+        den = e.sum(axis=1)
+        p = np.zeros_like(e)
+        p[has_key] = e[has_key] / den[has_key, None]
+        # the backward steps on these rows
+        dp = do[r0:r1] @ v.T
+        delta_rows = (p * dp).sum(axis=1)
+        ds = p * (dp - delta_rows[:, None])
+        sel = np.nonzero((q_rows >= r0) & (q_rows < r1))[0]
+        dq_rows[sel] = scale * (ds[q_rows[sel] - r0] @ k)
+        dk_rows += scale * (ds[:, k_rows].T @ q[r0:r1])
+        dv_rows += p[:, k_rows].T @ do[r0:r1]
+    return dq_rows, dk_rows, dv_rows
 
 
 def attention_backward_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,

@@ -181,3 +181,40 @@ def test_bwd_gqa_long_context_sampled():
     inp = make_dense(4902, 1, 8192, 8192, 32, 8, 128, "bf16", mask="causal_qbegin")
     do = make_grad(4903, (1, 8192, 32, 128), "bf16")
     _sampled_full_size("GQA 8192 bwd", inp, do, heads=[20, 21, 22, 23])
+
+
+def test_bwd_tensors_beyond_2gib():
+    # B=1, 17000 queries and keys, 512 heads, D=128 bf16 causal: 2.2 GB per tensor, so the byte
+    # offsets of rows 16384 and later pass 2^31 in every tensor (descriptors placed at each
+    # workgroup's rows and at each streamed tile).  Inputs and dO drawn on the device; O and
+    # LSE from fmha_fwd; heads 0 and 511 compared whole (every row of dQ, dK, dV) with the
+    # row-block oracle.
+    import head_attention_03_amd as fmha
+    from workloads import make_dense_on_device, make_grad_on_device
+    S, H, D = 17000, 512, 128
+    dev = torch.device("cuda:0")
+    inp = make_dense_on_device(4950, 1, S, S, H, H, D, "bf16", mask="causal_qbegin")
+    do = make_grad_on_device(4951, (1, S, H, D), "bf16")
+    log(f"[case] bwd beyond 2 GiB: B=1 Sq=Sk={S} H={H} D={D} causal_qbegin seed=4950 "
+        f"({inp.q.numel() * 2 / 2**30:.2f} GiB per tensor)")
+    o = torch.empty_like(inp.q)
+    lse = torch.empty((1, H, S), dtype=torch.float32, device=dev)
+    st = fmha.fmha_fwd(inp.q, inp.k, inp.v, o, lse, 1, S, S, H, H, D, inp.kernel_scale, inp.mask, inp.dtype, 1.0,
+                       None, torch.cuda.current_stream())
+    assert st == 0, fmha.fmha_status_string(st)
+    dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
+    need = fmha.fmha_bwd_workspace_size(1, S, S, H, H, D, None)
+    ws = torch.full((max(need, 16) // 4,), float("nan"), dtype=torch.float32, device=dev)
+    st = fmha.fmha_bwd(inp.q, inp.k, inp.v, o, do, lse, dq, dk, dv, 1, S, S, H, H, D, inp.kernel_scale, inp.mask,
+                       inp.dtype, None, ws, need, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert st == 0, fmha.fmha_status_string(st)
+    rows = list(range(S))
+    for h in (0, H - 1):
+        q_h, k_h, v_h, do_h = (oracle.decode(to_bits(t[0, :, h].cpu()), inp.dtype) for t in (inp.q, inp.k, inp.v, do))
+        gq, gk, gv = oracle.attention_head_backward_rows(q_h, k_h, v_h, do_h, inp.scale, inp.mask, rows, rows)
+        compare_grad(f"beyond 2 GiB dQ head {h}", dq[0, :, h].cpu(), inp.dtype, gq)
+        compare_grad(f"beyond 2 GiB dK head {h}", dk[0, :, h].cpu(), inp.dtype, gk)
+        compare_grad(f"beyond 2 GiB dV head {h}", dv[0, :, h].cpu(), inp.dtype, gv)
+    del inp, do, o, dq, dk, dv, ws
+    torch.cuda.empty_cache()

@@ -203,7 +203,40 @@ def pin_invariants(mod):
             np.testing.assert_allclose(dv[k0:k1], gv[0], rtol=1e-12, atol=1e-14)
 
 
-PINS = [pin_autograd, pin_library_sdpa, pin_finite_differences, pin_closed_forms, pin_invariants]
+def pin_rows_autograd(mod):
+    """The row-block form (long sequences) against autograd directly, several block sizes."""
+    rng = np.random.default_rng(12)
+    for sq, sk in ((7, 7), (5, 9), (9, 6)):
+        for mask in MASKS:
+            if mask == "causal_qend" and sk < sq:
+                continue
+            q, k, v, do = _rand(rng, sq, 8), _rand(rng, sk, 8), _rand(rng, sk, 8), _rand(rng, sq, 8)
+            ref = _autograd_head(q, k, v, do, 0.6, mask)
+            rows_q, rows_k = [0, 2, sq - 1], [0, sk // 2, sk - 1]
+            for chunk in (1, 3, 64):
+                dq, dk, dv = mod.attention_head_backward_rows(q, k, v, do, 0.6, mask, rows_q, rows_k, chunk)
+                np.testing.assert_allclose(dq, ref[0][rows_q], rtol=1e-10, atol=1e-12)
+                np.testing.assert_allclose(dk, ref[1][rows_k], rtol=1e-10, atol=1e-12)
+                np.testing.assert_allclose(dv, ref[2][rows_k], rtol=1e-10, atol=1e-12)
+
+
+def pin_rows_keyless_rows(mod):
+    """Rows that see no key (causal_qend with more queries than keys) get dQ = 0 and give no dK
+    or dV; the keys' gradients equal the sums over the rows that see them (autograd on those)."""
+    rng = np.random.default_rng(13)
+    sq, sk = 9, 4
+    q, k, v, do = _rand(rng, sq, 8), _rand(rng, sk, 8), _rand(rng, sk, 8), _rand(rng, sq, 8)
+    seen = sq - sk  # rows 0 .. sq - sk - 1 see no key
+    dq, dk, dv = mod.attention_head_backward_rows(q, k, v, do, 0.8, "causal_qend", list(range(sq)), list(range(sk)), 2)
+    assert np.all(dq[:seen] == 0.0)
+    ref = _autograd_head(q[seen:], k, v, do[seen:], 0.8, "causal_qbegin")
+    np.testing.assert_allclose(dq[seen:], ref[0], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, ref[1], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, ref[2], rtol=1e-10, atol=1e-12)
+
+
+PINS = [pin_autograd, pin_library_sdpa, pin_finite_differences, pin_closed_forms, pin_invariants,
+        pin_rows_autograd, pin_rows_keyless_rows]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -225,6 +258,13 @@ MUTATIONS = {
     "GQA overwrite": ("            dk[b, :, kvh] += gk\n", "            dk[b, :, kvh] = gk\n"),
     "wrong GQA head": ("            kvh = h // group\n            gq, gk, gv = attention_head_backward(q[b, :, h]",
                        "            kvh = h % H_kv\n            gq, gk, gv = attention_head_backward(q[b, :, h]"),
+    "rows: softmax row term dropped": ("ds = p * (dp - delta_rows[:, None])", "ds = p * dp"),
+    "rows: dV from dS": ("dv_rows += p[:, k_rows].T @ do[r0:r1]", "dv_rows += ds[:, k_rows].T @ do[r0:r1]"),
+    "rows: dQ row off by one": ("dq_rows[sel] = scale * (ds[q_rows[sel] - r0] @ k)",
+                                "dq_rows[sel] = scale * (ds[q_rows[sel] - r0 - 1] @ k)"),
+    "rows: block mask from row 0": ("vis = visible_keys(sq, sk, mask, rows=range(r0, r1))",
+                                    "vis = visible_keys(sq, sk, mask, rows=range(0, r1 - r0))"),
+    "rows: dK without scale": ("dk_rows += scale * (ds[:, k_rows].T @ q[r0:r1])", "dk_rows += ds[:, k_rows].T @ q[r0:r1]"),
     "varlen key offset": ("gq, gk, gv = attention_head_backward(q[q0:q1, h], k[k0:k1, kvh], v[k0:k1, kvh]",
                           "gq, gk, gv = attention_head_backward(q[q0:q1, h], k[q0:q0 + k1 - k0, kvh], v[k0:k1, kvh]"),
 }

@@ -11,6 +11,7 @@ from .synth import (  # noqa: F401
     config_seed,
     draw_normal,
     make_grad,
+    make_grad_on_device,
     make_new_rows,
     make_paged,
     PagedInputs,

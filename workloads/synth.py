@@ -270,6 +270,22 @@ def make_grad(seed: int, shape: Sequence[int], dtype: str) -> torch.Tensor:
     return t
 
 
+def make_grad_on_device(seed: int, shape: Sequence[int], dtype: str, device="cuda:0") -> torch.Tensor:
+    """Upstream gradient dO too large to draw on the host: N(0, 1) drawn in float32 by torch's seeded
+    generator on ``device`` (Philox), a row block at a time, rounded to the 16-bit storage type."""
+    if dtype not in ("f16", "bf16"):
+        raise ValueError("device-drawn gradients are 16-bit")
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    out = torch.empty(tuple(shape), dtype=TORCH_DTYPES[dtype], device=device)
+    rows = max(1, (1 << 28) // max(1, int(np.prod(shape[2:])) * shape[0]))
+    for r0 in range(0, shape[1], rows):
+        r1 = min(shape[1], r0 + rows)
+        out[:, r0:r1] = torch.randn((shape[0], r1 - r0) + tuple(shape[2:]), generator=g, device=device,
+                                    dtype=torch.float32).to(TORCH_DTYPES[dtype])
+    return out
+
+
 @dataclasses.dataclass
 class PagedInputs:
     q: torch.Tensor        # [B, Sq, H, D]
