@@ -219,13 +219,16 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
   const int mask_from = min(__builtin_amdgcn_readfirstlane(wg_min), k1);
   const int lim_row = min(vis_end, k1) - 1 - 4 * h32;  // last key this lane keeps, less its key offset
 
-  // ---- descriptors: bounded to the rows of this sequence ------------------------------
+  // ---- descriptors: bounded to the rows of this sequence; K/V start at the split's first key
+  // (the host keeps a split's keys, with its last tiles, below 2^30 bytes), so a sequence's
+  // K/V may be any length ------------------------------------------------------------
   const uint32_t qstride = (uint32_t)p.H * D * E;
   const uint32_t kstride = (uint32_t)p.H_kv * RBK;
   const size_t q_base = (size_t)q_row0 * p.H * D * E;
-  const size_t k_base = ((size_t)k_row0 * p.H_kv + kvh) * RBK;
+  const size_t k_base = ((size_t)k_row0 + (paged ? 0 : k0)) * kstride + (size_t)kvh * RBK;
   const uint32_t q_bytes = Sq_b > 0 ? (uint32_t)Sq_b * qstride : 0;
-  const uint32_t k_bytes = Sk_b > 0 ? (uint32_t)(Sk_b - 1) * kstride + RBK : 0;
+  const int k_rows = paged ? 0 : min(Sk_b - k0, p.chunk + kWaves * kTN * STG);  // rows from k_base
+  const uint32_t k_bytes = k_rows > 0 ? (uint32_t)(k_rows - 1) * kstride + RBK : 0;
   const i32x4 rq = make_rsrc_words((const char*)p.q + q_base, q_bytes);
   const i32x4 rk = make_rsrc_words((const char*)p.k + k_base, k_bytes);
   const i32x4 rv = make_rsrc_words((const char*)p.v + k_base, k_bytes);
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
     const int kt = k0 + (wave_u + n * kWaves) * kTN;  // first key of the tile
     const uint32_t st = ring + (uint32_t)((n % STG) * STAGE);
     i32x4 tk = rk, tv = rv;
-    uint32_t key0 = (uint32_t)kt * kstride;
+    uint32_t key0 = (uint32_t)(kt - k0) * kstride;  // (contiguous: from the split's first key)
     if (paged) {
       const int ps = 1 << p.page_shift;
       const int lp = kt >> p.page_shift;
@@ -555,11 +558,15 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
 }
 
 // Splits per (sequence, K/V head) and keys per split: split until about `target` workgroups,
-// but never below kMinChunk keys per split; chunks are whole wave-tile rounds.
-inline void plan(int64_t units, int64_t Sk, int64_t target, int32_t* n_splits, int32_t* chunk) {
+// but never below kMinChunk keys per split, and never above max_chunk keys (which keeps a
+// split's byte offsets within 31 bits); chunks are whole wave-tile rounds.
+inline void plan(int64_t units, int64_t Sk, int64_t target, int64_t max_chunk, int32_t* n_splits, int32_t* chunk) {
   int64_t n = units > 0 ? (target + units - 1) / units : 1;
   const int64_t n_max = Sk > kMinChunk ? (Sk + kMinChunk - 1) / kMinChunk : 1;
   n = n < 1 ? 1 : n > n_max ? n_max : n;
+  // and at least enough splits that none exceeds max_chunk keys
+  const int64_t n_min = Sk > max_chunk ? (Sk + max_chunk - 1) / max_chunk : 1;
+  n = n < n_min ? n_min : n;
   constexpr int64_t round = kWaves * kTN;
   int64_t c = Sk > 0 ? (Sk + n - 1) / n : round;
   c = (c + round - 1) / round * round;
@@ -646,21 +653,22 @@ fmha_status splitkv_plan(const void* q, const void* k, const void* v, const void
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FMHA_ERR_MISALIGNED;
   if ((uintptr_t)lse & 3) return FMHA_ERR_MISALIGNED;
   const int64_t rows_q = packed ? varlen->total_length_q : Sq;
-  const int64_t rows_k = packed ? varlen->total_length_k : Sk;
   const int64_t lim = (int64_t)1 << 31;
-  // per-sequence byte offsets (tiles run up to one wave-tile round past a split) fit 31 bits;
-  // a paged cache addresses each page on its own
+  // Q byte offsets of one sequence fit 31 bits.  K/V descriptors start at each split's first key
+  // and splits are capped at 2^30 bytes of K (a paged cache addresses each page on its own).
   const int64_t qe = q8 ? 1 : 2, ke = k8 ? 1 : 2;
-  if (rows_q * H * D * qe >= lim || (!paged && (rows_k + kWaves * kTN * kStages) * H_kv * D * ke >= lim))
-    return FMHA_ERR_UNSUPPORTED;
+  if (rows_q * H * D * qe >= lim) return FMHA_ERR_UNSUPPORTED;
+  const int64_t k_row_bytes = (int64_t)H_kv * D * ke;
+  const int64_t max_chunk = k_row_bytes > 0 ? ((int64_t)1 << 30) / k_row_bytes : ((int64_t)1 << 30);
+  if (max_chunk < kMinChunk) return FMHA_ERR_UNSUPPORTED;
   const int64_t q_rows = packed ? (int64_t)varlen->total_length_q : (int64_t)B * Sq;
   const int64_t group = H > 0 ? H / H_kv : 1;
   const int64_t M = group * Sq;
   const int64_t mblks = (M + kRows - 1) / kRows;
   // The workspace is sized for the larger split target, so one size serves both cache types.
   int32_t n_splits = 1, chunk = kWaves * kTN, ws_splits = 1, ws_chunk = kWaves * kTN;
-  plan((int64_t)B * H_kv * mblks, Sk, k8 ? kTargetWgs8 : kTargetWgs, &n_splits, &chunk);
-  plan((int64_t)B * H_kv * mblks, Sk, kTargetWgs8, &ws_splits, &ws_chunk);
+  plan((int64_t)B * H_kv * mblks, Sk, k8 ? kTargetWgs8 : kTargetWgs, max_chunk, &n_splits, &chunk);
+  plan((int64_t)B * H_kv * mblks, Sk, kTargetWgs8, max_chunk, &ws_splits, &ws_chunk);
   const int64_t rows = q_rows * H;
   if (rows >= lim || (int64_t)ws_splits * rows * D >= lim * 2) return FMHA_ERR_UNSUPPORTED;
   *grid = (int64_t)B * H_kv * mblks * n_splits;

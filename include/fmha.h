@@ -71,8 +71,10 @@ typedef enum {
                                     2^31 bytes or more, and dense B * Sq or B * Sk of 2^31 rows or
                                     more; fmha_bwd refuses 256 query rows or 128 K/V rows of 2^31
                                     bytes or more, or a statistics workspace of 2^31 bytes or more.
-                                    fmha_fwd_splitkv refuses any tensor of one sequence of 2^31
-                                    bytes or more. */
+                                    fmha_fwd_splitkv starts its K/V descriptors at each split and
+                                    splits the keys so that none spans 2^30 bytes: it refuses only
+                                    one sequence's Q of 2^31 bytes or more, or a K/V row (all K/V
+                                    heads of one key) of more than 4 MiB. */
   FMHA_ERR_MISALIGNED = 4,       /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   FMHA_ERR_INVALID_ARGUMENT = 5, /* scale not finite and > 0, or o_scale not finite */
   FMHA_ERR_HIP = 6,              /* the kernel launch failed (hipGetLastError), or the device address

@@ -86,7 +86,8 @@ def call_skv(**kw):
     (dict(varlen=fmha.make_varlen(P, None, 1, 300)), 1),
     (dict(B=-1), 2), (dict(H=3, H_kv=2), 2), (dict(D=96), 2),
     (dict(dtype="f8e4m3", D=32), 3), (dict(dtype=7), 3), (dict(mask=9), 3),
-    (dict(Sk=1 << 22, H=64, H_kv=64, D=128), 3),
+    (dict(Sq=1 << 16, H=128, H_kv=128, D=128), 3),  # 2 GiB of Q in one sequence
+    (dict(H=1 << 15, H_kv=1 << 15, D=128), 3),  # a K row of 8 MiB: a split would pass 31-bit offsets
     (dict(q=P + 4), 4), (dict(lse=P + 1), 4), (dict(workspace=P + 8), 4),
     (dict(scale=0.0), 5), (dict(o_scale=float("nan")), 5), (dict(workspace_bytes=100), 5),
 ])
@@ -157,12 +158,12 @@ def test_noalloc_empty_problems_return_ok_without_launch(kw):
 
 
 def test_splitkv_workspace_size_ignores_kv_bytes():
-    # a cache of 2^20 keys x 8 heads x 128 dims (2 GiB of K): too large for the contiguous kernels'
-    # 32-bit offsets, but the paged entry point takes it and needs the same workspace as 8192 keys
-    # split the same number of ways
+    # a cache of 2^20 keys x 8 heads x 128 dims (2 GiB of K): both entry points take it (the
+    # contiguous kernels place their descriptors at each split); 8 units of work split 128 ways
+    # for the 1024-workgroup target, so the workspace holds 128 partials of 32 rows
     need = fmha.fmha_fwd_splitkv_workspace_size(1, 1, 1 << 20, 32, 8, 128)
-    assert need > 0 and need % (32 * 129 * 4) == 0
-    assert call_skv(Sk=1 << 20, H=32, H_kv=8, D=128, workspace_bytes=need) == 3  # contiguous: refused
+    assert need == 128 * 32 * (128 + 1) * 4
+    assert call_skv(Sk=1 << 20, H=32, H_kv=8, D=128, workspace_bytes=need - 1) == 5  # shapes pass, one byte short
     pk = fmha.make_paged_kv(P, P, 1 << 13, 128, 1 << 13, "bf16")
     assert fmha.fmha_fwd_splitkv_paged(q=P, k_cache=P, v_cache=P, o=P, lse=None, B=1, Sq=1, Sk=1 << 20, H=32, H_kv=8,
                                        D=128, scale=0.125, mask="none", dtype="bf16", paged=pk, workspace=P,

@@ -120,3 +120,43 @@ def test_splitkv_full_size_decode_workload():
     # 32/8, D128 bf16, LSE), in its launch configuration: every output element and every LSE
     from workloads import make_config
     _dense("decode workload", make_config(6))
+
+
+def test_splitkv_cache_beyond_2gib():
+    # one sequence's K and V of 2.25 GB each (1,100,000 keys x 8 K/V heads x 128 dims, bf16), two
+    # new tokens under causal-qend: key offsets pass 2^31, handled by descriptors placed at each
+    # split.  Inputs drawn on the device; the LSE and the rows of four query heads (K/V heads 0, 1,
+    # 6, 7) compared with the oracle one row at a time.
+    import oracle
+    import head_attention_03_amd as fmha
+    from harness import compare
+    from workloads import make_dense_on_device, to_bits
+    B, Sq, Sk, H, H_kv, D = 1, 2, 1_100_000, 32, 8, 128
+    dev = torch.device("cuda:0")
+    inp = make_dense_on_device(3400, B, Sq, Sk, H, H_kv, D, "bf16", mask="causal_qend")
+    log(f"[case] splitkv cache beyond 2 GiB: B={B} Sq={Sq} Sk={Sk} H={H}/{H_kv} D={D} causal_qend seed=3400 "
+        f"({inp.k.numel() * 2 / 2**30:.2f} GiB per K/V tensor)")
+    o = torch.empty_like(inp.q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    need = fmha.fmha_fwd_splitkv_workspace_size(B, Sq, Sk, H, H_kv, D, None)
+    ws = torch.full((max(need, 16) // 4,), float("nan"), dtype=torch.float32, device=dev)
+    st = fmha.fmha_fwd_splitkv(inp.q, inp.k, inp.v, o, lse, B, Sq, Sk, H, H_kv, D, inp.kernel_scale, inp.mask,
+                               inp.dtype, 1.0, None, ws, need, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert st == 0, fmha.fmha_status_string(st)
+    got, exp_o, got_lse, exp_lse = [], [], [], []
+    for h in (0, 7, 24, 31):
+        kvh = h // (H // H_kv)
+        k_h = oracle.decode(to_bits(inp.k[:, :, kvh:kvh + 1].cpu()), inp.dtype)
+        v_h = oracle.decode(to_bits(inp.v[:, :, kvh:kvh + 1].cpu()), inp.dtype)
+        q_h = oracle.decode(to_bits(inp.q[:, :, h:h + 1].cpu()), inp.dtype)
+        o_rows, l_rows = oracle.attention_rows(q_h, k_h, v_h, inp.scale, inp.mask, [(0, 0, i) for i in range(Sq)])
+        exp_o.append(o_rows)
+        exp_lse.append(l_rows)
+        got.append(np.stack([to_bits(o[0, i, h].cpu()) for i in range(Sq)]))
+        got_lse.append(np.array([float(lse[0, h, i]) for i in range(Sq)]))
+        del k_h, v_h, q_h
+    compare("splitkv cache beyond 2 GiB (8 rows)", np.concatenate(got), inp.dtype, np.concatenate(exp_o),
+            np.concatenate(got_lse), np.concatenate(exp_lse))
+    del inp, o, ws
+    torch.cuda.empty_cache()
