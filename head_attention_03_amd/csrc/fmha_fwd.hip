@@ -690,9 +690,11 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {  // scores 4 qd .. 4 qd + 3: keys 8 qd + 4 h32 + 0..3
           float e[4];
-          if constexpr (F8 && !VSUM) {
-            // 2^x from the bits 2^23 (x + 127 - c) (kF8ExpCentre).  v_cvt_u32_f32 saturates:
-            // a masked score (-inf) or one far below the row max gives +0.
+          if constexpr (F8 && !VSUM && !MASKED) {
+            // 2^x from the bits 2^23 (x + 127 - c) (kF8ExpCentre).  v_cvt_u32_f32 saturates: a
+            // score far below the row max gives +0.  (Tiles that some row of the wave sees only
+            // in part take the exact exponential below: a row with few keys has all of them
+            // there, and its few weights would not average the approximation out.)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const float y = __builtin_fmaf(s[jb][4 * qd + u], sl2_bits, bits_add);
@@ -719,8 +721,13 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
             if ((j * 4 * NJB) / LPP == 4 * jb + qd) hook(j);
         }
     };
-    if constexpr (F8) {
+    if constexpr (F8 && (VSUM || !MASKABLE)) {
       exps(std::false_type{});
+    } else if constexpr (F8) {
+      if (__builtin_amdgcn_readfirstlane(t >= w_full))
+        exps(std::true_type{});
+      else
+        exps(std::false_type{});
     } else if constexpr (MASKABLE) {
       pk_masked = __builtin_amdgcn_readfirstlane(t >= w_full);
       if (pk_masked)

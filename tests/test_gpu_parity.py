@@ -180,6 +180,7 @@ def test_several_qtiles_per_workgroup_fp8(mask, D):
     assert _items_per_workgroup(1, 128, 1100, mask, 300, 16, D, 1) >= 2
     inp = make_dense(2950 + D, 1, 1100, 300, 128, 16, D, "f8e4m3", mask=mask, o_scale=0.5)
     _dense_case(f"multi-item fp8 D{D} {mask}", inp)
+    _dense_case(f"multi-item fp8 D{D} {mask} (no LSE)", inp, want_lse=False)
 
 
 def test_several_qtiles_per_workgroup_repeatable():
@@ -250,8 +251,10 @@ FP8_TILE_EDGES = [
 @pytest.mark.parametrize("case", FP8_TILE_EDGES, ids=lambda c: f"k{c[1]}-{c[5]}-D{c[4]}")
 def test_varlen_fp8_key_tile_edges(case):
     lq, lk, H, H_kv, D, mask = case
-    _varlen_case(f"varlen fp8 tile edges {lq}/{lk}",
-                 make_varlen(2680 + len(lk), lq, lk, H, H_kv, D, "f8e4m3", mask=mask, o_scale=0.5))
+    inp = make_varlen(2680 + len(lk), lq, lk, H, H_kv, D, "f8e4m3", mask=mask, o_scale=0.5)
+    _varlen_case(f"varlen fp8 tile edges {lq}/{lk}", inp)
+    # without an LSE the probabilities come from the fp32 bit pattern of 2^x
+    _varlen_case(f"varlen fp8 tile edges {lq}/{lk} (no LSE)", inp, want_lse=False)
 
 
 def test_varlen_poisoned_padding_never_read_fp8():
