@@ -92,21 +92,20 @@ constexpr float kF8ExpCentre = 0.0430357f;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Row-sum MFMAs on the accumulator type of each path (fp8: f32x4 of a 16x16x128 product;
-// 16-bit: f32x16 of the 32x32x16 product).  The other path never calls the other one.
-template <class Acc>
-__device__ inline Acc rowsum_f8(i32x8 ones, i32x8 p, Acc c) {
-  if constexpr (sizeof(Acc) == sizeof(f32x4))
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, p, c, 0, 0, 0, 127, 0, 127);
-  else
-    return c;
+// Row-sum MFMAs on the 16x16 shapes: the selecting all-ones operand (see rowsum_lane in the
+// kernel) against the probability operand of the PV product; C element 0 of every lane is the
+// sum of its query's probabilities over the operand's keys.
+__device__ inline f32x4 rowsum_f8(i32x8 ones, i32x8 p, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, p, c, 0, 0, 0, 127, 0, 127);
 }
-template <class T, class Acc>
-__device__ inline Acc rowsum_16(i32x4 ones, i32x4 p, Acc c) {
-  if constexpr (sizeof(Acc) == sizeof(f32x16))
-    return T::mma(ones, p, c);
+template <int DT>
+__device__ inline f32x4 rowsum_16(i32x4 ones, i32x4 p, f32x4 c) {
+  if constexpr (DT == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones), __builtin_bit_cast(bf16x8, p), c,
+                                                   0, 0, 0);
   else
-    return c;
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ones), __builtin_bit_cast(f16x8, p), c, 0,
+                                                  0, 0);
 }
 
 // pack_f8x4 written over an old register value: both halves are replaced, so the register
@@ -416,22 +415,22 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   uint32_t pk[NJB][NPK] = {};       // probabilities of the tile between its softmax and PV phases
   bool pk_masked = false;           // 16-bit: pk holds a masked tile, whose row sum the matrix cores add
   float m_run = -__builtin_inff();  // running max of scale*log2(e)*s for query l32
-  // Row sums on the matrix cores: an all-ones A operand against the probability operand of
-  // the PV product, so element 0 of acc_l holds the row sum of this lane's query over the
-  // rounded probabilities that O is built from (exact in fp32).  fp8 sums every tile there
-  // (one 16x16x128 MFMA per 64 keys, see pv_mma); the 16-bit paths only the tiles that
-  // needed the mask (4 MFMAs after the tile's PV product), where a row with few visible keys
-  // must be normalised by exactly the weights of its numerator, and add the fp32
-  // probabilities of fully visible tiles on the vector ALU (l_run + l_run2), where the
+  // Row sums on the matrix cores: a selecting all-ones A operand against the probability
+  // operand of the PV product, so element 0 of acc_l holds the row sum of this lane's query
+  // over the rounded probabilities that O is built from (exact in fp32).  fp8 sums every tile
+  // there (one 16x16x128 MFMA per 64 keys, see pv_mma); the 16-bit paths only the tiles that
+  // needed the mask (one 16x16x32 MFMA per 16 keys after the tile's PV product), where a row
+  // with few visible keys must be normalised by exactly the weights of its numerator, and add
+  // the fp32 probabilities of fully visible tiles on the vector ALU (l_run + l_run2), where the
   // longer 16-bit matrix phase hides them.
-  using AccL = std::conditional_t<F8, f32x4, f32x16>;
-  AccL acc_l = {};
-  // fp8: the A operand of the row-sum MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, where lane l
-  // holds A row l % 16 over k-block l / 16 and receives C rows 4 (l / 16) + 0..3 of column
-  // l % 16).  The probability operand puts query q = l % 32 in column q % 16 of k-blocks
-  // (q / 16) + {0, 2}, so A rows 0 and 8 take blocks 0 and 2 (queries 0..15), rows 4 and 12
-  // blocks 1 and 3 (queries 16..31), and every lane's C element 0 is its own query's sum.
-  const int f8_ones = (((lane & 3) == 0) && (((lane >> 2) ^ (lane >> 4)) & 1) == 0) ? 0x38383838 : 0;
+  f32x4 acc_l = {};
+  // The A operand of those 16x16 MFMAs: lane l holds A row l % 16 over k-block l / 16 and
+  // receives C rows 4 (l / 16) + 0..3 of column l % 16.  The probability operand puts query
+  // q = l % 32 in column q % 16 of k-blocks (q / 16) + {0, 2}, so A rows 0 and 8 take blocks 0
+  // and 2 (queries 0..15), rows 4 and 12 blocks 1 and 3 (queries 16..31), all other rows
+  // nothing, and every lane's C element 0 is its own query's sum.
+  const bool rowsum_lane = ((lane & 3) == 0) && (((lane >> 2) ^ (lane >> 4)) & 1) == 0;
+  const int f8_ones = rowsum_lane ? 0x38383838 : 0;
   float l_run = 0.0f;  // this lane's part of the VALU row sum (l_run + l_run2)
   float l_run2 = 0.0f;
   constexpr bool VSUM = !F8 || LSE_SUM;  // keep the VALU row sum
@@ -627,13 +626,13 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(acc_o[db]));
     if constexpr (!F8 && MASKABLE) {
       if (pk_masked) {
-        constexpr int one = DT == kBF16 ? 0x3F803F80 : 0x3C003C00;
+        const int one = rowsum_lane ? (DT == kBF16 ? 0x3F803F80 : 0x3C003C00) : 0;
         const i32x4 ones = {one, one, one, one};
 #pragma unroll
         for (int jc = 0; jc < 4; ++jc) {
           const i32x4 bp = {(int)pk[jc >> 1][4 * (jc & 1)], (int)pk[jc >> 1][4 * (jc & 1) + 1],
                             (int)pk[jc >> 1][4 * (jc & 1) + 2], (int)pk[jc >> 1][4 * (jc & 1) + 3]};
-          acc_l = rowsum_16<T>(ones, bp, acc_l);
+          acc_l = rowsum_16<DT>(ones, bp, acc_l);
         }
       }
     }
@@ -821,7 +820,7 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
-    acc_l = AccL{};
+    acc_l = f32x4{};
     l_run = 0.0f;
     l_run2 = 0.0f;
     m_run = -__builtin_inff();
