@@ -37,15 +37,15 @@
 //   of the article's section "lazy rescale": probabilities stay <= 256, far inside the
 //   range of the 16-bit and fp8 operand types, and the O rescale is skipped for most tiles).
 // * The row sum l: on tiles that need the mask (the causal diagonal, the ragged tail) the
-//   matrix cores add the rounded probabilities they multiply (an all-ones operand against
-//   the probability operand of the PV product: 4 more MFMAs per 64-key tile, exact in
-//   fp32), so a row with few visible keys is normalised by exactly the weights of its
-//   numerator; on fully visible tiles the vector ALU adds the fp32 probabilities (as the
-//   FlashAttention papers do), with two independent partial sums per lane.  Summing every
-//   tile on the matrix cores cost more than it saved once the VALU and MFMA phases are
-//   balanced; v_dot2 against 1.0 waits behind the other wave's MFMAs on gfx950.  fp8 sums
-//   every tile on the matrix cores (one MFMA per tile), since its matrix phase is the
-//   short one; with an LSE it also keeps the fp32 sum.
+//   matrix cores add the rounded probabilities they multiply (a selecting all-ones operand
+//   against the probability operand of the PV product: 4 more 16x16x32 MFMAs per 64-key
+//   tile, exact in fp32), so a row with few visible keys is normalised by exactly the
+//   weights of its numerator; on fully visible tiles the vector ALU adds the fp32
+//   probabilities (as the FlashAttention papers do), with two independent partial sums per
+//   lane.  Summing every tile on the matrix cores cost more than it saved once the VALU and
+//   MFMA phases are balanced; v_dot2 against 1.0 waits behind the other wave's MFMAs on
+//   gfx950.  fp8 sums every tile on the matrix cores (two 16x16x128 MFMAs per 128-key tile);
+//   with an LSE it also keeps the fp32 sum.
 // * Steps over tiles that every row sees completely run a build with no mask code at all;
 //   boundary tiles (causal diagonal, ragged tail) run the masked build, the trip-count
 //   split of the CUTLASS fusion point.
