@@ -123,15 +123,16 @@ def test_splitkv_full_size_decode_workload():
 
 
 def test_splitkv_cache_beyond_2gib():
-    # one sequence's K and V of 2.25 GB each (1,100,000 keys x 8 K/V heads x 128 dims, bf16), two
-    # new tokens under causal-qend: key offsets pass 2^31, handled by descriptors placed at each
-    # split.  Inputs drawn on the device; the LSE and the rows of four query heads (K/V heads 0, 1,
-    # 6, 7) compared with the oracle one row at a time.
+    # two sequences whose K and V hold 2.25 GB each (1,100,000 keys x 8 K/V heads x 128 dims, bf16),
+    # two new tokens under causal-qend: key offsets inside a sequence pass 2^31 and the second
+    # sequence starts past 2^31 bytes, handled by descriptors placed at each split.  Inputs drawn
+    # on the device; the LSE and the rows of four query heads (K/V heads 0, 1, 6, 7) of both
+    # sequences compared with the oracle one row at a time.
     import oracle
     import head_attention_03_amd as fmha
     from harness import compare
     from workloads import make_dense_on_device, to_bits
-    B, Sq, Sk, H, H_kv, D = 1, 2, 1_100_000, 32, 8, 128
+    B, Sq, Sk, H, H_kv, D = 2, 2, 1_100_000, 32, 8, 128
     dev = torch.device("cuda:0")
     inp = make_dense_on_device(3400, B, Sq, Sk, H, H_kv, D, "bf16", mask="causal_qend")
     log(f"[case] splitkv cache beyond 2 GiB: B={B} Sq={Sq} Sk={Sk} H={H}/{H_kv} D={D} causal_qend seed=3400 "
@@ -145,18 +146,19 @@ def test_splitkv_cache_beyond_2gib():
     torch.cuda.synchronize()
     assert st == 0, fmha.fmha_status_string(st)
     got, exp_o, got_lse, exp_lse = [], [], [], []
-    for h in (0, 7, 24, 31):
-        kvh = h // (H // H_kv)
-        k_h = oracle.decode(to_bits(inp.k[:, :, kvh:kvh + 1].cpu()), inp.dtype)
-        v_h = oracle.decode(to_bits(inp.v[:, :, kvh:kvh + 1].cpu()), inp.dtype)
-        q_h = oracle.decode(to_bits(inp.q[:, :, h:h + 1].cpu()), inp.dtype)
-        o_rows, l_rows = oracle.attention_rows(q_h, k_h, v_h, inp.scale, inp.mask, [(0, 0, i) for i in range(Sq)])
-        exp_o.append(o_rows)
-        exp_lse.append(l_rows)
-        got.append(np.stack([to_bits(o[0, i, h].cpu()) for i in range(Sq)]))
-        got_lse.append(np.array([float(lse[0, h, i]) for i in range(Sq)]))
-        del k_h, v_h, q_h
-    compare("splitkv cache beyond 2 GiB (8 rows)", np.concatenate(got), inp.dtype, np.concatenate(exp_o),
+    for b in range(B):
+        for h in (0, 7, 24, 31):
+            kvh = h // (H // H_kv)
+            k_h = oracle.decode(to_bits(inp.k[b:b + 1, :, kvh:kvh + 1].cpu()), inp.dtype)
+            v_h = oracle.decode(to_bits(inp.v[b:b + 1, :, kvh:kvh + 1].cpu()), inp.dtype)
+            q_h = oracle.decode(to_bits(inp.q[b:b + 1, :, h:h + 1].cpu()), inp.dtype)
+            o_rows, l_rows = oracle.attention_rows(q_h, k_h, v_h, inp.scale, inp.mask, [(0, 0, i) for i in range(Sq)])
+            exp_o.append(o_rows)
+            exp_lse.append(l_rows)
+            got.append(np.stack([to_bits(o[b, i, h].cpu()) for i in range(Sq)]))
+            got_lse.append(np.array([float(lse[b, h, i]) for i in range(Sq)]))
+            del k_h, v_h, q_h
+    compare("splitkv cache beyond 2 GiB (16 rows)", np.concatenate(got), inp.dtype, np.concatenate(exp_o),
             np.concatenate(got_lse), np.concatenate(exp_lse))
     del inp, o, ws
     torch.cuda.empty_cache()
