@@ -17,7 +17,10 @@ for a given upstream gradient dO.  Per (sequence, head), with every matrix mater
     dK = scale * dS^T Q
 
 delta is computed from its definition; it equals sum_d O_id dO_id (the quantity the
-walk-through's first kernel sums), which the pins check.  Masked positions have P = 0,
+walk-through's first kernel sums), which the pins check.  A backward pass receives O as stored
+(rounded to its type, e4m3 for fp8 inputs), and its first kernel sums that O; the optional `o`
+argument takes delta from a given O in the same way, so that the effect of a coarsely stored O
+is part of the expected result rather than of the error.  Masked positions have P = 0,
 hence dS = 0: no gradient crosses them.  A query row with no visible key has an all-zero
 P row and contributes nothing.
 
@@ -34,7 +37,7 @@ Packed variable-length batches: sequence b owns rows [cu[b], cu[b+1]) as in the 
 """
 from __future__ import annotations
 
-from typing import Sequence, Tuple
+from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -42,8 +45,13 @@ from .attention import attention_head, visible_keys
 
 
 def attention_head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
-                            mask: str) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """One sequence and head: q, do [sq, D]; k, v [sk, D].  Returns dQ [sq, D], dK, dV [sk, D] (fp64)."""
+                            mask: str, o: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One sequence and head: q, do [sq, D]; k, v [sk, D].  Returns dQ [sq, D], dK, dV [sk, D] (fp64).
+
+    o: None, or the forward output [sq, D] as a backward pass receives it (rounded to a storage
+    type).  Given, delta is the row sum of O * dO over it, the quantity the walk-through's first
+    backward kernel forms from its O input, instead of sum_j P_ij dP_ij; the two are equal when
+    o is the exact output."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -51,7 +59,10 @@ def attention_head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.
     _, _, _, p = attention_head(q, k, v, scale, mask, return_p=True)
     dv = p.T @ do
     dp = do @ v.T
-    delta = (p * dp).sum(axis=1)
+    if o is None:
+        delta = (p * dp).sum(axis=1)
+    else:
+        delta = sum_o_do(o, do)
     ds = p * (dp - delta[:, None])
     dq = scale * (ds @ k)
     dk = scale * (ds.T @ q)
@@ -99,8 +110,9 @@ def attention_head_backward_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do
 
 
 def attention_backward_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
-                             mask: str) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """BSHD layout: q, do [B, Sq, H, D]; k, v [B, Sk, H_kv, D] -> dQ [B, Sq, H, D], dK, dV [B, Sk, H_kv, D]."""
+                             mask: str, o: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """BSHD layout: q, do [B, Sq, H, D]; k, v [B, Sk, H_kv, D] -> dQ [B, Sq, H, D], dK, dV [B, Sk, H_kv, D].
+    o: None or the forward output [B, Sq, H, D] as received (see attention_head_backward)."""
     B, Sq, H, D = q.shape
     H_kv = k.shape[2]
     if H % H_kv:
@@ -112,7 +124,8 @@ def attention_backward_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np
     for b in range(B):
         for h in range(H):
             kvh = h // group
-            gq, gk, gv = attention_head_backward(q[b, :, h], k[b, :, kvh], v[b, :, kvh], do[b, :, h], scale, mask)
+            gq, gk, gv = attention_head_backward(q[b, :, h], k[b, :, kvh], v[b, :, kvh], do[b, :, h], scale, mask,
+                                                 None if o is None else o[b, :, h])
             dq[b, :, h] = gq
             dk[b, :, kvh] += gk
             dv[b, :, kvh] += gv
@@ -120,9 +133,10 @@ def attention_backward_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np
 
 
 def attention_backward_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, cu_q: Sequence[int],
-                              cu_k: Sequence[int], scale: float,
-                              mask: str) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Packed layout: q, do [total_q, H, D]; k, v [total_k, H_kv, D] -> dQ, dK, dV of the same shapes."""
+                              cu_k: Sequence[int], scale: float, mask: str,
+                              o: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Packed layout: q, do [total_q, H, D]; k, v [total_k, H_kv, D] -> dQ, dK, dV of the same shapes.
+    o: None or the forward output [total_q, H, D] as received (see attention_head_backward)."""
     total_q, H, D = q.shape
     H_kv = k.shape[1]
     if H % H_kv:
@@ -136,7 +150,7 @@ def attention_backward_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: n
         for h in range(H):
             kvh = h // group
             gq, gk, gv = attention_head_backward(q[q0:q1, h], k[k0:k1, kvh], v[k0:k1, kvh], do[q0:q1, h], scale,
-                                                 mask)
+                                                 mask, None if o is None else o[q0:q1, h])
             dq[q0:q1, h] = gq
             dk[k0:k1, kvh] += gk
             dv[k0:k1, kvh] += gv

@@ -235,8 +235,71 @@ def pin_rows_keyless_rows(mod):
     np.testing.assert_allclose(dv, ref[2], rtol=1e-10, atol=1e-12)
 
 
+def _given_o_head(q, k, v, do, scale, mask, err):
+    """Expected gradients when the backward receives O + err instead of the exact O: autograd's
+    exact gradients, with delta shifted by d_i = sum_d err_id dO_id.  dS moves by -P_ij d_i, so
+    dQ moves by -scale d_i (P K)_i, dK by -scale (P^T diag(d) Q) and dV not at all."""
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64) for x in (q, k, v))
+    s = (scale * (tq @ tk.T)).masked_fill(~torch.from_numpy(_visible(q.shape[0], k.shape[0], mask)), float("-inf"))
+    p = torch.softmax(s, dim=-1).numpy()
+    o = p @ v
+    gq, gk, gv = _autograd_head(q, k, v, do, scale, mask)
+    d = (err * do).sum(axis=1)
+    return o + err, gq - scale * d[:, None] * (p @ k), gk - scale * (p * d[:, None]).T @ q, gv
+
+
+def pin_given_o(mod):
+    """delta from a given O (as a backward pass receives it): the exact O reproduces autograd, and
+    a perturbed O moves the gradients by the closed form of _given_o_head, per head, through the
+    dense wrapper with a GQA group and through the packed wrapper."""
+    rng = np.random.default_rng(14)
+    for sq, sk, mask in ((5, 5, "causal_qbegin"), (4, 7, "none"), (6, 6, "causal_qend")):
+        q, k, v, do = _rand(rng, sq, 8), _rand(rng, sk, 8), _rand(rng, sk, 8), _rand(rng, sq, 8)
+        o_exact, *ref = _given_o_head(q, k, v, do, 0.55, mask, np.zeros((sq, 8)))
+        for a, r in zip(mod.attention_head_backward(q, k, v, do, 0.55, mask, o=o_exact), ref):
+            np.testing.assert_allclose(a, r, rtol=1e-10, atol=1e-12)
+        err = 0.05 * _rand(rng, sq, 8)
+        o_pert, *ref = _given_o_head(q, k, v, do, 0.55, mask, err)
+        for a, r in zip(mod.attention_head_backward(q, k, v, do, 0.55, mask, o=o_pert), ref):
+            np.testing.assert_allclose(a, r, rtol=1e-10, atol=1e-12)
+    # dense, H = 4 over H_kv = 2
+    B, Sq, Sk, H, H_kv, D = 2, 5, 6, 4, 2, 8
+    q, do = _rand(rng, B, Sq, H, D), _rand(rng, B, Sq, H, D)
+    k, v = _rand(rng, B, Sk, H_kv, D), _rand(rng, B, Sk, H_kv, D)
+    err = 0.05 * _rand(rng, B, Sq, H, D)
+    o = np.zeros((B, Sq, H, D))
+    eq, ek, ev = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // H_kv)
+            o[b, :, h], gq, gk, gv = _given_o_head(q[b, :, h], k[b, :, g], v[b, :, g], do[b, :, h], 0.4, "causal_qend",
+                                                   err[b, :, h])
+            eq[b, :, h] = gq
+            ek[b, :, g] += gk
+            ev[b, :, g] += gv
+    for a, r in zip(mod.attention_backward_dense(q, k, v, do, 0.4, "causal_qend", o=o), (eq, ek, ev)):
+        np.testing.assert_allclose(a, r, rtol=1e-10, atol=1e-12)
+    # packed: two sequences whose query and key rows start at different offsets
+    cu_q, cu_k, H, H_kv = [0, 3, 7], [0, 5, 8], 2, 1
+    q, do = _rand(rng, 7, H, D), _rand(rng, 7, H, D)
+    k, v = _rand(rng, 8, H_kv, D), _rand(rng, 8, H_kv, D)
+    err = 0.05 * _rand(rng, 7, H, D)
+    o = np.zeros(q.shape)
+    eq, ek, ev = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(2):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        for h in range(H):
+            o[q0:q1, h], gq, gk, gv = _given_o_head(q[q0:q1, h], k[k0:k1, 0], v[k0:k1, 0], do[q0:q1, h], 0.4, "none",
+                                                    err[q0:q1, h])
+            eq[q0:q1, h] = gq
+            ek[k0:k1, 0] += gk
+            ev[k0:k1, 0] += gv
+    for a, r in zip(mod.attention_backward_varlen(q, k, v, do, cu_q, cu_k, 0.4, "none", o=o), (eq, ek, ev)):
+        np.testing.assert_allclose(a, r, rtol=1e-10, atol=1e-12)
+
+
 PINS = [pin_autograd, pin_library_sdpa, pin_finite_differences, pin_closed_forms, pin_invariants,
-        pin_rows_autograd, pin_rows_keyless_rows]
+        pin_rows_autograd, pin_rows_keyless_rows, pin_given_o]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -265,6 +328,11 @@ MUTATIONS = {
     "rows: block mask from row 0": ("vis = visible_keys(sq, sk, mask, rows=range(r0, r1))",
                                     "vis = visible_keys(sq, sk, mask, rows=range(0, r1 - r0))"),
     "rows: dK without scale": ("dk_rows += scale * (ds[:, k_rows].T @ q[r0:r1])", "dk_rows += ds[:, k_rows].T @ q[r0:r1]"),
+    "given O ignored": ("        delta = sum_o_do(o, do)\n", "        delta = (p * dp).sum(axis=1)\n"),
+    "given O without dO": ("        delta = sum_o_do(o, do)\n", "        delta = np.asarray(o).sum(axis=1)\n"),
+    "dense: given O of the K/V head": ("None if o is None else o[b, :, h])", "None if o is None else o[b, :, kvh])"),
+    "varlen: given O at the key rows": ("None if o is None else o[q0:q1, h])",
+                                        "None if o is None else o[k0:k0 + q1 - q0, h])"),
     "varlen key offset": ("gq, gk, gv = attention_head_backward(q[q0:q1, h], k[k0:k1, kvh], v[k0:k1, kvh]",
                           "gq, gk, gv = attention_head_backward(q[q0:q1, h], k[q0:q0 + k1 - k0, kvh], v[k0:k1, kvh]"),
 }
