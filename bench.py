@@ -233,7 +233,7 @@ def main():
         # the backward's inputs: dO (seeded), and O and LSE of the forward, computed once here
         from workloads import make_grad
         do_cpu = make_grad(inp.seed + 1, (inp.B, inp.Sq, inp.H, inp.D), inp.dtype)
-        bws = fmha.fmha_bwd_workspace_size(B, Sq, Sk, inp.H, inp.H_kv, inp.D, None)
+        bws = fmha.fmha_bwd_workspace_size(B, Sq, Sk, inp.H, inp.H_kv, inp.D, inp.dtype, None)
         for s_ in sets:
             lse = s_["lse"] if s_["lse"] is not None else torch.empty((B, inp.H, Sq), dtype=torch.float32, device=dev)
             fmha.check(fmha.fmha_fwd(s_["q"], s_["k"], s_["v"], s_["o"], lse, B, Sq, Sk, inp.H, inp.H_kv, inp.D,

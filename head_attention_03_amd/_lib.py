@@ -74,7 +74,7 @@ def load() -> ctypes.CDLL:
         ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.POINTER(fmha_varlen), ctypes.c_void_p, ctypes.c_size_t,
         ctypes.c_void_p]
     lib.fmha_bwd_workspace_size.restype = ctypes.c_size_t
-    lib.fmha_bwd_workspace_size.argtypes = [ctypes.c_int32] * 6 + [ctypes.POINTER(fmha_varlen)]
+    lib.fmha_bwd_workspace_size.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_int, ctypes.POINTER(fmha_varlen)]
     lib.fmha_status_string.restype = ctypes.c_char_p
     lib.fmha_status_string.argtypes = [ctypes.c_int]
     lib.fmha_version.restype = ctypes.c_int32
@@ -188,10 +188,11 @@ def fmha_bwd(q, k, v, o, dout, lse, dq, dk, dv, B: int, Sq: int, Sk: int, H: int
                             _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
-def fmha_bwd_workspace_size(B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int,
+def fmha_bwd_workspace_size(B: int, Sq: int, Sk: int, H: int, H_kv: int, D: int, dtype,
                             varlen: Optional[fmha_varlen] = None) -> int:
+    dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     vl = ctypes.byref(varlen) if varlen is not None else None
-    return int(load().fmha_bwd_workspace_size(int(B), int(Sq), int(Sk), int(H), int(H_kv), int(D), vl))
+    return int(load().fmha_bwd_workspace_size(int(B), int(Sq), int(Sk), int(H), int(H_kv), int(D), dtype, vl))
 
 
 def fmha_status_string(status: int) -> str:

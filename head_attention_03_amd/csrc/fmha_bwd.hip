@@ -711,6 +711,39 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
   for (int db = 0; db < NDB; ++db) store_block<DT>(acc[db], f, rout, at + 64 * db, h32);
 }
 
+// ------------------------------------------------------------------------------------------
+// e4m3 inputs: widened to bf16 in the workspace before the two kernels (exact: every e4m3fn
+// value, subnormals and NaN included, is a bf16 value).  Tensor blockIdx.y of the table, 16
+// input bytes per thread and grid-stride step.
+// ------------------------------------------------------------------------------------------
+constexpr int kWidenTensors = 5;  // q, o, dO, k, v
+constexpr int kWidenThreads = 256;
+
+struct Widen {
+  const void* src[kWidenTensors];
+  void* dst[kWidenTensors];
+  uint64_t n16[kWidenTensors];  // 16-byte chunks of e4m3 input (0: nothing to widen)
+};
+
+__global__ __launch_bounds__(kWidenThreads) void widen_e4m3_kernel(const Widen w) {
+  const int t = blockIdx.y;
+  const uint64_t n = w.n16[t];
+  const i32x4* src = (const i32x4*)w.src[t];
+  i32x4* dst = (i32x4*)w.dst[t];
+  for (uint64_t i = (uint64_t)blockIdx.x * kWidenThreads + threadIdx.x; i < n;
+       i += (uint64_t)gridDim.x * kWidenThreads) {
+    const i32x4 x = src[i];
+    int y[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {  // bytes 4h .. 4h+3 -> bf16 elements 4h .. 4h+3, in order
+      y[2 * h] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[h], 1.0f, false));
+      y[2 * h + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[h], 1.0f, true));
+    }
+    dst[2 * i] = i32x4{y[0], y[1], y[2], y[3]};
+    dst[2 * i + 1] = i32x4{y[4], y[5], y[6], y[7]};
+  }
+}
+
 template <int DT, int D>
 hipError_t launch(Params p, int n_q_tiles, int n_k_tiles, bool have_q, bool have_k, bool wide_k, bool wide_q,
                   hipStream_t stream) {
@@ -781,6 +814,31 @@ fmha_status plan(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int
   return FMHA_OK;
 }
 
+// Workspace layout: the row-statistics blocks first, then, for e4m3 inputs, bf16 copies of q, o,
+// dO, k and v (in that order), each at a 256-byte boundary.
+struct WsLayout {
+  size_t off[kWidenTensors];
+  uint64_t n16[kWidenTensors];  // 16-byte chunks of e4m3 input per copy (0: no copy)
+  size_t total;
+};
+
+inline WsLayout ws_layout(size_t stats_bytes, bool f8, int64_t rows_q, int64_t rows_k, int64_t H, int64_t H_kv,
+                          int64_t D) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const uint64_t elems[kWidenTensors] = {(uint64_t)(rows_q * H * D), (uint64_t)(rows_q * H * D),
+                                         (uint64_t)(rows_q * H * D), (uint64_t)(rows_k * H_kv * D),
+                                         (uint64_t)(rows_k * H_kv * D)};
+  WsLayout w;
+  size_t at = up(stats_bytes);
+  for (int t = 0; t < kWidenTensors; ++t) {
+    w.off[t] = at;
+    w.n16[t] = f8 ? elems[t] / 16 : 0;  // D is a multiple of 16
+    if (f8) at += up(2 * (size_t)elems[t]);
+  }
+  w.total = f8 ? at : stats_bytes;
+  return w;
+}
+
 }  // namespace bwd
 }  // namespace fmha
 
@@ -790,10 +848,15 @@ fmha_status plan(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int
 extern "C" {
 
 size_t fmha_bwd_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
-                               const fmha_varlen* varlen) {
-  fmha::bwd::Params p;
+                               fmha_dtype dtype, const fmha_varlen* varlen) {
+  using namespace fmha::bwd;
+  if ((int)dtype < 0 || (int)dtype > 2) return 0;
+  Params p;
   size_t bytes = 0;
-  return fmha::bwd::plan(B, Sq, Sk, H, H_kv, D, varlen, &p, &bytes) == FMHA_OK ? bytes : 0;
+  if (plan(B, Sq, Sk, H, H_kv, D, varlen, &p, &bytes) != FMHA_OK) return 0;
+  const int64_t rows_q = varlen ? varlen->total_length_q : (int64_t)B * Sq;
+  const int64_t rows_k = varlen ? varlen->total_length_k : (int64_t)B * Sk;
+  return ws_layout(bytes, dtype == FMHA_DTYPE_F8E4M3, rows_q, rows_k, H, H_kv, D).total;
 }
 
 fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -810,7 +873,7 @@ fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o,
   if (st != FMHA_OK) return st;
   if ((int)dtype < 0 || (int)dtype > 2) return FMHA_ERR_UNSUPPORTED;
   if ((int)mask < 0 || (int)mask > 3) return FMHA_ERR_UNSUPPORTED;
-  if (dtype == FMHA_DTYPE_F8E4M3) return FMHA_ERR_UNSUPPORTED;  // 16-bit types only
+  const bool f8 = dtype == FMHA_DTYPE_F8E4M3;
   const bool have_q = B > 0 && H > 0 && (packed ? varlen->total_length_q > 0 : Sq > 0);
   const bool have_k = B > 0 && H > 0 && (packed ? varlen->total_length_k > 0 : Sk > 0);
   if (have_q && (!q || !o || !dout || !lse || !dq)) return FMHA_ERR_NULL_POINTER;
@@ -821,12 +884,15 @@ fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o,
   if ((uintptr_t)lse & 3) return FMHA_ERR_MISALIGNED;
   if (!(scale > 0.0f) || !isfinite(scale)) return FMHA_ERR_INVALID_ARGUMENT;
   if (!have_q && !have_k) return FMHA_OK;
-  if (have_q || have_k) {
-    // the dK/dV kernel reads the statistics of every row it visits
-    if (have_q && !workspace) return FMHA_ERR_NULL_POINTER;
-    if ((uintptr_t)workspace & 15) return FMHA_ERR_MISALIGNED;
-    if (have_q && workspace_bytes < need) return FMHA_ERR_INVALID_ARGUMENT;
-  }
+  // the dK/dV kernel reads the statistics of every row it visits; e4m3 inputs are widened into
+  // the workspace first
+  const int64_t rows_q = packed ? varlen->total_length_q : (int64_t)B * Sq;
+  const int64_t rows_k = packed ? varlen->total_length_k : (int64_t)B * Sk;
+  const WsLayout wl = ws_layout(need, f8, have_q ? rows_q : 0, have_k ? rows_k : 0, H, H_kv, D);
+  const bool need_ws = have_q || f8;
+  if (need_ws && !workspace) return FMHA_ERR_NULL_POINTER;
+  if ((uintptr_t)workspace & 15) return FMHA_ERR_MISALIGNED;
+  if (need_ws && workspace_bytes < wl.total) return FMHA_ERR_INVALID_ARGUMENT;
   const int64_t n_q = (Sq + kQM - 1) / kQM;
   const int64_t n_k = (Sk + kKvN - 1) / kKvN;
   const int64_t lim = (int64_t)1 << 31;
@@ -856,14 +922,35 @@ fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o,
   // Streams whose byte offsets from the start of one sequence could pass 31 bits (one tile to
   // spare; packed batches bounded by their totals) take the kernels that place descriptors at
   // every streamed tile: K/V in the dQ kernel, Q/dO in the dK/dV kernel.
-  const int64_t rows_q = packed ? varlen->total_length_q : Sq;
-  const int64_t rows_k = packed ? varlen->total_length_k : Sk;
-  const bool wide_k = (rows_k + kKvN) * H_kv * D * 2 >= lim;
-  const bool wide_q = (rows_q + kKvN) * H * D * 2 >= lim;
+  const int64_t seq_q = packed ? varlen->total_length_q : Sq;
+  const int64_t seq_k = packed ? varlen->total_length_k : Sk;
+  const bool wide_k = (seq_k + kKvN) * H_kv * D * 2 >= lim;
+  const bool wide_q = (seq_q + kKvN) * H * D * 2 >= lim;
+
+  if (f8) {  // bf16 copies of the e4m3 inputs; the gradients are computed and written in bf16
+    char* ws = (char*)workspace;
+    const void* src[kWidenTensors] = {q, o, dout, k, v};
+    const void** use[kWidenTensors] = {&p.q, &p.o, &p.dout, &p.k, &p.v};
+    Widen w;
+    uint64_t most = 0;
+    for (int t = 0; t < kWidenTensors; ++t) {
+      w.src[t] = src[t];
+      w.dst[t] = ws + wl.off[t];
+      w.n16[t] = wl.n16[t];
+      if (wl.n16[t]) *use[t] = w.dst[t];
+      most = wl.n16[t] > most ? wl.n16[t] : most;
+    }
+    if (most) {
+      const uint64_t blocks = (most + kWidenThreads - 1) / kWidenThreads;
+      hipLaunchKernelGGL(widen_e4m3_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096), kWidenTensors),
+                         dim3(kWidenThreads), 0, stream, w);
+      if (hipGetLastError() != hipSuccess) return FMHA_ERR_HIP;
+    }
+  }
 
   hipError_t err = hipSuccess;
   const int nq = (int)n_q, nk = (int)n_k;
-  if (dtype == FMHA_DTYPE_BF16) {
+  if (dtype == FMHA_DTYPE_BF16 || f8) {
     if (D == 32) err = launch<fmha::kBF16, 32>(p, nq, nk, have_q, have_k, wide_k, wide_q, stream);
     if (D == 64) err = launch<fmha::kBF16, 64>(p, nq, nk, have_q, have_k, wide_k, wide_q, stream);
     if (D == 128) err = launch<fmha::kBF16, 128>(p, nq, nk, have_q, have_k, wide_k, wide_q, stream);

@@ -217,31 +217,41 @@ size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_
  *   dq           same shape as q, written
  *   dk, dv       same shapes as k and v, written (keys that no query sees get 0)
  *   B, Sq, Sk, H, H_kv, D, scale, mask, varlen   as in fmha_fwd
- *   dtype        FMHA_DTYPE_F16 or FMHA_DTYPE_BF16 (fp8: FMHA_ERR_UNSUPPORTED); every tensor
- *                above except lse has this type
+ *   dtype        FMHA_DTYPE_F16 or FMHA_DTYPE_BF16: every tensor above except lse has this type.
+ *                FMHA_DTYPE_F8E4M3 (the walk-through lists fp8 among the backward's types):
+ *                q, k, v, o and dout are e4m3 and dq, dk, dv are written as bf16, since a
+ *                3-bit mantissa without a scale (the pages give none for gradients) would flush
+ *                most gradient values.  The e4m3 values are taken as they are: scale is the
+ *                forward's (with q's and k's dequantisation scales folded in), o is fmha_fwd's
+ *                e4m3 output with o_scale 1, and a caller with per-tensor scales s_q, s_k, s_v,
+ *                s_do multiplies dq by s_do s_v / s_q, dk by s_do s_v / s_k and dv by s_do.  The
+ *                inputs are widened exactly to bf16 in the workspace and run the bf16 kernels.
  *   workspace    device memory owned by the caller, 16-byte aligned, at least
- *                fmha_bwd_workspace_size(...) bytes for the same shape; contents on entry do
- *                not matter (calls that overlap in time must not share it).  It holds 8 bytes of
- *                row statistics per query row and head, in blocks of 64 rows.
+ *                fmha_bwd_workspace_size(...) bytes for the same shape and dtype; contents on
+ *                entry do not matter (calls that overlap in time must not share it).  It holds
+ *                8 bytes of row statistics per query row and head, in blocks of 64 rows, and for
+ *                e4m3 the bf16 copies of q, o, dout, k and v.
  *   workspace_bytes  its size
- * The gradients are computed in fp32 with the probabilities and dS rounded to dtype for the
- * matrix cores, and written rounded to nearest even.
+ * The gradients are computed in fp32 with the probabilities and dS rounded to the 16-bit type
+ * for the matrix cores, and written rounded to nearest even.
  * Errors as fmha_fwd (o, dout, lse and dq are required when there are query rows; k, v, dk and
  * dv when there are keys; all but lse 16-byte aligned), and: workspace NULL ->
  * FMHA_ERR_NULL_POINTER, not 16-byte aligned -> FMHA_ERR_MISALIGNED, smaller than needed ->
- * FMHA_ERR_INVALID_ARGUMENT (checked when there are query rows).  With query rows but no keys dq is zeroed; with keys but no query rows
- * dk and dv are zeroed.  Rows and keys outside the sequences are never touched.
+ * FMHA_ERR_INVALID_ARGUMENT (checked when there are query rows, and for e4m3 whenever there is
+ * work).  With query rows but no keys dq is zeroed; with keys but no query rows dk and dv are
+ * zeroed.  Rows and keys outside the sequences are never touched.
  */
 fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                      void* dq, void* dk, void* dv, int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv,
                      int32_t D, float scale, fmha_mask mask, fmha_dtype dtype, const fmha_varlen* varlen,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes fmha_bwd needs for this shape (host arithmetic only; the packed form reads
- * only varlen->total_length_q).  Returns 0 for an invalid shape, or one too large for the
- * kernels' 32-bit offsets. */
+/* Workspace bytes fmha_bwd needs for this shape and dtype (host arithmetic only; the packed
+ * form reads only varlen->total_length_q and total_length_k).  Returns 0 for an invalid shape or
+ * dtype, or one too large for the kernels' 32-bit offsets (and for fp16/bf16 with no query rows,
+ * where no workspace is used). */
 size_t fmha_bwd_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D,
-                               const fmha_varlen* varlen);
+                               fmha_dtype dtype, const fmha_varlen* varlen);
 
 /* Paged K/V cache: fixed-size pages shared by all sequences, addressed through a block table.
  * This is the KV-cache-block layout that the sm120 article's TODO section names as the core of

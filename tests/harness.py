@@ -195,6 +195,11 @@ BWD_SCALE_FLOOR = 2.0 ** -8
 GRAD_SENTINEL = {"f16": 0x7BAD, "bf16": 0x4B1D}
 
 
+def grad_dtype(dtype: str) -> str:
+    """Type fmha_bwd writes the gradients in: the input type, bf16 for e4m3 inputs."""
+    return "bf16" if dtype == "f8e4m3" else dtype
+
+
 def oracle_forward_inputs(inp):
     """O (rounded to the input type) and fp32 LSE from the oracle, as the backward's inputs."""
     if isinstance(inp, VarlenInputs):
@@ -215,8 +220,9 @@ def run_bwd_dense(inp: DenseInputs, do: torch.Tensor, o: torch.Tensor, lse: np.n
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     o_d, do_d = o.to(dev), do.to(dev)
     lse_d = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to(dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    need = fmha.fmha_bwd_workspace_size(inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D, None)
+    gt = TORCH_DTYPES[grad_dtype(inp.dtype)]
+    dq, dk, dv = (torch.empty(t.shape, dtype=gt, device=dev) for t in (q, k, v))
+    need = fmha.fmha_bwd_workspace_size(inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D, inp.dtype, None)
     ws = _bwd_workspace(need)
     st = fmha.fmha_bwd(q, k, v, o_d, do_d, lse_d, dq, dk, dv, inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D,
                        inp.kernel_scale, inp.mask, inp.dtype, None, ws, need,
@@ -236,14 +242,15 @@ def run_bwd_varlen(inp: VarlenInputs, do_buf: torch.Tensor, o: torch.Tensor, lse
     o_buf[inp.pad_q:] = o
     o_buf, do_d = o_buf.to(dev), do_buf.to(dev)
     lse_d = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32).reshape(inp.H, -1)).to(dev)
-    bits = GRAD_SENTINEL[inp.dtype]
-    dq = torch.full(q_buf.shape, bits, dtype=torch.int16).view(TORCH_DTYPES[inp.dtype]).to(dev)
-    dk = torch.full(k_buf.shape, bits, dtype=torch.int16).view(TORCH_DTYPES[inp.dtype]).to(dev)
-    dv = torch.full(v_buf.shape, bits, dtype=torch.int16).view(TORCH_DTYPES[inp.dtype]).to(dev)
+    gd = grad_dtype(inp.dtype)
+    bits = GRAD_SENTINEL[gd]
+    dq = torch.full(q_buf.shape, bits, dtype=torch.int16).view(TORCH_DTYPES[gd]).to(dev)
+    dk = torch.full(k_buf.shape, bits, dtype=torch.int16).view(TORCH_DTYPES[gd]).to(dev)
+    dv = torch.full(v_buf.shape, bits, dtype=torch.int16).view(TORCH_DTYPES[gd]).to(dev)
     cu_q = torch.from_numpy(inp.cu_q).to(dev)
     cu_k = torch.from_numpy(inp.cu_k).to(dev)
     vl = fmha.make_varlen(cu_q, cu_k, inp.total_q, inp.total_k)
-    need = fmha.fmha_bwd_workspace_size(inp.B, inp.max_q, inp.max_k, inp.H, inp.H_kv, inp.D, vl)
+    need = fmha.fmha_bwd_workspace_size(inp.B, inp.max_q, inp.max_k, inp.H, inp.H_kv, inp.D, inp.dtype, vl)
     ws = _bwd_workspace(need)
     pq, pk = inp.pad_q, inp.pad_k
     st = fmha.fmha_bwd(q_buf[pq:], k_buf[pk:], v_buf[pk:], o_buf[pq:], do_d[pq:], lse_d, dq[pq:], dk[pk:], dv[pk:],

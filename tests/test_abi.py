@@ -186,11 +186,14 @@ def call_bwd(**kw):
     (dict(varlen=fmha.make_varlen(P, None, 16, 16)), 1), (dict(varlen=fmha.make_varlen(None, None, 16, 16)), 1),
     (dict(B=-1), 2), (dict(Sk=-1), 2), (dict(H=3, H_kv=2), 2), (dict(H_kv=0), 2), (dict(D=48), 2),
     (dict(varlen=fmha.make_varlen(P, P, 16, -1)), 2),
-    (dict(dtype="f8e4m3"), 3), (dict(dtype=3), 3), (dict(mask=4), 3), (dict(mask=-1), 3),
+    (dict(dtype=3), 3), (dict(mask=4), 3), (dict(mask=-1), 3),
     (dict(H=70000, H_kv=70000, Sq=1, Sk=1), 3), (dict(Sq=1 << 22, H=64, H_kv=64, D=128), 3),
     (dict(q=P + 2), 4), (dict(dq=P + 8), 4), (dict(dk=P + 4), 4), (dict(dout=P + 2), 4), (dict(lse=P + 2), 4),
     (dict(workspace=P + 8), 4),
     (dict(scale=0.0), 5), (dict(scale=float("inf")), 5), (dict(scale=float("nan")), 5), (dict(workspace_bytes=0), 5),
+    # e4m3: the statistics alone are not enough (the bf16 copies of the inputs follow them)
+    (dict(dtype="f8e4m3", workspace_bytes=2 * 512), 5), (dict(dtype="f8e4m3", q=None), 1),
+    (dict(dtype="f8e4m3", o=P + 8), 4),
     # no query rows: the q-side pointers and the workspace are not needed; no keys: the k side
     (dict(B=0, q=None, k=None, workspace=None), 0),
 ])
@@ -200,18 +203,34 @@ def test_bwd_rejects_bad_arguments(kw, status):
 
 def test_bwd_workspace_size():
     # dense: 512 bytes per 64-row block of every (sequence, head)
-    assert fmha.fmha_bwd_workspace_size(4, 2048, 2048, 16, 16, 128, None) == 4 * 16 * 32 * 512
-    assert fmha.fmha_bwd_workspace_size(2, 65, 10, 3, 1, 64, None) == 2 * 3 * 2 * 512
-    assert fmha.fmha_bwd_workspace_size(1, 0, 10, 3, 1, 64, None) == 0
+    assert fmha.fmha_bwd_workspace_size(4, 2048, 2048, 16, 16, 128, "bf16", None) == 4 * 16 * 32 * 512
+    assert fmha.fmha_bwd_workspace_size(2, 65, 10, 3, 1, 64, "f16", None) == 2 * 3 * 2 * 512
+    assert fmha.fmha_bwd_workspace_size(1, 0, 10, 3, 1, 64, "bf16", None) == 0
     # packed: per head, floor(total_q / 64) + B + 1 blocks (sequences start on their own block)
     vl = fmha.make_varlen(P, P, 1000, 50)
-    assert fmha.fmha_bwd_workspace_size(5, 400, 30, 4, 2, 128, vl) == 4 * (1000 // 64 + 5 + 1) * 512
-    # invalid shapes
-    assert fmha.fmha_bwd_workspace_size(1, 16, 16, 3, 2, 64, None) == 0
-    assert fmha.fmha_bwd_workspace_size(1, 16, 16, 2, 2, 48, None) == 0
+    assert fmha.fmha_bwd_workspace_size(5, 400, 30, 4, 2, 128, "bf16", vl) == 4 * (1000 // 64 + 5 + 1) * 512
+    # e4m3: the statistics, then bf16 copies of q, o, dO (rows_q x H x D) and k, v (rows_k x H_kv x D),
+    # each starting on a 256-byte boundary
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    stats = 2 * 3 * 2 * 512
+    assert fmha.fmha_bwd_workspace_size(2, 65, 10, 3, 1, 64, "f8e4m3", None) == (
+        up(stats) + 3 * up(2 * 2 * 65 * 3 * 64) + 2 * up(2 * 2 * 10 * 1 * 64))
+    assert fmha.fmha_bwd_workspace_size(5, 400, 30, 4, 2, 128, "f8e4m3", vl) == (
+        up(4 * (1000 // 64 + 5 + 1) * 512) + 3 * up(2 * 1000 * 4 * 128) + 2 * up(2 * 50 * 2 * 128))
+    # e4m3 with no query rows still needs the copies of k and v
+    assert fmha.fmha_bwd_workspace_size(1, 0, 10, 3, 1, 64, "f8e4m3", None) == 2 * up(2 * 10 * 64)
+    # invalid shapes and dtypes
+    assert fmha.fmha_bwd_workspace_size(1, 16, 16, 3, 2, 64, "bf16", None) == 0
+    assert fmha.fmha_bwd_workspace_size(1, 16, 16, 2, 2, 48, "bf16", None) == 0
+    assert fmha.fmha_bwd_workspace_size(1, 16, 16, 2, 2, 64, 7, None) == 0
     # one byte short of the size is rejected
-    need = fmha.fmha_bwd_workspace_size(1, 16, 16, 2, 1, 64, None)
+    need = fmha.fmha_bwd_workspace_size(1, 16, 16, 2, 1, 64, "bf16", None)
     assert call_bwd(workspace_bytes=need - 1) == 5
+    need8 = fmha.fmha_bwd_workspace_size(1, 16, 16, 2, 1, 64, "f8e4m3", None)
+    assert need8 > need
+    assert call_bwd(dtype="f8e4m3", workspace_bytes=need8 - 1) == 5
+    # e4m3 with keys but no query rows: the workspace is required
+    assert call_bwd(dtype="f8e4m3", Sq=0, q=None, workspace=None) == 1
 
 
 # ----------------------------------------------------------------------------------------------

@@ -134,6 +134,109 @@ def test_bwd_varlen(case):
         assert np.all(to_bits(t[:pad]) == s)
 
 
+# ----------------------------------------------------------------------------------------------
+# e4m3 inputs: q, k, v, O and dO in e4m3, taken at face value (scale = the forward's kernel scale,
+# O written with o_scale 1); the gradients come back in bf16.  The oracle takes delta from the same
+# e4m3 O the kernels receive (oracle.attention_backward_* with o=...), so the coarse O is part of
+# the expected value, not of the error; the kernels then compute as for bf16 inputs (exact
+# widening), and the bf16 tolerance applies.
+# ----------------------------------------------------------------------------------------------
+def _face(t):
+    return oracle.decode(to_bits(t), "f8e4m3")
+
+
+def _e4m3(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).clamp(-448, 448).to(torch.float8_e4m3fn)
+
+
+def _check_f8_dense(name, inp, do, o=None, lse=None):
+    log(f"[case] bwd e4m3 {name} B={inp.B} Sq={inp.Sq} Sk={inp.Sk} H={inp.H} H_kv={inp.H_kv} D={inp.D} "
+        f"mask={inp.mask} seed={inp.seed}")
+    q8, k8, v8, do8 = (_face(t) for t in (inp.q, inp.k, inp.v, do))
+    if o is None:
+        o_ex, lse = oracle.attention_dense(q8, k8, v8, inp.kernel_scale, inp.mask)
+        o, lse = _e4m3(o_ex), lse.astype(np.float32)
+    st, dq, dk, dv = run_bwd_dense(inp, do, o, lse)
+    assert st == 0
+    assert dq.dtype == torch.bfloat16 and dk.dtype == torch.bfloat16 and dv.dtype == torch.bfloat16
+    eq, ek, ev = oracle.attention_backward_dense(q8, k8, v8, do8, inp.kernel_scale, inp.mask, o=_face(o))
+    compare_grad(f"e4m3 {name} dQ", dq, "bf16", eq)
+    compare_grad(f"e4m3 {name} dK", dk, "bf16", ek)
+    compare_grad(f"e4m3 {name} dV", dv, "bf16", ev)
+
+
+F8_DENSE = [
+    # (B, Sq, Sk, H, H_kv, D, mask)
+    (1, 128, 128, 2, 2, 64, "none"),             # one tile of each kernel
+    (2, 300, 300, 4, 2, 128, "causal_qbegin"),   # ragged tiles, GQA group of 2
+    (1, 257, 513, 4, 4, 64, "causal_qend"),      # more keys than queries
+    (2, 513, 200, 2, 1, 128, "causal_qend"),     # MQA; rows without keys
+    (1, 1000, 1000, 2, 2, 32, "residual"),       # D = 32, several tiles both ways
+]
+
+
+@pytest.mark.parametrize("case", F8_DENSE, ids=lambda c: f"B{c[0]}-q{c[1]}-k{c[2]}-H{c[3]}/{c[4]}-D{c[5]}-{c[6]}")
+def test_bwd_e4m3_dense(case):
+    B, Sq, Sk, H, H_kv, D, mask = case
+    inp = make_dense(5100 + Sq + 7 * Sk, B, Sq, Sk, H, H_kv, D, "f8e4m3", mask=mask)
+    do = make_grad(5200 + Sq + 7 * Sk, (B, Sq, H, D), "f8e4m3")
+    _check_f8_dense(str(case), inp, do)
+
+
+def test_bwd_e4m3_end_to_end_from_hip_forward():
+    # O (e4m3, o_scale 1) and LSE from the fp8 fmha_fwd, as a training step would feed them
+    import head_attention_03_amd as fmha
+    dev = torch.device("cuda:0")
+    inp = make_dense(5300, 2, 384, 448, 8, 2, 128, "f8e4m3", mask="causal_qbegin")
+    do = make_grad(5301, (2, 384, 8, 128), "f8e4m3")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((2, 8, 384), dtype=torch.float32, device=dev)
+    st = fmha.fmha_fwd(q, k, v, o, lse, 2, 384, 448, 8, 2, 128, inp.kernel_scale, inp.mask, "f8e4m3", 1.0, None,
+                       torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert st == 0
+    _check_f8_dense("end-to-end", inp, do, o=o.cpu(), lse=lse.cpu().numpy())
+
+
+def test_bwd_e4m3_varlen():
+    lq, lk, H, H_kv, D, mask = [100, 1, 333, 64], [180, 50, 333, 17], 4, 2, 128, "causal_qend"
+    inp = make_varlen(5400, lq, lk, H, H_kv, D, "f8e4m3", mask=mask)
+    log(f"[case] bwd e4m3 varlen {lq} {lk} H={H}/{H_kv} D={D} {mask} seed={inp.seed}")
+    do_buf = make_grad(5401, tuple(inp.q_buf.shape), "f8e4m3")
+    q8, k8, v8 = (_face(getattr(inp, w)) for w in ("q", "k", "v"))
+    do8 = _face(do_buf[inp.pad_q:])
+    o_ex, lse = oracle.attention_varlen(q8, k8, v8, inp.cu_q, inp.cu_k, inp.kernel_scale, mask)
+    o = _e4m3(o_ex)
+    st, dq, dk, dv = run_bwd_varlen(inp, do_buf, o, lse.astype(np.float32))
+    assert st == 0
+    eq, ek, ev = oracle.attention_backward_varlen(q8, k8, v8, do8, inp.cu_q, inp.cu_k, inp.kernel_scale, mask,
+                                                  o=_face(o))
+    compare_grad("e4m3 varlen dQ", dq[inp.pad_q:], "bf16", eq)
+    compare_grad("e4m3 varlen dK", dk[inp.pad_k:], "bf16", ek)
+    compare_grad("e4m3 varlen dV", dv[inp.pad_k:], "bf16", ev)
+    s = GRAD_SENTINEL["bf16"]
+    for t, pad in ((dq, inp.pad_q), (dk, inp.pad_k), (dv, inp.pad_k)):
+        assert np.all(to_bits(t[:pad]) == s)
+
+
+def test_bwd_e4m3_no_query_rows():
+    # keys but no query rows: dK = dV = 0 in bf16 (the workspace still takes the widened K and V)
+    import head_attention_03_amd as fmha
+    dev = torch.device("cuda:0")
+    k = torch.randn(1, 100, 2, 64).to(torch.float8_e4m3fn).to(dev)
+    dk = torch.full((1, 100, 2, 64), 7.0, dtype=torch.bfloat16, device=dev)
+    dv = torch.full((1, 100, 2, 64), 7.0, dtype=torch.bfloat16, device=dev)
+    need = fmha.fmha_bwd_workspace_size(1, 0, 100, 2, 2, 64, "f8e4m3", None)
+    assert need == 2 * 2 * 100 * 2 * 64
+    ws = torch.empty(need // 4, dtype=torch.float32, device=dev)
+    st = fmha.fmha_bwd(None, k, k, None, None, None, None, dk, dv, 1, 0, 100, 2, 2, 64, 0.125, "causal_qbegin",
+                       "f8e4m3", None, ws, need, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
 def test_bwd_bitwise_repeatable():
     inp = make_dense(4800, 2, 520, 520, 4, 2, 128, "bf16", mask="causal_qbegin")
     do = make_grad(4801, (2, 520, 4, 128), "bf16")
@@ -203,7 +306,7 @@ def test_bwd_tensors_beyond_2gib():
                        None, torch.cuda.current_stream())
     assert st == 0, fmha.fmha_status_string(st)
     dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
-    need = fmha.fmha_bwd_workspace_size(1, S, S, H, H, D, None)
+    need = fmha.fmha_bwd_workspace_size(1, S, S, H, H, D, inp.dtype, None)
     ws = torch.full((max(need, 16) // 4,), float("nan"), dtype=torch.float32, device=dev)
     st = fmha.fmha_bwd(inp.q, inp.k, inp.v, o, do, lse, dq, dk, dv, 1, S, S, H, H, D, inp.kernel_scale, inp.mask,
                        inp.dtype, None, ws, need, torch.cuda.current_stream())

@@ -95,7 +95,7 @@ def test_bwd_captured():
                          inp.dtype, 1.0, None, torch.cuda.current_stream()) == 0
     do = make_grad(7004, tuple(q.shape), "bf16").to(dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    need = fmha.fmha_bwd_workspace_size(inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D, None)
+    need = fmha.fmha_bwd_workspace_size(inp.B, inp.Sq, inp.Sk, inp.H, inp.H_kv, inp.D, inp.dtype, None)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     _replays_match("fmha_bwd", lambda s: fmha.fmha_bwd(q, k, v, o, do, lse, dq, dk, dv, inp.B, inp.Sq, inp.Sk, inp.H,
