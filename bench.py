@@ -23,7 +23,9 @@ bytes; bf16 queries and output).
 --config 7 is the backward pass (one fmha_bwd call per step: its two kernels, dQ with the row
 statistics, then dK/dV) of the prefill shape, with O and LSE from fmha_fwd computed once before timing.  Its
 FLOPs follow the 5-matmul count (S, dP, dV, dQ, dK: 2.5 times the forward's 4*B*H*Sq*Sk*D,
-halved for causal masks); the roofline is taken over the whole call.
+halved for causal masks); the roofline is taken over the whole call.  --config 10 is the same backward
+with e4m3 inputs (O from the fp8 forward, an e4m3 dO) and bf16 gradients: the inputs are widened to
+bf16 in the workspace by a third kernel, so its peak is the bf16 one.
 """
 from __future__ import annotations
 
@@ -238,8 +240,10 @@ def main():
             lse = s_["lse"] if s_["lse"] is not None else torch.empty((B, inp.H, Sq), dtype=torch.float32, device=dev)
             fmha.check(fmha.fmha_fwd(s_["q"], s_["k"], s_["v"], s_["o"], lse, B, Sq, Sk, inp.H, inp.H_kv, inp.D,
                                      inp.kernel_scale, inp.mask, inp.dtype, 1.0, None, stream))
-            s_.update(lse=lse, do=do_cpu.to(dev), dq=torch.empty_like(s_["q"]), dk=torch.empty_like(s_["k"]),
-                      dv=torch.empty_like(s_["v"]))
+            gt = torch.bfloat16 if inp.dtype == "f8e4m3" else s_["q"].dtype  # e4m3 inputs: bf16 gradients
+            s_.update(lse=lse, do=do_cpu.to(dev), dq=torch.empty(s_["q"].shape, dtype=gt, device=dev),
+                      dk=torch.empty(s_["k"].shape, dtype=gt, device=dev),
+                      dv=torch.empty(s_["v"].shape, dtype=gt, device=dev))
         bw = torch.empty(max(bws, 16), dtype=torch.uint8, device=dev)
         flops_step = BWD_FLOP_FACTOR * flops_step
         torch.cuda.synchronize()
@@ -291,11 +295,20 @@ def main():
 
     value = flops_step * args.steps / elapsed / 1e12
     achieved = flops_step / len(masks) / avg_launch_s / 1e12
-    peak = PEAK_TFLOPS[inp.dtype]
+    # the backward computes e4m3 inputs on the bf16 matrix cores (after an exact widening)
+    peak = PEAK_TFLOPS["bf16" if bwd else inp.dtype]
     traffic = measured_traffic(c)
-    metric, unit, bound = "FMHA fwd TFLOP/s and % of MI355X dense MFMA peak (bf16, D=128, causal)", "TFLOP/s", "mfma"
+    # the label names the workload's type, head dim and masks (the prefill workload's reads
+    # "(bf16, D=128, causal)")
+    mask_txt = " + ".join("causal" if m.startswith("causal") else ("no mask" if m == "none" else m) for m in masks)
+    type_txt = {"f16": "f16", "bf16": "bf16", "f8e4m3": "fp8 e4m3"}[inp.dtype]
+    metric = f"FMHA fwd TFLOP/s and % of MI355X dense MFMA peak ({type_txt}, D={inp.D}, {mask_txt})"
+    unit, bound = "TFLOP/s", "mfma"
     if bwd:
         metric = "FMHA bwd TFLOP/s (5-matmul count) and % of MI355X dense MFMA peak (bf16, D=128, causal)"
+        if inp.dtype == "f8e4m3":
+            metric = ("FMHA bwd TFLOP/s (5-matmul count) and % of MI355X dense bf16 MFMA peak (e4m3 inputs widened "
+                      "to bf16, D=128, causal)")
     tflops = value
     if splitkv:  # HBM-bound: GB/s of algorithmic bytes
         bytes_step = algorithmic_bytes(inp, want_lse)
@@ -326,7 +339,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f16": "f16", "bf16": "bf16", "f8e4m3": "fp8_e4m3"}[inp.dtype],
+        # the arithmetic type: the e4m3 backward computes on widened bf16 copies
+        "dtype": "bf16" if bwd and inp.dtype == "f8e4m3" else {"f16": "f16", "bf16": "bf16", "f8e4m3": "fp8_e4m3"}[inp.dtype],
         "data": "synthetic (seeded N(0,1))",
         "config": cfg,
         "pct_of_peak": round(100.0 * value / peak, 2),

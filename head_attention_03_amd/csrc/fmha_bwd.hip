@@ -713,11 +713,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
 
 // ------------------------------------------------------------------------------------------
 // e4m3 inputs: widened to bf16 in the workspace before the two kernels (exact: every e4m3fn
-// value, subnormals and NaN included, is a bf16 value).  Tensor blockIdx.y of the table, 16
-// input bytes per thread and grid-stride step.
+// value, subnormals and NaN included, is a bf16 value).  Tensor blockIdx.y of the table.  A wave
+// takes 2 KiB of input per step as four 512-byte rows, lane j bytes 8j .. 8j + 7 of each, and
+// writes each row's 1 KiB of bf16 with one contiguous store; a tail of fewer than 2 KiB goes 16
+// bytes per thread.
 // ------------------------------------------------------------------------------------------
 constexpr int kWidenTensors = 5;  // q, o, dO, k, v
 constexpr int kWidenThreads = 256;
+constexpr int kWidenRows = 4;     // 512-byte input rows per wave and step
 
 struct Widen {
   const void* src[kWidenTensors];
@@ -725,22 +728,35 @@ struct Widen {
   uint64_t n16[kWidenTensors];  // 16-byte chunks of e4m3 input (0: nothing to widen)
 };
 
+template <bool HI>
+__device__ inline int widen2(int x) {  // e4m3 bytes 2 HI, 2 HI + 1 of x -> two bf16
+  return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HI));
+}
+
 __global__ __launch_bounds__(kWidenThreads) void widen_e4m3_kernel(const Widen w) {
   const int t = blockIdx.y;
   const uint64_t n = w.n16[t];
-  const i32x4* src = (const i32x4*)w.src[t];
-  i32x4* dst = (i32x4*)w.dst[t];
-  for (uint64_t i = (uint64_t)blockIdx.x * kWidenThreads + threadIdx.x; i < n;
-       i += (uint64_t)gridDim.x * kWidenThreads) {
-    const i32x4 x = src[i];
-    int y[8];
+  const char* src = (const char*)w.src[t];
+  char* dst = (char*)w.dst[t];
+  const int lane = threadIdx.x & 63;
+  const uint64_t n_steps = n / (kWidenRows * 32);  // whole 2 KiB input steps
+  const uint64_t waves = (uint64_t)gridDim.x * (kWidenThreads / 64);
+  for (uint64_t u = ((uint64_t)blockIdx.x * kWidenThreads + threadIdx.x) / 64; u < n_steps; u += waves) {
+    i32x2 x[kWidenRows];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {  // bytes 4h .. 4h+3 -> bf16 elements 4h .. 4h+3, in order
-      y[2 * h] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[h], 1.0f, false));
-      y[2 * h + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[h], 1.0f, true));
-    }
-    dst[2 * i] = i32x4{y[0], y[1], y[2], y[3]};
-    dst[2 * i + 1] = i32x4{y[4], y[5], y[6], y[7]};
+    for (int r = 0; r < kWidenRows; ++r) x[r] = *(const i32x2*)(src + (u * kWidenRows + r) * 512 + 8 * lane);
+#pragma unroll
+    for (int r = 0; r < kWidenRows; ++r)
+      *(i32x4*)(dst + (u * kWidenRows + r) * 1024 + 16 * lane) =
+          i32x4{widen2<false>(x[r][0]), widen2<true>(x[r][0]), widen2<false>(x[r][1]), widen2<true>(x[r][1])};
+  }
+  const i32x4* src16 = (const i32x4*)src;
+  i32x4* dst16 = (i32x4*)dst;
+  for (uint64_t i = n_steps * kWidenRows * 32 + (uint64_t)blockIdx.x * kWidenThreads + threadIdx.x; i < n;
+       i += (uint64_t)gridDim.x * kWidenThreads) {
+    const i32x4 x = src16[i];
+    dst16[2 * i] = i32x4{widen2<false>(x[0]), widen2<true>(x[0]), widen2<false>(x[1]), widen2<true>(x[1])};
+    dst16[2 * i + 1] = i32x4{widen2<false>(x[2]), widen2<true>(x[2]), widen2<false>(x[3]), widen2<true>(x[3])};
   }
 }
 
@@ -940,9 +956,9 @@ fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o,
       if (wl.n16[t]) *use[t] = w.dst[t];
       most = wl.n16[t] > most ? wl.n16[t] : most;
     }
-    if (most) {
-      const uint64_t blocks = (most + kWidenThreads - 1) / kWidenThreads;
-      hipLaunchKernelGGL(widen_e4m3_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096), kWidenTensors),
+    if (most) {  // one wave per 2 KiB step of the largest tensor, at most 2048 workgroups per tensor
+      const uint64_t blocks = (most + 4 * kWidenRows * 32 - 1) / (4 * kWidenRows * 32);
+      hipLaunchKernelGGL(widen_e4m3_kernel, dim3((unsigned)(blocks < 2048 ? blocks : 2048), kWidenTensors),
                          dim3(kWidenThreads), 0, stream, w);
       if (hipGetLastError() != hipSuccess) return FMHA_ERR_HIP;
     }

@@ -589,8 +589,8 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
       }
     } else {
       // fp8: the S^T MFMAs first, then the PV MFMAs, so the tile's row max (in the softmax code,
-      // free to move here) runs on the vector ALU while the PV products execute: in fp8 the
-      // softmax phase, not the matrix phase, sets the step.
+      // free to move here) runs on the vector ALU while the PV products execute: an fp8 phase
+      // has half the MFMA time of a 16-bit one per key, so the vector work beside it matters more.
 #pragma unroll
       for (int i = 0; i < NQK; ++i) qk_mma(ka, kb, i);
 #pragma unroll

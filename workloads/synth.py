@@ -444,7 +444,7 @@ def make_varlen(seed: int, seqlens_q: Sequence[int], seqlens_k: Sequence[int], H
 # The measured workloads.  Config 4 is run twice on the same inputs (residual, then causal-qend);
 # config 6 is the split-KV (decode) entry point's workload; config 7 is the backward pass (fmha_bwd)
 # of config 2's shape; config 8 is config 6 over a paged cache (fmha_fwd_splitkv_paged), config 9
-# the same over an e4m3 cache.
+# the same over an e4m3 cache; config 10 is config 7 with e4m3 inputs.
 CONFIGS = {
     1: dict(name="tiny dense fp16 D64 no mask", kind="dense", B=1, H=2, H_kv=2, Sq=128, Sk=128, D=64,
             dtype="f16", mask="none", lse=False, o_scale=1.0),
@@ -472,6 +472,11 @@ CONFIGS = {
     9: dict(name="paged decode GQA bf16 D128 over an e4m3 cache, 1 token vs 8192 keys, 128-key pages",
             kind="paged", entry="splitkv_paged", B=16, H=32, H_kv=8, Sq=1, Sk=8192, D=128, page_size=128,
             dtype="bf16", kv_dtype="f8e4m3", mask="none", lse=True, o_scale=1.0),
+    # Backward of the prefill shape with e4m3 inputs (O from the fp8 forward with o_scale 1, an
+    # e4m3 dO), gradients in bf16.
+    10: dict(name="backward of prefill causal-qbegin D128, e4m3 inputs, bf16 gradients", kind="dense", entry="bwd",
+             B=4, H=16, H_kv=16, Sq=2048, Sk=2048, D=128, dtype="f8e4m3", mask="causal_qbegin", lse=True,
+             o_scale=1.0),
 }
 
 
