@@ -199,6 +199,34 @@ def test_bwd_e4m3_end_to_end_from_hip_forward():
     _check_f8_dense("end-to-end", inp, do, o=o.cpu(), lse=lse.cpu().numpy())
 
 
+def test_bwd_e4m3_prefill_full_size_sampled():
+    # the e4m3 backward workload: B4 H16 2048 x 2048 D128 causal-qbegin, O and LSE from the fp8
+    # forward (o_scale 1); dQ of heads 0 and 13 of sequence 0 and dK, dV of the same heads, whole
+    import head_attention_03_amd as fmha
+    dev = torch.device("cuda:0")
+    B, S, H, D = 4, 2048, 16, 128
+    inp = make_dense(5500, B, S, S, H, H, D, "f8e4m3", mask="causal_qbegin")
+    do = make_grad(5501, (B, S, H, D), "f8e4m3")
+    log(f"[case] bwd e4m3 full size B={B} S={S} H={H} D={D} causal_qbegin seed=5500")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    st = fmha.fmha_fwd(q, k, v, o, lse, B, S, S, H, H, D, inp.kernel_scale, inp.mask, "f8e4m3", 1.0, None,
+                       torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert st == 0
+    o_cpu, lse_cpu = o.cpu(), lse.cpu().numpy()
+    st, dq, dk, dv = run_bwd_dense(inp, do, o_cpu, lse_cpu)
+    assert st == 0
+    q8, k8, v8, do8, o8 = (_face(t)[0] for t in (inp.q, inp.k, inp.v, do, o_cpu))
+    for h in (0, 13):
+        gq, gk, gv = oracle.attention_head_backward(q8[:, h], k8[:, h], v8[:, h], do8[:, h], inp.kernel_scale,
+                                                    inp.mask, o=o8[:, h])
+        compare_grad(f"e4m3 full size dQ head {h}", dq[0, :, h], "bf16", gq)
+        compare_grad(f"e4m3 full size dK head {h}", dk[0, :, h], "bf16", gk)
+        compare_grad(f"e4m3 full size dV head {h}", dv[0, :, h], "bf16", gv)
+
+
 def test_bwd_e4m3_varlen():
     lq, lk, H, H_kv, D, mask = [100, 1, 333, 64], [180, 50, 333, 17], 4, 2, 128, "causal_qend"
     inp = make_varlen(5400, lq, lk, H, H_kv, D, "f8e4m3", mask=mask)
