@@ -827,19 +827,28 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   };
 
   // ---- prologue: Q of the first item, L(0) (K of its first tile and the zero V(-1)) and L(1)
-  // into stages 0 and 1; the phases start once Q and L(0) are in (L(1) is waited for at the
-  // end of phase 1, like every later tile).  Then the block takes the second item's Q rows.
-  load_q(0);
+  // into stages 0 and 1; the phases start once L(0) and group A's Q rows are in (L(1) is waited
+  // for at the end of phase 1, like every later tile).  Group B runs no matrix work before phase
+  // 1, so its waves request their Q rows after L(0) and read them at the end of phase 0: the
+  // first phase waits for half the Q bytes.  Then each block takes the second item's Q rows.
+  const bool grp_b = wave_u >= 4;  // (scalar: the branches below hold no accumulators)
+  if (!grp_b) load_q(0);
   no_work(P0{});
   no_work(P1{});
   advance();
+  if (grp_b) load_q(0);
   no_work(P0{});
   no_work(P1{});
   advance();
-  wait_vmcnt<NBLK / 8>();
+  if (grp_b)
+    wait_vmcnt<NBLK / 8 + QBLK>();  // L(0); Q and L(1) may be in flight
+  else
+    wait_vmcnt<NBLK / 8>();  // Q and L(0)
   phase_barrier();
-  read_q();
-  if (n_items > 1) load_q(1);
+  if (!grp_b) {
+    read_q();
+    if (n_items > 1) load_q(1);
+  }
 
   // Phases 0 .. 2 n_stream + 1.  Group A: matrix(u) in phase 2u, softmax(u) in 2u+1.  Group
   // B: softmax(u-1) in phase 2u, matrix(u) in 2u+1.  Each group runs its own straight loop
@@ -933,6 +942,11 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
     odd_end();
   } else {
     no_work(P0{});
+    // this wave's Q rows (requested after L(0), before L(1)): only L(1) and this phase's loads
+    // may still be in flight
+    wait_vmcnt<NBLK / 8 + LPP>();
+    read_q();
+    if (n_items > 1) load_q(1);
     even_end();
     auto step = [&](auto special_tag) __attribute__((always_inline)) {
       constexpr bool SPECIAL = decltype(special_tag)::value;
