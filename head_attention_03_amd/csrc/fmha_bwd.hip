@@ -13,7 +13,7 @@
 // masked positions carrying P = 0 (the backward mask of the walk-through's fusion-point
 // section: the forward masks with the causal offset 0 or Sk - Sq).
 //
-// CDNA4 design (two kernels, no atomics, deterministic):
+// CDNA4 design (two kernels, no atomics, deterministic; e4m3 inputs add a widening pass first):
 // * dq_kernel: a workgroup owns 256 query rows of one (sequence, head), 32 per wave, with its Q
 //   and dO rows held as MFMA B operands in registers.  It first forms the rows' statistics,
 //   delta_i and LSE_i * log2(e) (+inf for a row with no key), from its dO fragment and the same

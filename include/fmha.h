@@ -207,7 +207,7 @@ size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_
  * walk-through "CUTLASS Blackwell FMHA 示例完全解析", section "FMHA for Blackwell: Backward":
  * a row sum of O * dO, the main dQ/dK/dV pass, dQ converted to the output type; masks as that
  * section's backward mask, i.e. the forward masks).  Two kernels run on `stream`: dQ (which
- * also forms the row statistics), then dK/dV.  No atomics: results are bitwise repeatable.  With GQA/MQA
+ * also forms the row statistics), then dK/dV (after a widening pass for e4m3 inputs).  No atomics: results are bitwise repeatable.  With GQA/MQA
  * (H_kv < H), dk and dv of a K/V head are the sums over its group of query heads (the
  * CUTLASS backward does not support GQA; this is the gradient of the shared head).
  *
