@@ -199,9 +199,9 @@ def test_bwd_e4m3_end_to_end_from_hip_forward():
     _check_f8_dense("end-to-end", inp, do, o=o.cpu(), lse=lse.cpu().numpy())
 
 
-def test_bwd_e4m3_prefill_full_size_sampled():
+def test_bwd_e4m3_prefill_full_size_whole():
     # the e4m3 backward workload: B4 H16 2048 x 2048 D128 causal-qbegin, O and LSE from the fp8
-    # forward (o_scale 1); dQ of heads 0 and 13 of sequence 0 and dK, dV of the same heads, whole
+    # forward (o_scale 1); dQ, dK, dV of every (sequence, head)
     import head_attention_03_amd as fmha
     dev = torch.device("cuda:0")
     B, S, H, D = 4, 2048, 16, 128
@@ -218,13 +218,8 @@ def test_bwd_e4m3_prefill_full_size_sampled():
     o_cpu, lse_cpu = o.cpu(), lse.cpu().numpy()
     st, dq, dk, dv = run_bwd_dense(inp, do, o_cpu, lse_cpu)
     assert st == 0
-    q8, k8, v8, do8, o8 = (_face(t)[0] for t in (inp.q, inp.k, inp.v, do, o_cpu))
-    for h in (0, 13):
-        gq, gk, gv = oracle.attention_head_backward(q8[:, h], k8[:, h], v8[:, h], do8[:, h], inp.kernel_scale,
-                                                    inp.mask, o=o8[:, h])
-        compare_grad(f"e4m3 full size dQ head {h}", dq[0, :, h], "bf16", gq)
-        compare_grad(f"e4m3 full size dK head {h}", dk[0, :, h], "bf16", gk)
-        compare_grad(f"e4m3 full size dV head {h}", dv[0, :, h], "bf16", gv)
+    q8, k8, v8, do8, o8 = (_face(t) for t in (inp.q, inp.k, inp.v, do, o_cpu))
+    _whole_bwd("e4m3 full size", q8, k8, v8, do8, o8, inp.kernel_scale, inp.mask, dq, dk, dv)
 
 
 def test_bwd_e4m3_varlen():
@@ -275,43 +270,62 @@ def test_bwd_bitwise_repeatable():
         assert np.array_equal(to_bits(x), to_bits(y))
 
 
-def _sampled_full_size(name, inp, do, heads):
-    """HIP forward and backward at full size; the oracle's gradients for the query heads `heads`
-    of sequence 0 (whole GQA groups, so dK and dV of their K/V heads are complete)."""
+def _whole_bwd(name, q, k, v, do, o, scale, mask, dq, dk, dv, workers=8):
+    """Every (sequence, head) of a dense backward against the oracle, head by head (several
+    heads at a time: numpy's matmul and exp release the GIL); dK and dV of a K/V head are the
+    sums over its query heads.  o: the O the kernels received (delta from it), or None."""
+    from concurrent.futures import ThreadPoolExecutor
+    B, _, H, _ = q.shape
+    H_kv = k.shape[2]
+    g = H // H_kv
+
+    def one(bh):
+        b, h = bh
+        return oracle.attention_head_backward(q[b, :, h], k[b, :, h // g], v[b, :, h // g], do[b, :, h], scale, mask,
+                                              None if o is None else o[b, :, h])
+
+    units = [(b, h) for b in range(B) for h in range(H)]
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        res = dict(zip(units, ex.map(one, units)))
+    gd = "bf16" if dq.dtype == torch.bfloat16 else "f16"
+    for b in range(B):
+        for kvh in range(H_kv):
+            ek = sum(res[(b, h)][1] for h in range(kvh * g, (kvh + 1) * g))
+            ev = sum(res[(b, h)][2] for h in range(kvh * g, (kvh + 1) * g))
+            for h in range(kvh * g, (kvh + 1) * g):
+                compare_grad(f"{name} dQ b{b} h{h}", dq[b, :, h], gd, res[(b, h)][0])
+            compare_grad(f"{name} dK b{b} kv{kvh}", dk[b, :, kvh], gd, ek)
+            compare_grad(f"{name} dV b{b} kv{kvh}", dv[b, :, kvh], gd, ev)
+
+
+def test_bwd_prefill_full_size_whole():
+    # the backward workload: B4 H16 2048 x 2048 D128 bf16 causal-qbegin, O and LSE from the HIP
+    # forward; dQ, dK, dV of every (sequence, head)
+    inp = make_dense(4900, 4, 2048, 2048, 16, 16, 128, "bf16", mask="causal_qbegin")
+    do = make_grad(4901, (4, 2048, 16, 128), "bf16")
+    log(f"[case] bwd prefill full size whole seed={inp.seed}")
     res = run_dense(inp, want_lse=True)
     assert res.status == 0
     o = torch.from_numpy(res.o_bits.view(np.int16)).view(TORCH_DTYPES[inp.dtype])
     st, dq, dk, dv = run_bwd_dense(inp, do, o, res.lse)
     assert st == 0
-    group = inp.H // inp.H_kv
-    q, k, v = (decoded(inp, w)[0] for w in ("q", "k", "v"))
-    g = oracle.decode(to_bits(do), inp.dtype)[0]
-    kv_heads = sorted({h // group for h in heads})
-    for kvh in kv_heads:
-        ek = np.zeros((inp.Sk, inp.D))
-        ev = np.zeros((inp.Sk, inp.D))
-        for h in range(kvh * group, (kvh + 1) * group):
-            gq, gk, gv = oracle.attention_head_backward(q[:, h], k[:, kvh], v[:, kvh], g[:, h], inp.scale, inp.mask)
-            ek += gk
-            ev += gv
-            if h in heads:
-                compare_grad(f"{name} dQ head {h}", dq[0, :, h], inp.dtype, gq)
-        compare_grad(f"{name} dK kv head {kvh}", dk[0, :, kvh], inp.dtype, ek)
-        compare_grad(f"{name} dV kv head {kvh}", dv[0, :, kvh], inp.dtype, ev)
+    q, k, v = (decoded(inp, w) for w in ("q", "k", "v"))
+    _whole_bwd("prefill bwd", q, k, v, oracle.decode(to_bits(do), inp.dtype), None, inp.scale, inp.mask, dq, dk, dv)
 
 
-def test_bwd_prefill_full_size_sampled():
-    # the backward workload: B4 H16 2048 x 2048 D128 bf16 causal-qbegin; heads 0 and 13 of sequence 0
-    inp = make_dense(4900, 4, 2048, 2048, 16, 16, 128, "bf16", mask="causal_qbegin")
-    do = make_grad(4901, (4, 2048, 16, 128), "bf16")
-    _sampled_full_size("prefill bwd", inp, do, heads=[0, 13])
-
-
-def test_bwd_gqa_long_context_sampled():
-    # GQA 32/8 at 8192 x 8192 D128 bf16 causal: one whole group (query heads 20..23, K/V head 5)
+def test_bwd_gqa_long_context_whole():
+    # GQA 32/8 at 8192 x 8192 D128 bf16 causal, O and LSE from the HIP forward: dQ of all 32
+    # query heads, dK and dV of all 8 K/V heads (each the sum over its group of 4)
     inp = make_dense(4902, 1, 8192, 8192, 32, 8, 128, "bf16", mask="causal_qbegin")
     do = make_grad(4903, (1, 8192, 32, 128), "bf16")
-    _sampled_full_size("GQA 8192 bwd", inp, do, heads=[20, 21, 22, 23])
+    log(f"[case] bwd GQA 8192 whole seed={inp.seed}")
+    res = run_dense(inp, want_lse=True)
+    assert res.status == 0
+    o = torch.from_numpy(res.o_bits.view(np.int16)).view(TORCH_DTYPES[inp.dtype])
+    st, dq, dk, dv = run_bwd_dense(inp, do, o, res.lse)
+    assert st == 0
+    q, k, v = (decoded(inp, w) for w in ("q", "k", "v"))
+    _whole_bwd("GQA 8192 bwd", q, k, v, oracle.decode(to_bits(do), inp.dtype), None, inp.scale, inp.mask, dq, dk, dv)
 
 
 def test_bwd_tensors_beyond_2gib():
