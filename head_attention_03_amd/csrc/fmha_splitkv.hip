@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const Params p) {
   constexpr int KS = D / 16;         // MFMA k-steps over the head dimension
   constexpr int NDB = D / 32;        // 32-wide blocks of the head dimension in O
   static_assert(TILE % 1024 == 0 && QB % 1024 == 0, "whole 1 KiB loads");
-  static_assert(!KV8 || D >= 64, "e4m3 K/V rows of at least 64 bytes");
+  static_assert(!KV8 || D >= 32, "e4m3 K/V rows of at least 32 bytes (two 16-byte chunks)");
   static_assert((STG - 1) * NLD < 64, "vmcnt range");
   typedef Elem<DT> T;
   // eight e4m3 values (bytes 0..7 of w) as eight 16-bit values of the MFMA type, in order
@@ -646,9 +646,8 @@ fmha_status splitkv_plan(const void* q, const void* k, const void* v, const void
   if (packed && (varlen->total_length_q < 0 || varlen->total_length_k < 0)) return FMHA_ERR_INVALID_SHAPE;
   if ((int)dtype < 0 || (int)dtype > 2) return FMHA_ERR_UNSUPPORTED;
   if ((int)mask < 0 || (int)mask > 3) return FMHA_ERR_UNSUPPORTED;
-  // e4m3 queries (with an e4m3 K/V) run the e4m3-cache kernels, which need rows of 64 bytes or more
+  // e4m3 queries (with an e4m3 K/V) run the e4m3-cache kernels
   const bool q8 = dtype == FMHA_DTYPE_F8E4M3;
-  if (q8 && D == 32) return FMHA_ERR_UNSUPPORTED;
   const bool k8 = kv8 || q8;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FMHA_ERR_MISALIGNED;
   if ((uintptr_t)lse & 3) return FMHA_ERR_MISALIGNED;
@@ -765,6 +764,7 @@ fmha_status splitkv_run(const void* q, const void* k, const void* v, void* o, fl
 
   hipError_t err = hipSuccess;
   if (dtype == FMHA_DTYPE_F8E4M3) {  // e4m3 Q, K, V widened to bf16 for the matrix cores
+    if (D == 32) err = fmha::skv::launch<fmha::kBF16, 32, true, false, true>(p, mp, (int)grid, stream);
     if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64, true, false, true>(p, mp, (int)grid, stream);
     if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128, true, false, true>(p, mp, (int)grid, stream);
   } else if (dtype == FMHA_DTYPE_BF16) {
@@ -830,7 +830,6 @@ fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const voi
   const int32_t ps = paged->page_size;
   if (ps < kTN || ps > (1 << 16) || (ps & (ps - 1))) return FMHA_ERR_INVALID_SHAPE;
   if (!kv8 && paged->kv_dtype != dtype) return FMHA_ERR_UNSUPPORTED;
-  if (kv8 && D == 32) return FMHA_ERR_UNSUPPORTED;  // e4m3 rows of 32 bytes: not built
   const bool q8 = dtype == FMHA_DTYPE_F8E4M3;     // (e4m3 queries need an e4m3 cache)
   if (paged->max_pages_per_seq < 0 || paged->num_pages < 0) return FMHA_ERR_INVALID_SHAPE;
   if (!no_keys && (paged->num_pages < 1 || (int64_t)paged->max_pages_per_seq * ps < Sk)) return FMHA_ERR_INVALID_SHAPE;
@@ -871,6 +870,7 @@ fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const voi
     // An empty cache: the block table and the lengths may be NULL, and no key is read.  The
     // contiguous kernels (no table) give every row O = 0 and LSE = -inf, whatever the cache type.
     if (q8) {
+      if (D == 32) err = fmha::skv::launch<fmha::kBF16, 32, true, false, true>(p, mp, (int)grid, stream);
       if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64, true, false, true>(p, mp, (int)grid, stream);
       if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128, true, false, true>(p, mp, (int)grid, stream);
     } else if (dtype == FMHA_DTYPE_BF16) {
@@ -884,12 +884,15 @@ fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const voi
     }
   } else if (kv8) {
     if (q8) {
+      if (D == 32) err = fmha::skv::launch<fmha::kBF16, 32, true, true, true>(p, mp, (int)grid, stream);
       if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64, true, true, true>(p, mp, (int)grid, stream);
       if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128, true, true, true>(p, mp, (int)grid, stream);
     } else if (dtype == FMHA_DTYPE_BF16) {
+      if (D == 32) err = fmha::skv::launch<fmha::kBF16, 32, true, true>(p, mp, (int)grid, stream);
       if (D == 64) err = fmha::skv::launch<fmha::kBF16, 64, true, true>(p, mp, (int)grid, stream);
       if (D == 128) err = fmha::skv::launch<fmha::kBF16, 128, true, true>(p, mp, (int)grid, stream);
     } else {
+      if (D == 32) err = fmha::skv::launch<fmha::kF16, 32, true, true>(p, mp, (int)grid, stream);
       if (D == 64) err = fmha::skv::launch<fmha::kF16, 64, true, true>(p, mp, (int)grid, stream);
       if (D == 128) err = fmha::skv::launch<fmha::kF16, 128, true, true>(p, mp, (int)grid, stream);
     }

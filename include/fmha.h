@@ -152,11 +152,10 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
  *                    contents on entry do not matter and are overwritten (calls that
  *                    overlap in time must not share it)
  *   workspace_bytes  its size
- *   dtype            FMHA_DTYPE_F16, FMHA_DTYPE_BF16, or FMHA_DTYPE_F8E4M3 with D 64 or 128: e4m3 q,
+ *   dtype            FMHA_DTYPE_F16, FMHA_DTYPE_BF16, or FMHA_DTYPE_F8E4M3 (D 32, 64 or 128): e4m3 q,
  *                    k, v and o, the per-tensor dequantisation scales folded into scale and o_scale as
  *                    for fmha_fwd, the output saturated to +-448.  e4m3 values widen exactly to bf16,
- *                    so the fp8 call runs on the 16-bit matrix cores with its probabilities in bf16
- *                    (fp8 with D == 32: FMHA_ERR_UNSUPPORTED).
+ *                    so the fp8 call runs on the 16-bit matrix cores with its probabilities in bf16.
  * Errors as fmha_fwd, and: workspace NULL -> FMHA_ERR_NULL_POINTER, not 16-byte aligned
  * -> FMHA_ERR_MISALIGNED, smaller than needed -> FMHA_ERR_INVALID_ARGUMENT (checked only
  * when there is work).
@@ -269,7 +268,7 @@ size_t fmha_bwd_workspace_size(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int
  *                     e4m3 cache under fp16/bf16 queries (the fp8/INT8 KV quantisation the sm120
  *                     article's TODO section lists).  e4m3 values widen exactly to fp16/bf16 for
  *                     the matrix cores; the caller folds the cache's per-tensor dequantisation
- *                     scales into scale (K) and o_scale (V), as for fp8 in fmha_fwd.  D 64 or 128.
+ *                     scales into scale (K) and o_scale (V), as for fp8 in fmha_fwd.  D 32, 64 or 128.
  * Rows of a page past its sequence's end are never read. */
 typedef struct {
   const int32_t* block_table;
@@ -287,12 +286,11 @@ typedef struct {
  * splits, and max_pages_per_seq * page_size must reach it).  The causal-qend offset of sequence b
  * is seqlens_k[b] - Sq.  workspace: fmha_fwd_splitkv_workspace_size(B, Sq, Sk, H, H_kv, D, NULL)
  * bytes.  dtype (q and o): FMHA_DTYPE_F16 or FMHA_DTYPE_BF16, or FMHA_DTYPE_F8E4M3 over an e4m3 cache
- * (q and o e4m3 as in fmha_fwd_splitkv; D 64 or 128).
+ * (q and o e4m3 as in fmha_fwd_splitkv).
  * Errors as fmha_fwd_splitkv, and: paged NULL, or (when Sk > 0) k_cache, v_cache, block_table or
  * seqlens_k NULL -> FMHA_ERR_NULL_POINTER; page_size not a power of two in [32, 65536],
  * max_pages_per_seq * page_size < Sk, or num_pages < 1 -> FMHA_ERR_INVALID_SHAPE; kv_dtype neither
- * dtype nor FMHA_DTYPE_F8E4M3 (e4m3 queries need an e4m3 cache), or an e4m3 cache with D == 32 ->
- * FMHA_ERR_UNSUPPORTED.
+ * dtype nor FMHA_DTYPE_F8E4M3 (e4m3 queries need an e4m3 cache) -> FMHA_ERR_UNSUPPORTED.
  */
 fmha_status fmha_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                                    int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t H_kv, int32_t D, float scale,

@@ -85,7 +85,7 @@ def call_skv(**kw):
     (dict(q=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(workspace=None), 1),
     (dict(varlen=fmha.make_varlen(P, None, 1, 300)), 1),
     (dict(B=-1), 2), (dict(H=3, H_kv=2), 2), (dict(D=96), 2),
-    (dict(dtype="f8e4m3", D=32), 3), (dict(dtype=7), 3), (dict(mask=9), 3),
+    (dict(dtype="f8e4m3", D=32, workspace_bytes=100), 5), (dict(dtype=7), 3), (dict(mask=9), 3),
     (dict(Sq=1 << 16, H=128, H_kv=128, D=128), 3),  # 2 GiB of Q in one sequence
     (dict(H=1 << 15, H_kv=1 << 15, D=128), 3),  # a K row of 8 MiB: a split would pass 31-bit offsets
     (dict(q=P + 4), 4), (dict(lse=P + 1), 4), (dict(workspace=P + 8), 4),
@@ -135,7 +135,7 @@ def call_noalloc(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(q=None), 1), (dict(v=None), 1), (dict(B=-1), 2), (dict(D=96), 2), (dict(dtype="f8e4m3", D=32), 3),
+    (dict(q=None), 1), (dict(v=None), 1), (dict(B=-1), 2), (dict(D=96), 2), (dict(dtype="f8e4m3", D=32, q=P + 4), 4),
     (dict(q=P + 4), 4), (dict(scale=0.0), 5),
     # 64 sequences x 16 new tokens x 64 heads x D 128: the partials need more than the 32 MiB scratch
     (dict(B=64, Sq=16, Sk=8192, H=64, H_kv=8, D=128), 7),
@@ -251,9 +251,9 @@ def call_paged(**kw):
     (dict(paged=fmha.make_paged_kv(P, P, 3, 128, 8, "bf16")), 2), (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 0, "bf16")), 2),
     (dict(paged=fmha.make_paged_kv(P, P, 4, 1 << 17, 8, "bf16")), 2),
     (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 8, "f16")), 3), (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 8, 7)), 3),
-    (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 8, "f8e4m3"), D=32), 3),
+    (dict(paged=fmha.make_paged_kv(P, P, 4, 128, 8, "f8e4m3"), D=32, workspace_bytes=16), 5),
     (dict(dtype="f8e4m3"), 3),  # e4m3 queries over a bf16 cache
-    (dict(dtype="f8e4m3", paged=fmha.make_paged_kv(P, P, 4, 128, 8, "f8e4m3"), D=32), 3),
+    (dict(dtype="f8e4m3", paged=fmha.make_paged_kv(P, P, 4, 128, 8, "f8e4m3"), D=32, workspace_bytes=16), 5),
     (dict(dtype="f8e4m3", paged=fmha.make_paged_kv(P, P, 4, 128, 8, "f8e4m3"), q=P + 4), 4),  # accepted up to alignment
     (dict(H=3), 2), (dict(D=48), 2),
     (dict(k_cache=P + 8), 4), (dict(workspace=P + 8), 4),

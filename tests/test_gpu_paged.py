@@ -51,6 +51,7 @@ def test_paged_decode(case):
     (4, 1, [4097, 1, 300, 0], 32, 8, 128, "none", 128),
     (3, 4, [1000, 64, 2500], 16, 2, 64, "causal_qend", 32),
     (2, 2, [2112, 500], 8, 8, 128, "none", 32),  # a split over more than 64 pages: table read per tile
+    (3, 1, [900, 33, 2049], 8, 2, 32, "causal_qend", 64),  # D = 32: e4m3 rows of 32 bytes
 ], ids=lambda c: f"B{c[0]}-q{c[1]}-H{c[3]}/{c[4]}-D{c[5]}-{c[6]}-p{c[7]}")
 def test_paged_fp8_queries(case):
     # e4m3 queries and output over an e4m3 cache (NaN codes in the pages no sequence owns)
@@ -141,6 +142,8 @@ PAGED_FP8 = [
     (3, 4, [1000, 64, 2500], 16, 2, 64, "f16", "causal_qend", 32),
     (2, 16, [3000, 33], 8, 2, 128, "bf16", "causal_qend", 64),
     (2, 2, [700, 1300], 4, 1, 64, "bf16", "causal_qbegin", 256),
+    (3, 1, [900, 33, 2049], 8, 2, 32, "bf16", "none", 64),   # D = 32: e4m3 rows of 32 bytes
+    (2, 4, [2500, 130], 16, 4, 32, "f16", "causal_qend", 32),
 ]
 
 

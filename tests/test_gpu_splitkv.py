@@ -95,6 +95,8 @@ DECODE_FP8 = [
     (2, 16, 3000, 8, 2, 128, "residual"),
     (1, 130, 100, 4, 2, 64, "causal_qend"),   # rows without keys: O = 0, LSE = -inf
     (8, 1, 16384, 32, 8, 128, "causal_qend"),
+    (3, 2, 2500, 8, 2, 32, "causal_qend"),    # D = 32: e4m3 rows of 32 bytes
+    (2, 1, 700, 4, 4, 32, "none"),
 ]
 
 
