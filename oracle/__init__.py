@@ -36,7 +36,11 @@ from K, GQA overwrite or wrong head, varlen key offset) fail the pins.  The row-
 for sequences too long to hold S (attention_head_backward_rows) is pinned against autograd
 directly at several block sizes and on rows that see no key; its planted mistakes (dropped
 softmax term, dV from dS, dQ row off by one, block mask taken from row 0, dK without the
-scale) fail the pins too.
+scale) fail the pins too.  delta taken from a given O (the ``o`` argument, for an O stored in a
+coarse type such as e4m3) is pinned against autograd with the exact O and against the closed
+form of a perturbed O (dQ and dK shift by the changed delta times P K and P^T Q, dV does not),
+through the single-head, dense GQA and packed forms; planted mistakes (the given O ignored,
+delta without dO, the K/V head's O, O at the key rows) fail the pins.
 
 Paged-cache pins (tests/test_oracle_paged.py): brute force with per-key page arithmetic and
 the plain softmax quotient; the dense forward oracle on a cache laid out in order; invariance
