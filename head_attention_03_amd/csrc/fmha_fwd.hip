@@ -136,6 +136,7 @@ struct Params {
   int32_t qend;     // causal aligned to the last key
   int32_t xcd_per;  // (sequence, head) pairs per XCD when B*H % 8 == 0, else 0
   int32_t ngrp;     // workgroups per (sequence, head)
+  int32_t rank_seqs;  // packed batch of at most 64 sequences: sequences taken longest (in keys) first
   float scale_log2; // scale * log2(e)
   float o_scale;
 };
@@ -195,7 +196,32 @@ __global__ __launch_bounds__(kThreads, 1) void fmha_fwd_kernel(const Params p) {
   const int BH = p.B * p.H;
   const int x = blockIdx.x;
   int bh, grp;
-  if (p.xcd_per) {  // round-robin dispatch puts workgroup x on XCD x % 8
+  if (p.rank_seqs) {
+    // Packed batch: (sequence, head) pairs in the order of the sequences' key counts, longest
+    // first, so that the longest streams start in the first round of workgroups (in batch order
+    // a long sequence's q-tiles can land behind every other sequence's and run one after another
+    // on one compute unit).  The pairs are dealt to the XCDs in turn and the workgroups of one
+    // pair sit side by side on its XCD; lane i ranks sequence i (B <= 64).
+    int pr;
+    if (p.xcd_per) {
+      const int slot = x >> 3;
+      pr = (slot / p.ngrp) * 8 + (x & 7);
+      grp = slot % p.ngrp;
+    } else {
+      pr = x / p.ngrp;
+      grp = x % p.ngrp;
+    }
+    const int r = pr / p.H;
+    const int hh = pr - r * p.H;
+    const int sk_l = lane < p.B ? p.cu_k[lane + 1] - p.cu_k[lane] : -1;
+    int rank = 0;
+    for (int j = 0; j < p.B; ++j) {
+      const int sk_j = __builtin_amdgcn_readlane(sk_l, j);
+      rank += (sk_j > sk_l) | ((sk_j == sk_l) & (j < lane));
+    }
+    const uint64_t of_r = __ballot(lane < p.B && rank == r);  // one lane: the ranks are 0 .. B-1
+    bh = (int)__builtin_ctzll(of_r) * p.H + hh;
+  } else if (p.xcd_per) {  // round-robin dispatch puts workgroup x on XCD x % 8
     const int slot = x >> 3;
     if (p.ipw > 1) {  // the workgroups of one (sequence, head) side by side
       grp = slot % p.ngrp;
@@ -1078,7 +1104,12 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
   // even when causal (pairs of a heavy and a light tile); one when there is less work
   const int cus = compute_units();
   if (cus < 1) return FMHA_ERR_HIP;
-  int64_t ipw = BH * n_qtiles / cus;
+  // packed batches of up to 64 sequences are ordered by key count in the kernel, and their
+  // q-tiles are counted from the total rows (at most total / 256 + B), not as B times the longest
+  p.rank_seqs = packed && B <= 64 ? 1 : 0;
+  int64_t qtiles_all = (int64_t)B * n_qtiles;
+  if (p.rank_seqs && varlen->total_length_q / kBM + B < qtiles_all) qtiles_all = varlen->total_length_q / kBM + B;
+  int64_t ipw = (int64_t)H * qtiles_all / cus;
   ipw = ipw < 1 ? 1 : ipw > 8 ? 8 : ipw;
   if (ipw > n_qtiles) ipw = n_qtiles;
   if (p.causal && ipw > 1) ipw &= ~(int64_t)1;

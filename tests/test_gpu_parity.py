@@ -132,14 +132,19 @@ def test_bitwise_repeatable():
 # several q-tiles per workgroup: enough (sequence, head, q-tile) items that every workgroup runs
 # two or more of them as one K/V stream (item changes, one- and two-tile items, ragged tiles)
 # ----------------------------------------------------------------------------------------------
-def _items_per_workgroup(B, H, Sq, mask, Sk=0, H_kv=1, D=128, esz=2):
+def _items_per_workgroup(B, H, Sq, mask, Sk=0, H_kv=1, D=128, esz=2, total_q=None):
     """The launch rule of the library: q-tiles of 256 rows, about one workgroup per compute unit,
     at most 8 per workgroup, pairs when causal; then, when B*H is a multiple of 8, the largest
-    halving (down to 2) at which the K/V heads that an XCD's resident workgroups stream fit 4 MiB."""
+    halving (down to 2) at which the K/V heads that an XCD's resident workgroups stream fit 4 MiB.
+    Packed batches of at most 64 sequences (total_q given) count their q-tiles as at most
+    total_q // 256 + B instead of B times the longest sequence's."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     n_qt = (Sq + 255) // 256
     causal = mask.startswith("causal")
-    ipw = max(1, min(8, B * H * n_qt // cus, n_qt))
+    qt_all = B * n_qt
+    if total_q is not None and B <= 64:
+        qt_all = min(qt_all, total_q // 256 + B)
+    ipw = max(1, min(8, H * qt_all // cus, n_qt))
     if causal and ipw > 1:
         ipw &= ~1
     if (B * H) % 8 == 0 and ipw > 2:
@@ -269,12 +274,24 @@ def test_varlen_poisoned_padding_never_read():
 
 def test_varlen_several_qtiles_per_workgroup():
     # q-tiles per sequence from 0 to 4 under one launch rule (4 per workgroup): workgroups of the
-    # short sequences run fewer items, or none
+    # short sequences run fewer items, or none; the sequences are taken longest first
     lq = [1000, 300, 64, 1, 0, 513, 777, 256]
     lk = [900, 310, 64, 1, 5, 600, 1000, 40]
     inp = make_varlen(2970, lq, lk, 128, 16, 64, "bf16", mask="causal_qend", poison_pads=True)
-    assert _items_per_workgroup(len(lq), 128, max(lq), "causal_qend") >= 2
+    assert _items_per_workgroup(len(lq), 128, max(lq), "causal_qend", max(lk), 16, 64, 2, sum(lq)) >= 2
     _varlen_case("varlen multi-item", inp)
+
+
+@pytest.mark.parametrize("n_seq", [64, 65])
+def test_varlen_many_sequences(n_seq):
+    # up to 64 sequences the kernel takes them in the order of their key counts (ties in batch
+    # order), past 64 in batch order: both work orders, with ties, empty and one-row sequences
+    rng = np.random.default_rng(2990 + n_seq)
+    lq = [int(x) for x in rng.integers(0, 600, size=n_seq)]
+    lk = [int(x) for x in rng.choice([0, 1, 64, 300, 300, 700, 1500], size=n_seq)]
+    lq[0], lq[1] = 1, 0
+    inp = make_varlen(2990 + n_seq, lq, lk, 4, 2, 64, "bf16", mask="causal_qend")
+    _varlen_case(f"varlen {n_seq} sequences", inp)
 
 
 def test_varlen_equals_dense_runs():
