@@ -282,6 +282,16 @@ def test_varlen_several_qtiles_per_workgroup():
     _varlen_case("varlen multi-item", inp)
 
 
+def test_varlen_ranked_several_qtiles_without_xcd_groups():
+    # the longest-first order with four q-tiles per workgroup (pairs of heavy and light tiles)
+    # and B*H not a multiple of 8 (pairs dealt in plain order, not per XCD)
+    lq, lk, H, H_kv = [700, 1024, 300], [900, 1024, 1500], 170, 17
+    assert (len(lq) * H) % 8 != 0
+    assert _items_per_workgroup(len(lq), H, max(lq), "causal_qend", max(lk), H_kv, 64, 2, sum(lq)) >= 2
+    inp = make_varlen(2980, lq, lk, H, H_kv, 64, "f16", mask="causal_qend")
+    _varlen_case("varlen ranked, several q-tiles, plain order", inp)
+
+
 @pytest.mark.parametrize("n_seq", [64, 65])
 def test_varlen_many_sequences(n_seq):
     # up to 64 sequences the kernel takes them in the order of their key counts (ties in batch
