@@ -91,6 +91,7 @@ struct Params {
   int32_t aux_hstride;   // blocks between consecutive heads of one sequence
   int32_t n_tiles;       // dq: q tiles per sequence; dkdv: key tiles
   int32_t xcd_per;       // (sequence, head) pairs per XCD when their count is a multiple of 8
+  int32_t rank_seqs;     // packed batch of at most 64 sequences: sequences taken longest first
   int32_t causal, qend;
   float scale, scale_log2;
 };
@@ -122,10 +123,36 @@ __device__ inline int aux_seq_base(const Params& p, int b, int q_row0) {
 }
 
 // (pair, group) of a workgroup: round-robin dispatch puts workgroup x on XCD x % 8, so the
-// pairs are dealt out per XCD and the workgroups of one pair share that XCD's L2.
-__device__ inline void decode_unit(const Params& p, int npairs, int* pair, int* grp) {
+// pairs are dealt out per XCD and the workgroups of one pair share that XCD's L2.  Packed
+// batches of at most 64 sequences (rank_seqs) take the sequences longest first, by query rows
+// (by_q: the dK/dV kernel, whose key blocks see them) or by keys (the dQ kernel), with all the
+// workgroups of a pair side by side; in batch order a long sequence's tiles can land behind every
+// other sequence's and run one after another on one compute unit.
+__device__ inline void decode_unit(const Params& p, int npairs, int* pair, int* grp, bool by_q) {
   const int x = blockIdx.x;
-  if (p.xcd_per) {
+  if (p.rank_seqs) {
+    int pr;
+    if (p.xcd_per) {
+      const int slot = x >> 3;
+      pr = (slot / p.n_tiles) * 8 + (x & 7);
+      *grp = slot % p.n_tiles;
+    } else {
+      pr = x / p.n_tiles;
+      *grp = x % p.n_tiles;
+    }
+    const int heads = npairs / p.B;
+    const int r = pr / heads;
+    const int lane = threadIdx.x & 63;
+    const int32_t* cu = by_q ? p.cu_q : p.cu_k;
+    const int len_l = lane < p.B ? cu[lane + 1] - cu[lane] : -1;  // lane i: sequence i (B <= 64)
+    int rank = 0;
+    for (int j = 0; j < p.B; ++j) {
+      const int len_j = __builtin_amdgcn_readlane(len_l, j);
+      rank += (len_j > len_l) | ((len_j == len_l) & (j < lane));
+    }
+    const uint64_t of_r = __ballot(lane < p.B && rank == r);  // one lane: the ranks are 0 .. B-1
+    *pair = (int)__builtin_ctzll(of_r) * heads + (pr - r * heads);
+  } else if (p.xcd_per) {
     const int slot = x >> 3;
     *grp = slot / p.xcd_per;
     *pair = (x & 7) * p.xcd_per + slot % p.xcd_per;
@@ -222,7 +249,7 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_kernel(const Params p) {
   const int h32 = lane >> 5;
 
   int bh, grp;
-  decode_unit(p, p.B * p.H, &bh, &grp);
+  decode_unit(p, p.B * p.H, &bh, &grp, false);
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int kvh = h / p.group;
@@ -449,7 +476,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkdv_kernel(const Params p) {
   const int kblk = wave_u & (kKvBlocks - 1);
 
   int bkv, grp;
-  decode_unit(p, p.B * p.H_kv, &bkv, &grp);
+  decode_unit(p, p.B * p.H_kv, &bkv, &grp, true);
   const int b = bkv / p.H_kv;
   const int kvh = bkv - b * p.H_kv;
   const Seq sq = seq_bounds(p, b);
@@ -934,6 +961,7 @@ fmha_status fmha_bwd(const void* q, const void* k, const void* v, const void* o,
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   p.xcd_per = 0;
   p.n_tiles = 0;
+  p.rank_seqs = packed && B <= 64 ? 1 : 0;
 
   // Streams whose byte offsets from the start of one sequence could pass 31 bits (one tile to
   // spare; packed batches bounded by their totals) take the kernels that place descriptors at

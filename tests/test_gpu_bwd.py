@@ -260,6 +260,27 @@ def test_bwd_e4m3_no_query_rows():
     assert torch.all(dk == 0) and torch.all(dv == 0)
 
 
+@pytest.mark.parametrize("n_seq", [64, 65])
+def test_bwd_varlen_many_sequences(n_seq):
+    # up to 64 sequences both kernels take them longest first (dQ by keys, dK/dV by query rows,
+    # ties in batch order), past 64 in batch order: both work orders, with empty sequences
+    rng = np.random.default_rng(4990 + n_seq)
+    lq = [int(x) for x in rng.choice([0, 1, 64, 200, 450], size=n_seq)]
+    lk = [int(x) for x in rng.choice([0, 1, 64, 300, 700], size=n_seq)]
+    inp = make_varlen(4990 + n_seq, lq, lk, 4, 2, 64, "bf16", mask="causal_qend")
+    log(f"[case] bwd varlen {n_seq} sequences seed={inp.seed}")
+    do_buf = make_grad(4995 + n_seq, tuple(inp.q_buf.shape), "bf16")
+    o, lse = oracle_forward_inputs(inp)
+    st, dq, dk, dv = run_bwd_varlen(inp, do_buf, o, lse)
+    assert st == 0
+    eq, ek, ev = oracle.attention_backward_varlen(
+        decoded(inp, "q"), decoded(inp, "k"), decoded(inp, "v"),
+        oracle.decode(to_bits(do_buf[inp.pad_q:]), "bf16"), inp.cu_q, inp.cu_k, inp.scale, "causal_qend")
+    compare_grad(f"varlen {n_seq} dQ", dq[inp.pad_q:], "bf16", eq)
+    compare_grad(f"varlen {n_seq} dK", dk[inp.pad_k:], "bf16", ek)
+    compare_grad(f"varlen {n_seq} dV", dv[inp.pad_k:], "bf16", ev)
+
+
 def test_bwd_bitwise_repeatable():
     inp = make_dense(4800, 2, 520, 520, 4, 2, 128, "bf16", mask="causal_qbegin")
     do = make_grad(4801, (2, 520, 4, 128), "bf16")
